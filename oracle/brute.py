@@ -1,0 +1,150 @@
+"""ORACLE pins -- test infrastructure only (imported by tests/ alone).
+
+Independent formulations used to pin ``moe_oracle`` on tiny inputs.  None of
+them shares code with ``moe_oracle``:
+
+  * ``dense_forward``: every token goes through every expert (no sorting, no
+    permutation, no segments); the expert outputs are then mixed with a gate
+    matrix built from a full softmax over all experts, masked to the top-k and
+    renormalised.  This is the "dense" reading of the same layer: the MoE layer
+    of the pages computes exactly this, only faster.
+  * ``topk_by_scan``: top-k by repeated scans over a Python list.
+  * ``torch_dense_grads``: the dense formulation in torch fp64 with autograd,
+    for the backward pass.
+  * ``logits_exact``: the router logit fma chain evaluated with exact rational
+    arithmetic and one correct rounding to fp32 per step.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+import math
+
+import numpy as np
+
+
+def topk_by_scan(row, k):
+    """k indices of the largest values; equal values -> lower index first."""
+    vals = [float(v) for v in row]
+    taken = [False] * len(vals)
+    out = []
+    for _ in range(k):
+        best = -1
+        for i, v in enumerate(vals):
+            if taken[i]:
+                continue
+            if best < 0 or v > vals[best]:
+                best = i
+        taken[best] = True
+        out.append(best)
+    return out
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def dense_forward(x, w_r, w_gu, w_down, k, bias=None, noise=None, logits=None):
+    """fp64 dense formulation.  If ``logits`` is given it is used for the routing
+    decision (so that a near-tie resolved in fp32 is resolved the same way);
+    the gate values always come from the fp64 softmax of those logits."""
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    E = w_r.shape[0]
+    f = w_gu.shape[1] // 2
+    if logits is None:
+        L = x @ np.asarray(w_r, np.float64).T
+        if bias is not None:
+            L = L + np.asarray(bias, np.float64)[None, :]
+        if noise is not None:
+            L = L + np.asarray(noise, np.float64)
+    else:
+        L = np.asarray(logits, np.float64)
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)          # full softmax over all experts
+    gate = np.zeros((T, E))
+    sel = np.zeros((T, k), np.int64)
+    for t in range(T):
+        s = topk_by_scan(L[t], k)
+        sel[t] = s
+        gate[t, s] = p[t, s] / p[t, s].sum()        # renormalised over the selected
+    y = np.zeros((T, d))
+    for e in range(E):                              # every token through every expert
+        gu = x @ np.asarray(w_gu[e], np.float64).T
+        h = _silu(gu[:, :f]) * gu[:, f:]
+        y += gate[:, e:e + 1] * (h @ np.asarray(w_down[e], np.float64).T)
+    return {"logits": L, "gate": gate, "sel": sel, "y": y}
+
+
+def torch_dense_grads(x, w_r, w_gu, w_down, dy, sel, bias=None, noise=None):
+    """Gradients of sum(Y * dY) for the dense formulation with the selection
+    fixed to ``sel`` [T,k], via torch fp64 autograd on the CPU."""
+    import torch
+    dt = torch.float64
+    X = torch.tensor(np.asarray(x), dtype=dt, requires_grad=True)
+    Wr = torch.tensor(np.asarray(w_r), dtype=dt, requires_grad=True)
+    Wgu = torch.tensor(np.asarray(w_gu), dtype=dt, requires_grad=True)
+    Wd = torch.tensor(np.asarray(w_down), dtype=dt, requires_grad=True)
+    f = Wgu.shape[1] // 2
+    L = X @ Wr.T
+    if bias is not None:
+        L = L + torch.tensor(np.asarray(bias), dtype=dt)[None, :]
+    if noise is not None:
+        L = L + torch.tensor(np.asarray(noise), dtype=dt)
+    L.retain_grad()
+    S = torch.tensor(np.asarray(sel), dtype=torch.int64)
+    w = torch.softmax(torch.gather(L, 1, S), dim=1)
+    outs = []
+    for e in range(Wgu.shape[0]):
+        gu = X @ Wgu[e].T
+        h = torch.nn.functional.silu(gu[:, :f]) * gu[:, f:]
+        outs.append(h @ Wd[e].T)
+    O = torch.stack(outs, dim=1)                      # [T, E, d]
+    Osel = torch.gather(O, 1, S[:, :, None].expand(-1, -1, O.shape[2]))
+    Y = (w[:, :, None] * Osel).sum(dim=1)
+    loss = (Y * torch.tensor(np.asarray(dy), dtype=dt)).sum()
+    loss.backward()
+    return {"y": Y.detach().numpy(), "dx": X.grad.numpy(), "dw_r": Wr.grad.numpy(),
+            "dw_gu": Wgu.grad.numpy(), "dw_down": Wd.grad.numpy(), "d_logits": L.grad.numpy()}
+
+
+def _round_fraction_to_f32(q: Fraction) -> float:
+    """Correct round-to-nearest-even of an exact rational to IEEE binary32."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    # fix e so that 2^e <= a < 2^(e+1)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                                  # subnormal spacing floor
+    scale = Fraction(2) ** (23 - e)                   # 24 significant bits
+    m = a * scale
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(Fraction(n) / scale)
+
+
+def logits_exact(x, w_r, bias=None, noise=None):
+    """Router logit chain with every fma evaluated exactly and rounded once."""
+    x = np.asarray(x, np.float32)
+    w_r = np.asarray(w_r, np.float32)
+    T, d = x.shape
+    E = w_r.shape[0]
+    out = np.zeros((T, E), np.float32)
+    for t in range(T):
+        for e in range(E):
+            acc = 0.0
+            for c in range(d):
+                acc = _round_fraction_to_f32(Fraction(float(x[t, c])) * Fraction(float(w_r[e, c]))
+                                             + Fraction(acc))
+            if bias is not None:
+                acc = _round_fraction_to_f32(Fraction(acc) + Fraction(float(bias[e])))
+            if noise is not None:
+                acc = _round_fraction_to_f32(Fraction(acc) + Fraction(float(noise[t, e])))
+            out[t, e] = acc
+    return out

@@ -1,0 +1,80 @@
+"""The pins must catch plausible mistakes in the oracle (CPU only).
+
+Each case plants one mistake in a copy of ``oracle/moe_oracle.py`` (a dropped
+term, a wrong sign, a wrong index map, a misplaced rounding), loads the copy as
+a separate module, and runs the pin tests against it: at least one must fail.
+"""
+import importlib.util
+import os
+import sys
+
+import pytest
+
+import tests.test_oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "moe_oracle.py")
+
+MUTATIONS = [
+    ("dropped dSiLU term", "dg = dh * u * sg * (1.0 + g * (1.0 - sg))", "dg = dh * u * sg"),
+    ("wrong sign in softmax adjoint", "w * (g - s), axis=1)", "w * (g + s), axis=1)"),
+    ("up gradient uses sigmoid instead of silu", "du = dh * g * sg\n", "du = dh * sg\n"),
+    ("row weight not applied to the expert output",
+     "y = _f64(wr)[:, None] * y", "y = y"),
+    ("row weight missing from the down-projection weight gradient",
+     "s = store(w[:, None] * _f64(dyr), bf16)\n    return dgu", "s = store(_f64(dyr), bf16)\n    return dgu"),
+    ("combine gathers with the wrong map", "s2r = np.asarray(slot_to_row, dtype=np.int64).reshape(T, k)\n    acc = np.zeros((T, y_perm",
+     "s2r = np.argsort(np.asarray(slot_to_row)).reshape(T, k)\n    acc = np.zeros((T, y_perm"),
+    ("slots of one expert in descending order", 'row_to_slot = np.argsort(flat, kind="stable")',
+     'row_to_slot = np.lexsort((-np.arange(flat.size), flat))'),
+    ("ties resolved to the higher id", 'idx = np.argsort(-L, axis=1, kind="stable")[:, :k]',
+     'idx = (L.shape[1] - 1 - np.argsort(-L[:, ::-1], axis=1, kind="stable"))[:, :k]'),
+    ("softmax over all experts, not renormalised", "w = ex / ex.sum(axis=1, keepdims=True)",
+     "w = ex / np.exp(L.astype(np.float64) - sel[:, :1]).sum(axis=1, keepdims=True)"),
+    ("H not rounded to bf16", "h = store(silu(gu[:, :f]) * _f64(gu[:, f:]), bf16)",
+     "h = np.asarray(silu(gu[:, :f]) * _f64(gu[:, f:]), np.float32)"),
+    ("gate and up halves swapped", "h = store(silu(gu[:, :f]) * _f64(gu[:, f:]), bf16)",
+     "h = store(silu(gu[:, f:]) * _f64(gu[:, :f]), bf16)"),
+    ("router weight gradient scaled", "return (dl @ _f64(w_r)).astype(np.float32), (dl.T @ _f64(x))",
+     "return (dl @ _f64(w_r)).astype(np.float32), (dl.T @ _f64(x) * 0.5)"),
+    ("router gradient not added to dX", "acc += _f64(dx_add)", "pass"),
+]
+
+PIN_TESTS = [
+    lambda: P.test_topk_ties_and_closed_forms(),
+    lambda: P.test_topk_matches_scan_and_softmax_sums_to_one(),
+    lambda: P.test_permutation_is_stable_sort_by_expert(),
+    lambda: P.test_combine_of_permute_identities(),
+    lambda: P.test_forward_matches_dense_formulation_fp32(),
+    lambda: P.test_forward_single_expert_is_dense_swiglu_with_bf16_storage(),
+    lambda: P.test_backward_matches_torch_autograd_fp32((25, 8, 4, 4, 12)),
+    lambda: P.test_backward_matches_torch_autograd_fp32((30, 16, 6, 2, 8)),
+    lambda: P.test_backward_invariants(),
+]
+
+
+def _load_mutant(old, new, tag):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    src = src.replace(old, new)
+    name = "oracle._mutant_%d" % abs(hash(tag))
+    spec = importlib.util.spec_from_loader(name, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__file__ = SRC
+    exec(compile(src, SRC, "exec"), mod.__dict__)
+    sys.modules[name] = mod
+    return mod
+
+
+@pytest.mark.parametrize("tag,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tag, old, new, monkeypatch):
+    mutant = _load_mutant(old, new, tag)
+    monkeypatch.setattr(P, "O", mutant)
+    caught = False
+    for run in PIN_TESTS:
+        try:
+            run()
+        except Exception:
+            caught = True
+            break
+    assert caught, "no pin caught: " + tag

@@ -1,0 +1,329 @@
+"""Pins of the oracle against things other than itself (CPU only).
+
+Each test checks one part of ``oracle/moe_oracle.py`` against an independent
+formulation (brute force, exact arithmetic, a library routine, torch autograd,
+finite differences), a closed form, or an invariant the mathematics fixes.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute
+from oracle import moe_oracle as O
+from mixture_experts_layer_03_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _tiny(T=24, d=16, E=6, k=2, f=8, seed=0, bf16=False, bias=False, noise=False):
+    w = I.Workload("t", T, d, E, k, f, "bf16" if bf16 else "fp32", True,
+                   "zipf" if bias else ("noise" if noise else "uniform"), x_scale="unit", seed=seed)
+    return w, I.make_inputs(w)
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    r = _rng(1)
+    a = np.concatenate([
+        r.standard_normal(20000).astype(np.float32) * 10.0,
+        np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 3.0e38, 1e-40, -1e-41], np.float32),
+        # exact ties: low 16 bits 0x8000 with even and odd kept lsb
+        np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x00008000], np.uint32).view(np.float32),
+    ])
+    ours = O.to_bf16(a)
+    ref = torch.from_numpy(a.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(O.to_bf16(np.array([np.nan], np.float32)))[0]
+
+
+def test_input_generator_is_seeded_and_bf16_exact():
+    w, a = _tiny(bf16=True, seed=5)
+    _, b = _tiny(bf16=True, seed=5)
+    _, c = _tiny(bf16=True, seed=6)
+    for key in ("x", "w_r", "w_gu", "w_down", "dy"):
+        assert np.array_equal(a[key], b[key])
+        assert not np.array_equal(a[key], c[key])
+        assert np.array_equal(O.to_bf16(a[key]), a[key])
+
+
+# ---------------------------------------------------------------- router logits
+
+@pytest.mark.parametrize("bf16,bias,noise", [(False, False, False), (False, True, False),
+                                              (True, False, True), (True, True, False)])
+def test_router_logits_bit_exact_to_exact_arithmetic(bf16, bias, noise):
+    w, a = _tiny(T=5, d=12, E=4, bf16=bf16, bias=bias, noise=noise, seed=11)
+    got = O.router_logits(a["x"], a["w_r"], a["bias"], a["noise"])
+    ref = brute.logits_exact(a["x"], a["w_r"], a["bias"], a["noise"])
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_router_logits_order_is_the_hidden_index_order():
+    # bf16 inputs: every product is exact in fp32, so the chain equals a plain
+    # fp32 multiply-then-add loop in hidden order; any other order differs
+    # somewhere on this input.
+    w, a = _tiny(T=64, d=256, E=8, bf16=True, seed=12)
+    got = O.router_logits(a["x"], a["w_r"])
+    acc = np.zeros((64, 8), np.float32)
+    for c in range(256):
+        acc = (acc + a["x"][:, c:c + 1] * a["w_r"][None, :, c]).astype(np.float32)
+    assert np.array_equal(got, acc)
+    rev = np.zeros((64, 8), np.float32)
+    for c in reversed(range(256)):
+        rev = (rev + a["x"][:, c:c + 1] * a["w_r"][None, :, c]).astype(np.float32)
+    assert not np.array_equal(got, rev)
+    ref = a["x"].astype(np.float64) @ a["w_r"].astype(np.float64).T
+    assert np.max(np.abs(got - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref)))
+
+
+# ---------------------------------------------------------------- top-k + softmax
+
+def test_topk_matches_scan_and_softmax_sums_to_one():
+    r = _rng(3)
+    for E, k in [(8, 2), (32, 4), (128, 8), (5, 5), (1, 1), (16, 16)]:
+        L = r.standard_normal((50, E)).astype(np.float32)
+        L[::7] = np.round(L[::7])                      # many exact ties
+        idx, w = O.route(L, k)
+        for t in range(50):
+            assert list(idx[t]) == brute.topk_by_scan(L[t], k)
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -23)
+        assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_topk_ties_and_closed_forms():
+    with open(os.path.join(GOLDEN, "routing_closed_forms.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        L = np.array(c["logits"], np.float32)
+        if c.get("logits_expr") == "log3":
+            L = np.array([[0.0, math.log(3.0), -5.0]], np.float32)
+        idx, w = O.route(L, c["k"])
+        assert idx.tolist() == c["topk_idx"], c["name"]
+        np.testing.assert_allclose(w, np.array(c["topk_w"], np.float32), rtol=0, atol=c["atol"],
+                                   err_msg=c["name"])
+
+
+# ---------------------------------------------------------------- permutation
+
+def _perm_by_loops(idx, E):
+    flat = idx.ravel()
+    s2r = np.full(flat.size, -1, np.int64)
+    nxt = 0
+    for e in range(E):
+        for s in range(flat.size):
+            if flat[s] == e:
+                s2r[s] = nxt
+                nxt += 1
+    return s2r
+
+
+def test_permutation_is_stable_sort_by_expert():
+    r = _rng(4)
+    for T, E, k in [(40, 8, 2), (33, 32, 4), (7, 3, 3), (0, 4, 2), (64, 1, 1)]:
+        L = r.standard_normal((T, E)).astype(np.float32)
+        idx, _ = O.route(L, k) if T else (np.zeros((0, k), np.int32), None)
+        counts, offsets, s2r, r2s = O.permute_maps(idx, E)
+        assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+        assert offsets[0] == 0 and offsets[-1] == T * k
+        assert np.array_equal(np.diff(offsets), counts)
+        assert np.array_equal(s2r, _perm_by_loops(idx, E))
+        assert np.array_equal(r2s[s2r], np.arange(T * k))       # bijection
+        for e in range(E):
+            rows = np.arange(offsets[e], offsets[e + 1])
+            assert np.all(idx.ravel()[r2s[rows]] == e)
+            assert np.all(np.diff(r2s[rows]) > 0)
+
+
+def test_combine_of_permute_identities():
+    r = _rng(5)
+    T, d, E = 48, 24, 8
+    x = O.to_bf16(r.standard_normal((T, d)).astype(np.float32))
+    # (i) k = 1 with unit weights: exact identity
+    idx, _ = O.route(r.standard_normal((T, E)).astype(np.float32), 1)
+    _, _, s2r, r2s = O.permute_maps(idx, E)
+    xp, _ = O.permute_rows(x, None, r2s, 1)
+    assert np.array_equal(O.combine(xp, s2r, T, 1, True), x)
+    # (ii) softmax weights (sum to one), rows scaled by their weight in bf16:
+    #      the sum rounds back to x exactly
+    for k in (2, 4, 8):
+        idx, w = O.route(r.standard_normal((T, E)).astype(np.float32), k)
+        _, _, s2r, r2s = O.permute_maps(idx, E)
+        xp, wp = O.permute_rows(x, w, r2s, k)
+        yp = O.to_bf16(wp[:, None].astype(np.float64) * xp)
+        got = O.combine(yp, s2r, T, k, True)
+        close = np.abs(got - x) <= 2.0 ** -7 * np.abs(x) + 1e-30
+        assert close.all()
+    # (iii) unweighted, k a power of two: exactly k * x
+    for k in (2, 4):
+        idx, _ = O.route(r.standard_normal((T, E)).astype(np.float32), k)
+        _, _, s2r, r2s = O.permute_maps(idx, E)
+        xp, _ = O.permute_rows(x, None, r2s, k)
+        assert np.array_equal(O.combine(xp, s2r, T, k, True), (k * x).astype(np.float32))
+
+
+# ---------------------------------------------------------------- forward
+
+def test_forward_matches_dense_formulation_fp32():
+    for seed, (T, d, E, k, f) in enumerate([(40, 16, 6, 2, 8), (31, 24, 8, 3, 16), (20, 8, 4, 4, 8)]):
+        w, a = _tiny(T=T, d=d, E=E, k=k, f=f, seed=20 + seed, bias=(seed == 1))
+        o = O.layer_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], k, a["bias"], a["noise"],
+                            bf16=False)
+        ref = brute.dense_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], k, a["bias"],
+                                  a["noise"], logits=o["logits"])
+        assert np.array_equal(o["topk_idx"], ref["sel"])
+        scale = np.max(np.abs(ref["y"]))
+        assert np.max(np.abs(o["y"] - ref["y"])) <= 1e-5 * scale
+        # logits from fp64 dot agree closely with the fp32 chain
+        ref2 = brute.dense_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], k, a["bias"], a["noise"])
+        assert np.max(np.abs(ref2["logits"] - o["logits"])) < 1e-5
+
+
+def test_forward_single_expert_is_dense_swiglu_with_bf16_storage():
+    import torch
+    r = _rng(6)
+    T, d, f = 37, 32, 48
+    x = O.to_bf16(r.standard_normal((T, d)).astype(np.float32))
+    wgu = O.to_bf16((r.standard_normal((1, 2 * f, d)) / math.sqrt(d)).astype(np.float32))
+    wd = O.to_bf16((r.standard_normal((1, d, f)) / math.sqrt(f)).astype(np.float32))
+    wr = np.zeros((1, d), np.float32)
+    o = O.layer_forward(x, wr, wgu, wd, 1, bf16=True)
+    assert np.all(o["topk_w"] == 1.0)
+
+    def bf(v):
+        return torch.from_numpy(np.asarray(v, np.float64)).to(torch.float32).to(
+            torch.bfloat16).to(torch.float64).numpy()
+
+    X = x.astype(np.float64)
+    g = bf(X @ wgu[0, :f].astype(np.float64).T)
+    u = bf(X @ wgu[0, f:].astype(np.float64).T)
+    h = bf(torch.nn.functional.silu(torch.from_numpy(g)).numpy() * u)
+    y = bf(h @ wd[0].astype(np.float64).T)
+    assert np.array_equal(o["y"], y.astype(np.float32))
+    assert np.array_equal(o["h"], h.astype(np.float32))
+
+
+# ---------------------------------------------------------------- backward
+
+def _fwd_bwd(a, k, bf16):
+    o = O.layer_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], k, a["bias"], a["noise"], bf16=bf16)
+    b = O.layer_backward(o, a["x"], a["w_r"], a["w_gu"], a["w_down"], a["dy"], k, bf16=bf16)
+    return o, b
+
+
+@pytest.mark.parametrize("shape", [(30, 16, 6, 2, 8), (25, 8, 4, 4, 12), (18, 12, 8, 1, 8)])
+def test_backward_matches_torch_autograd_fp32(shape):
+    T, d, E, k, f = shape
+    w, a = _tiny(T=T, d=d, E=E, k=k, f=f, seed=40 + T, noise=True)
+    o, b = _fwd_bwd(a, k, False)
+    ref = brute.torch_dense_grads(a["x"], a["w_r"], a["w_gu"], a["w_down"], a["dy"], o["topk_idx"],
+                                  a["bias"], a["noise"])
+    for key, got in [("dx", b["dx"]), ("dw_r", b["dw_r"]), ("dw_gu", b["dw_gu"]),
+                     ("dw_down", b["dw_down"]), ("d_logits", b["d_logits"])]:
+        scale = max(1e-12, np.max(np.abs(ref[key])))
+        err = np.max(np.abs(got - ref[key]))
+        assert err <= 2e-5 * scale, (key, err, scale)
+
+
+def test_backward_finite_differences_fp64_dense():
+    # central differences of sum(Y*dY) on the fp64 dense formulation, for a few
+    # entries of each weight, against the oracle's fp32-stored gradients
+    T, d, E, k, f = 12, 8, 4, 2, 6
+    w, a = _tiny(T=T, d=d, E=E, k=k, f=f, seed=77)
+    o, b = _fwd_bwd(a, k, False)
+    dy = a["dy"].astype(np.float64)
+
+    def loss(**over):
+        args = {n: a[n].astype(np.float64) for n in ("x", "w_r", "w_gu", "w_down")}
+        args.update(over)
+        ref = brute.dense_forward(args["x"], args["w_r"], args["w_gu"], args["w_down"], k,
+                                  logits=None)
+        assert np.array_equal(ref["sel"], o["topk_idx"])
+        return np.sum(ref["y"] * dy)
+
+    eps = 1e-6
+    r = _rng(8)
+    for name, grad in [("w_gu", b["dw_gu"]), ("w_down", b["dw_down"]), ("w_r", b["dw_r"]),
+                       ("x", b["dx"])]:
+        base = a[name].astype(np.float64)
+        for _ in range(4):
+            pos = tuple(int(r.integers(0, s)) for s in base.shape)
+            p = base.copy(); p[pos] += eps
+            m = base.copy(); m[pos] -= eps
+            fd = (loss(**{name: p}) - loss(**{name: m})) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-4 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def test_backward_invariants():
+    w, a = _tiny(T=64, d=16, E=8, k=2, f=8, seed=9, bias=True, bf16=True)
+    o, b = _fwd_bwd(a, 2, True)
+    # softmax Jacobian: each token's logit gradients sum to zero
+    assert np.all(np.abs(b["d_logits"].astype(np.float64).sum(1))
+                  <= 1e-6 * (1 + np.abs(b["d_logits"]).sum(1)))
+    # unselected logits get exactly zero
+    mask = np.ones_like(b["d_logits"], bool)
+    np.put_along_axis(mask, o["topk_idx"].astype(np.int64), False, axis=1)
+    assert np.all(b["d_logits"][mask] == 0)
+    # empty experts have exactly zero weight gradients (the zipf bias leaves some)
+    empty = np.where(o["counts"] == 0)[0]
+    assert len(empty) > 0
+    assert np.all(b["dw_gu"][empty] == 0) and np.all(b["dw_down"][empty] == 0)
+    # d_row_scale is <dY_t, unscaled expert output row>
+    e_of = O.expert_of_rows(o["offsets"], np.arange(len(o["w_perm"])))
+    for r_ in range(0, len(e_of), 7):
+        y_un = o["h"][r_].astype(np.float64) @ a["w_down"][e_of[r_]].astype(np.float64).T
+        t = o["row_to_slot"][r_] // 2
+        ref = np.dot(a["dy"][t].astype(np.float64), y_un)
+        assert abs(ref - b["d_row_scale"][r_]) <= 1e-5 * (1 + abs(ref))
+    # linearity in dY: doubling dY doubles every gradient exactly
+    b2 = O.layer_backward(o, a["x"], a["w_r"], a["w_gu"], a["w_down"], 2 * a["dy"], 2, bf16=True)
+    for key in ("dx", "dw_gu", "dw_down", "dw_r", "d_logits", "d_row_scale", "dx_perm", "dgu"):
+        assert np.array_equal(b2[key], 2 * b[key]), key
+    # stored activations are bf16 values; fp32 gradients are not all bf16 values
+    for key in ("dx", "dgu", "dx_perm"):
+        assert np.array_equal(O.to_bf16(b[key]), b[key])
+    assert not np.array_equal(O.to_bf16(b["dw_gu"]), b["dw_gu"])
+
+
+def test_bf16_rounding_points_stay_close_to_fp32_path():
+    w, a = _tiny(T=48, d=32, E=4, k=2, f=32, seed=13, bf16=True)
+    o1, b1 = _fwd_bwd(a, 2, True)
+    o2, b2 = _fwd_bwd(a, 2, False)
+    assert np.array_equal(o1["topk_idx"], o2["topk_idx"])
+    for key, tol in [("y", 0.05), ("dx", 0.05), ("dw_gu", 0.05), ("dw_down", 0.05)]:
+        src = o1 if key == "y" else b1
+        ref = o2 if key == "y" else b2
+        rel = np.linalg.norm(src[key] - ref[key]) / np.linalg.norm(ref[key])
+        assert rel < tol, (key, rel)
+        assert rel > 0
+
+
+# ---------------------------------------------------------------- sampled variants
+
+def test_sampled_variants_agree_with_full_oracle():
+    w, a = _tiny(T=80, d=32, E=4, k=2, f=16, seed=14, bf16=True)
+    o, b = _fwd_bwd(a, 2, True)
+    rows = np.array([0, 3, 17, 50, 99, 159])
+    gu, h, y = O.ffn_fwd_sampled_rows(o["x_perm"], o["offsets"], a["w_gu"], a["w_down"],
+                                      o["w_perm"], rows)
+    np.testing.assert_allclose(gu, o["gu"][rows], atol=1e-2)
+    np.testing.assert_allclose(y, o["y_perm"][rows], atol=1e-2)
+    dgu, dx, drs = O.ffn_bwd_sampled_rows(o["x_perm"], o["offsets"], a["w_gu"], a["w_down"],
+                                          o["w_perm"], b["dy_perm"], rows)
+    np.testing.assert_allclose(dgu, b["dgu"][rows], atol=1e-2)
+    np.testing.assert_allclose(dx, b["dx_perm"][rows], atol=1e-2)
+    np.testing.assert_allclose(drs, b["d_row_scale"][rows], rtol=1e-5, atol=1e-5)
+    for e in range(4):
+        cols = np.array([0, 5, 15])
+        dg, du, dd = O.weight_grads_sampled_cols(o["x_perm"], o["offsets"], a["w_gu"], a["w_down"],
+                                                 o["w_perm"], b["dy_perm"], e, cols)
+        np.testing.assert_allclose(dg, b["dw_gu"][e][cols], rtol=1e-4, atol=1e-3)
+        np.testing.assert_allclose(du, b["dw_gu"][e][16 + cols], rtol=1e-4, atol=1e-3)
+        np.testing.assert_allclose(dd, b["dw_down"][e][:, cols], rtol=1e-4, atol=1e-3)
