@@ -1,0 +1,198 @@
+"""Benchmark: MoE expert block forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+                    [--no-cpu-baseline] [--profile-steps N]
+
+A step is one full pass of the hot path over one batch of synthetic tokens:
+router logits -> top-k/softmax -> permute -> grouped gate/up GEMM + SwiGLU ->
+grouped down GEMM + row scale -> combine, then combine backward -> grouped FFN
+backward (dGU with dSwiGLU, dX, dW_down, dW_gate_up) -> route backward ->
+router backward -> permute backward.  Inputs are resident in HBM before the
+timed region starts.
+
+Prints one JSON line.  Besides throughput it reports the dominant kernel's
+roofline (algorithmic FLOPs per launch / its average launch time, measured with
+HIP events on the stream the kernel runs on) and the CPU oracle's throughput on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+METRIC = "MoE layer fwd+bwd tokens/s + grouped-GEMM % bf16 MFMA peak (gpt-oss-20b-like)"
+
+
+def gemm_flops(R, d, f):
+    """Algorithmic FLOPs of each grouped GEMM launch (routed rows only)."""
+    return {
+        "gg_fwd_gate_up_swiglu": 4.0 * R * d * f,
+        "gg_fwd_down_scale": 2.0 * R * d * f,
+        "gg_bwd_dh_dswiglu": 2.0 * R * d * f,
+        "gg_bwd_dx": 4.0 * R * d * f,
+        "gg_bwd_dw_down": 2.0 * R * d * f,
+        "gg_bwd_dw_gate_up": 4.0 * R * d * f,
+    }
+
+
+def cpu_baseline(w, a, sample_tokens):
+    """Oracle fwd+bwd on the first `sample_tokens` tokens of the same inputs."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    s = slice(0, sample_tokens)
+    x, dy = a["x"][s], a["dy"][s]
+    noise = None if a["noise"] is None else a["noise"][s]
+    t0 = time.perf_counter()
+    o = O.layer_forward(x, a["w_r"], a["w_gu"], a["w_down"], w.k, a["bias"], noise, bf16=True)
+    O.layer_backward(o, x, a["w_r"], a["w_gu"], a["w_down"], dy, w.k, bf16=True)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "first %d of %d tokens of the same workload, one fwd+bwd, %.1f s" %
+                      (sample_tokens, w.T, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--profile-steps", type=int, default=5,
+                    help="extra steps with per-kernel event timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    from mixture_experts_layer_03_amd import inputs as I
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+
+    w = I.BY_KEY[args.workload]
+    if w.routing == "prerouted":
+        print("pick a routed workload (c2, c3, c5)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating inputs for %s" % w.name, file=sys.stderr, flush=True)
+    a = I.make_inputs(w)
+
+    def up(v, bf=True):
+        if v is None:
+            return None
+        if bf:
+            return torch.from_numpy(I.bf16_bits(v).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+
+    x, wr, wgu, wd, dy = (up(a[n]) for n in ("x", "w_r", "w_gu", "w_down", "dy"))
+    bias, noise = up(a["bias"], False), up(a["noise"], False)
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        blk.forward(x, wr, wgu, wd, bias, noise)
+        blk.backward(x, wr, wgu, wd, dy)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / elapsed
+
+    # per-kernel durations: events around each launch, on the launch stream
+    kernels = {}
+    if args.profile_steps > 0:
+        abi.moe_timing_reset()
+        abi.moe_timing_enable(True)
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        abi.moe_timing_enable(False)
+        names = ["router_logits", "route_topk", "permute_hist", "permute_scan", "permute_place",
+                 "permute_rows", "tile_prefix", "gg_fwd_gate_up_swiglu", "gg_fwd_down_scale",
+                 "combine", "combine_bwd", "gg_bwd_dh_dswiglu", "drs_reduce", "gg_bwd_dx",
+                 "gg_bwd_dw_down", "gg_bwd_dw_gate_up", "route_bwd", "router_dx",
+                 "router_dw_partial", "router_dw_reduce", "permute_bwd"]
+        for n in names:
+            ms, cnt = abi.moe_timing_query(n)
+            if cnt:
+                kernels[n] = {"ms_total": ms, "launches": cnt}
+        for n, v in kernels.items():
+            v["avg_us"] = 1e3 * v["ms_total"] / max(1, v["launches"])
+        abi.moe_timing_reset()
+
+    R = w.R
+    flops = gemm_flops(R, w.d, w.f)
+    gemm_us = {n: kernels[n]["avg_us"] for n in flops if n in kernels}
+    roofline = None
+    gemm_frac = None
+    if gemm_us:
+        dom = max(gemm_us, key=gemm_us.get)
+        achieved = flops[dom] / (gemm_us[dom] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_launch_us": round(gemm_us[dom], 1),
+                    "algorithmic_flop_per_launch": flops[dom]}
+        tot_f = sum(flops[n] for n in gemm_us)
+        tot_t = sum(gemm_us[n] for n in gemm_us) * 1e-6
+        gemm_frac = tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, a, min(args.cpu_sample_tokens, w.T))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "d_model": w.d, "experts": w.E,
+                   "top_k": w.k, "d_ff": w.f, "routed_rows": R, "passes": "fwd+bwd"},
+        "grouped_gemm_frac_of_bf16_peak": None if gemm_frac is None else round(gemm_frac, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

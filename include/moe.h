@@ -1,0 +1,239 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) MoE expert block.
+ *
+ * The block, as the pages state the problem: a flat batch of token hidden
+ * states goes through an fp32 router and a per-token top-k; the selected
+ * (token, expert) rows are sorted by expert; each expert runs its SwiGLU FFN as
+ * one grouped matmul over its contiguous rows; the rows come back to their
+ * token in the same order, weighted by the top-k probabilities, and are summed
+ * ("Halo's 2.8x over TRL is not a kernel, and its own benchmark proves it",
+ * section "Where the gap actually is", EP token-routing figure and the EP
+ * forward path described under it).  The backward computes the matching
+ * activation, expert-weight and router gradients, with the routing adjoint
+ * written as gathers, free of atomic adds ("Halo: Frontier-Lab Training for
+ * Everyone", section "Some of the hard problems along the way").
+ *
+ * Conventions for every entry point:
+ *  - Status: returns MOE_OK (0) or a negative MOE_ERR_*.  Arguments are
+ *    validated on the host before anything is launched; an invalid call
+ *    launches nothing and writes nothing.  moe_last_error() gives a message
+ *    for the calling thread's last failure.
+ *  - Memory: every tensor argument is a caller-owned DEVICE pointer (current
+ *    HIP device), row-major and contiguous, 16-byte aligned.  The library
+ *    never allocates device memory in these calls; scratch comes from the
+ *    caller through a workspace pointer sized by the matching *_workspace_size
+ *    query.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream).  Every call
+ *    is asynchronous on that stream and makes no device-to-host copy; per
+ *    expert counts and offsets stay on the device.
+ *  - dtype: MOE_BF16 or MOE_F32 selects the storage type of activations and
+ *    expert weights (x, w_r, w_gu, w_down, x_perm, gu, h, y_perm, y, dy, ...).
+ *    Routing tensors are always fp32 / int32; weight and router gradients are
+ *    always fp32.  MOE_F32 covers the forward path and the copy-type backward
+ *    steps; moe_grouped_ffn_bwd and moe_router_logits_bwd need MOE_BF16.
+ *  - Shapes: T >= 0 tokens, d = d_model, f = d_ff, E experts, k = top-k;
+ *    1 <= k <= E <= 1024, k <= 32; d and f positive multiples of 8;
+ *    R = T*k routed rows, R < 2^31.  Element offsets are computed in 64 bits.
+ *  - Determinism: no floating-point atomics anywhere; repeated calls on the
+ *    same inputs give bitwise identical results.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1)   /* null pointer, bad size, misalignment */
+#define MOE_ERR_UNSUPPORTED (-2)   /* dtype / shape outside the supported set */
+#define MOE_ERR_WORKSPACE   (-3)   /* workspace missing or too small */
+#define MOE_ERR_HIP         (-4)   /* HIP launch or runtime error */
+
+#define MOE_F32  0
+#define MOE_BF16 1
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+/* Static description of a status code. */
+const char *moe_strerror(int status);
+/* Message for the calling thread's last failed call ("" if none). */
+const char *moe_last_error(void);
+
+/* ---------------------------------------------------------------- router */
+
+/*
+ * Router logits in fp32.  The pages fix the precision ("fp32 router logits" in
+ * the EP forward path, section "Where the gap actually is"; `fp32_router:
+ * true` in the recipe of section "The small-hardware end").  The summation
+ * order is fixed as part of the definition so that top-k decisions are
+ * reproducible bit for bit:
+ *   logits[t,e] = ((fma chain over c = 0..d-1 of x[t,c]*w_r[e,c], from +0)
+ *                  + bias[e]) + logit_add[t,e]
+ * x: [T,d] (dtype), w_r: [E,d] (dtype), bias: [E] fp32 or NULL,
+ * logit_add: [T,E] fp32 or NULL (additive noise), logits: [T,E] fp32 (out).
+ */
+int moe_router_logits(const void *x, const void *w_r, const float *bias,
+                      const float *logit_add, int dtype, int64_t T, int d, int E,
+                      float *logits, void *stream);
+
+/*
+ * Per-token top-k and the combine weights (the "per-token top-k router" and
+ * "weighted by the top-k probabilities" of the EP token-routing figure).
+ * topk_idx[t,0..k-1]: the k largest logits of token t, by value descending;
+ * equal values go to the lower expert id (-0 equals +0).  topk_w[t,j] =
+ * softmax over the k selected logits.  Logits must be finite.
+ * logits: [T,E] fp32; topk_idx: [T,k] int32 (out); topk_w: [T,k] fp32 (out).
+ */
+int moe_route(const float *logits, int64_t T, int E, int k,
+              int32_t *topk_idx, float *topk_w, void *stream);
+
+/* ---------------------------------------------------------------- permute */
+
+size_t moe_permute_workspace_size(int64_t T, int E, int k);
+
+/*
+ * Sorts the selected (token, expert) slots by expert -- the single-GPU core of
+ * the EP dispatch, which hands each expert its tokens "sorted by expert" (EP
+ * token-routing figure).  Slot s = t*k + j.  Rows are expert-major; inside an
+ * expert, slots keep ascending order.  Outputs:
+ *   counts[E], offsets[E+1] (offsets[0]=0, offsets[E]=R), slot_to_row[R],
+ *   row_to_slot[R] (int32);
+ *   x_perm[r] = x[row_to_slot[r] / k]   (exact copy; x may be NULL to skip),
+ *   w_perm[r] = topk_w[row_to_slot[r]]  (topk_w and w_perm may be NULL).
+ * topk_idx entries must lie in [0,E) and a token's k entries must be distinct.
+ * ws: device workspace of at least moe_permute_workspace_size(T,E,k) bytes.
+ */
+int moe_permute(const void *x, const int32_t *topk_idx, const float *topk_w, int dtype,
+                int64_t T, int d, int E, int k,
+                int32_t *counts, int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot,
+                void *x_perm, float *w_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- experts */
+
+size_t moe_grouped_ffn_workspace_size(int64_t R, int E, int d, int f, int dtype);
+
+/*
+ * Grouped SwiGLU expert FFN over rows sorted by expert ("grouped GEMM and
+ * fused SwiGLU", "Halo: Frontier-Lab Training for Everyone", section "Novel
+ * model integration example"; experts stored as single 3-D weight tensors,
+ * section "One trainer architecture, one parallelism stack").  For each
+ * expert e and each of its rows r in [offsets[e], offsets[e+1]):
+ *   [g | u] = x_perm[r] . w_gu[e]^T        (gate rows 0..f-1, up rows f..2f-1)
+ *   gu[r]   = store([g | u])                (store = dtype rounding)
+ *   h[r]    = store(silu(gu_g) * gu_u),  silu(v) = v / (1 + exp(-v))
+ *   y_perm[r] = store(row_scale[r] * (h[r] . w_down[e]^T))   (row_scale NULL = 1)
+ * fp32 accumulation.  Experts with no rows are skipped.
+ * x_perm: [R,d]; w_gu: [E,2f,d]; w_down: [E,d,f]; row_scale: [R] fp32 or NULL;
+ * gu: [R,2f] (out, or NULL if not needed for a backward); h: [R,f] (out);
+ * y_perm: [R,d] (out).  offsets: [E+1] int32 on the device, offsets[E] = R.
+ */
+int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, int E, int64_t R,
+                        int d, int f, const void *w_gu, const void *w_down,
+                        const float *row_scale, int dtype, void *gu, void *h, void *y_perm,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of moe_grouped_ffn_fwd (expert weights receive gradients: the
+ * "expert gradient all-to-all" that LoRA skips, section "One trainer
+ * architecture, one parallelism stack", is the exchange of these).  Per row r
+ * of expert e, with w = row_scale[r] (1 if NULL):
+ *   Gd          = dy_perm[r] . w_down[e]                      (fp32)
+ *   d_row_scale[r] = sum_c h[r,c] * Gd[c]                      (fp32)
+ *   dH = w*Gd;  s = sigmoid(g);  dg = dH*u*s*(1 + g*(1-s));  du = dH*g*s
+ *   dgu[r]      = store([dg | du])
+ *   dx_perm[r]  = store(dgu[r] . w_gu[e])
+ *   dw_down[e]  = sum_r store(w*dy_perm[r])^T (x) h[r]          (fp32, [E,d,f])
+ *   dw_gu[e]    = sum_r dgu[r]^T (x) x_perm[r]                  (fp32, [E,2f,d])
+ * (g, u = the stored gu; experts with no rows get exactly zero dw.)
+ * Inputs: x_perm [R,d], gu [R,2f], h [R,f] (saved by the forward), dy_perm [R,d].
+ * Outputs: dgu [R,2f], dx_perm [R,d], dw_gu, dw_down, d_row_scale [R] (or NULL).
+ * dtype must be MOE_BF16.
+ */
+int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const void *h,
+                        const int32_t *offsets, int E, int64_t R, int d, int f,
+                        const void *w_gu, const void *w_down, const float *row_scale,
+                        const void *dy_perm, int dtype, void *dgu, void *dx_perm,
+                        float *dw_gu, float *dw_down, float *d_row_scale,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- combine */
+
+/*
+ * Returns each row to its token and sums ("the same rows in the same order",
+ * EP token-routing figure; the weights were applied by the down projection):
+ *   y[t] = store(sum over j = 0..k-1, ascending, of y_perm[slot_to_row[t*k+j]])
+ * with an fp32 running sum.  y_perm: [R,d]; slot_to_row: [R]; y: [T,d] (out).
+ */
+int moe_combine(const void *y_perm, const int32_t *slot_to_row, int dtype,
+                int64_t T, int d, int k, void *y, void *stream);
+
+/*
+ * Adjoint of moe_combine: a copy of each token's gradient to its k rows,
+ *   dy_perm[slot_to_row[t*k+j]] = dy[t].
+ */
+int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int dtype,
+                    int64_t T, int d, int k, void *dy_perm, void *stream);
+
+/*
+ * Adjoint of the row permutation, as a gather (no atomic adds; "Halo:
+ * Frontier-Lab Training for Everyone", section "Some of the hard problems
+ * along the way"):
+ *   dx[t] = store(sum over j ascending of dx_perm[slot_to_row[t*k+j]] + dx_add[t])
+ * with an fp32 running sum; dx_add: [T,d] fp32 or NULL (the router's share).
+ */
+int moe_permute_bwd(const void *dx_perm, const int32_t *slot_to_row, const float *dx_add,
+                    int dtype, int64_t T, int d, int k, void *dx, void *stream);
+
+/* ---------------------------------------------------------------- router bwd */
+
+/*
+ * Adjoint of the softmax over the selected logits.  With g_j =
+ * d_row_scale[slot_to_row[t*k+j]] (the gradient of the loss with respect to
+ * topk_w[t,j]):
+ *   d_topk_w[t,j] = g_j                         (d_topk_w may be NULL)
+ *   d_logits[t,topk_idx[t,j]] = w_j * (g_j - sum_i w_i g_i), 0 elsewhere.
+ * All fp32; d_logits: [T,E] (out, fully written).
+ */
+int moe_route_bwd(const int32_t *topk_idx, const float *topk_w, const float *d_row_scale,
+                  const int32_t *slot_to_row, int64_t T, int E, int k,
+                  float *d_topk_w, float *d_logits, void *stream);
+
+size_t moe_router_logits_bwd_workspace_size(int64_t T, int d, int E);
+
+/*
+ * Adjoint of the router linear map (bias and added noise carry no gradient):
+ *   dx_router = d_logits . w_r    ([T,d] fp32, or NULL to skip)
+ *   dw_r      = d_logits^T . x    ([E,d] fp32, or NULL to skip)
+ * fp32 accumulation in a fixed order.  dtype must be MOE_BF16.
+ */
+int moe_router_logits_bwd(const void *x, const void *w_r, const float *d_logits, int dtype,
+                          int64_t T, int d, int E, float *dx_router, float *dw_r,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- timing */
+
+/*
+ * Per-kernel timing for measurement.  While enabled, every kernel launch is
+ * bracketed by a pair of HIP events on its own stream.  moe_timing_query
+ * waits for the recorded events and returns, for launches recorded under
+ * `name` (NULL = all), the summed duration in milliseconds and the launch
+ * count.  moe_timing_reset drops all records.  Off by default.  Launch names:
+ * router_logits, route_topk, permute_hist, permute_scan, permute_place,
+ * permute_rows, tile_prefix, gg_fwd_gate_up_swiglu, gg_fwd_down_scale,
+ * combine, combine_bwd, gg_bwd_dh_dswiglu, drs_reduce, gg_bwd_dx,
+ * gg_bwd_dw_down, gg_bwd_dw_gate_up, route_bwd, router_dx, router_dw_partial,
+ * router_dw_reduce, router_dw_zero, permute_bwd, ffn_gu_f32, ffn_down_f32.
+ */
+int moe_timing_enable(int on);
+int moe_timing_reset(void);
+int moe_timing_query(const char *name, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,423 @@
+// Token permutation into per-expert segments, combine, and their adjoints.
+//
+// The pages: each expert runs "a grouped matmul over tokens sorted by expert",
+// and the rows come back to their token "in the same order, weighted by the
+// top-k probabilities" ("Halo's 2.8x over TRL is not a kernel, and its own
+// benchmark proves it", section "Where the gap actually is", EP token-routing
+// figure).  On one GPU the dispatch all-to-all reduces to this row permutation.
+// The backward is written as gathers, with no atomic adds ("Halo: Frontier-Lab
+// Training for Everyone", section "Some of the hard problems along the way").
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ maps
+//
+// Slots s = t*k + j are cut into chunks of `chunk` consecutive slots.
+//  1. k_hist:  per-chunk expert histogram in LDS (integer atomics: the counts
+//              do not depend on their order).
+//  2. k_scan:  one block scans the histograms in expert-major order, giving
+//              every (expert, chunk) its first row, plus counts and offsets.
+//  3. k_place: inside a chunk, each wave walks its quarter in slot order,
+//              64 slots at a time; the lanes holding the same expert are found
+//              with one ballot per expert-id bit, and ranked by lane order.
+//              Row = base(expert, chunk) + earlier waves + earlier steps + rank.
+// Slots whose expert id is outside [0,E) get no row (slot_to_row = -1).
+
+struct PermPlan {
+  int64_t R;
+  int nchunk;
+  int chunk;   // multiple of 256
+};
+
+static PermPlan perm_plan(int64_t T, int k) {
+  PermPlan p;
+  p.R = T * k;
+  int64_t nchunk = (p.R + 2047) / 2048;
+  if (nchunk > 2048) nchunk = 2048;
+  if (nchunk < 1) nchunk = 1;
+  int64_t chunk = (p.R + nchunk - 1) / nchunk;
+  chunk = (chunk + 255) / 256 * 256;
+  if (chunk < 256) chunk = 256;
+  p.chunk = (int)chunk;
+  p.nchunk = (int)((p.R + chunk - 1) / chunk);
+  if (p.nchunk < 1) p.nchunk = 1;
+  return p;
+}
+
+__global__ __launch_bounds__(256) void k_hist(const int32_t *__restrict__ idx, int64_t R, int E,
+                                              int chunk, int nchunk, int32_t *__restrict__ hist) {
+  __shared__ int h[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t beg = (int64_t)blockIdx.x * chunk;
+  const int64_t end = min(beg + chunk, R);
+  for (int64_t s = beg + threadIdx.x; s < end; s += 256) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)e * nchunk + blockIdx.x] = h[e];
+}
+
+// Exclusive scan of n = E*nchunk ints (expert-major) by one block of 1024.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ hist, int E, int nchunk,
+                                               int32_t *__restrict__ base,
+                                               int32_t *__restrict__ counts,
+                                               int32_t *__restrict__ offsets) {
+  __shared__ int part[1024];
+  const int64_t n = (int64_t)E * nchunk;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t b = threadIdx.x * per;
+  const int64_t e_ = min(b + per, n);
+  int sum = 0;
+  for (int64_t i = b; i < e_; ++i) sum += hist[i];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = threadIdx.x ? part[threadIdx.x - 1] : 0;
+  for (int64_t i = b; i < e_; ++i) {
+    if (i % nchunk == 0) offsets[i / nchunk] = run;   // first chunk of expert i/nchunk
+    base[i] = run;
+    run += hist[i];
+  }
+  if (threadIdx.x == 1023) offsets[E] = part[1023];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int c = 0;
+    for (int ch = 0; ch < nchunk; ++ch) c += hist[(int64_t)e * nchunk + ch];
+    counts[e] = c;
+  }
+}
+
+__device__ __forceinline__ uint64_t peers_of(int e, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return valid ? m : 0ull;
+}
+
+__global__ __launch_bounds__(256) void k_place(const int32_t *__restrict__ idx, int64_t R, int E,
+                                               int chunk, int nchunk, int nbits,
+                                               const int32_t *__restrict__ base,
+                                               int32_t *__restrict__ slot_to_row,
+                                               int32_t *__restrict__ row_to_slot) {
+  __shared__ int cnt[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < 4 * E; e += 256) cnt[e / E][e % E] = 0;
+  __syncthreads();
+  const int64_t cbeg = (int64_t)blockIdx.x * chunk;
+  const int quarter = chunk / 4;   // multiple of 64
+  const int64_t wbeg = cbeg + (int64_t)wave * quarter;
+  const int64_t wend = min(wbeg + quarter, R);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // pass 1: per-wave counts
+  for (int64_t s0 = wbeg; s0 < wend; s0 += 64) {
+    const int64_t s = s0 + lane;
+    int e = (s < wend) ? idx[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    const uint64_t m = peers_of(e, valid, nbits);
+    if (valid && (m & lt) == 0) cnt[wave][e] += __popcll(m);
+  }
+  __syncthreads();
+  // turn counts into per-wave starting offsets inside the chunk
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = 0;
+    for (int w = 0; w < 4; ++w) {
+      const int c = cnt[w][e];
+      cnt[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // pass 2: ranks and placement
+  for (int64_t s0 = wbeg; s0 < wend; s0 += 64) {
+    const int64_t s = s0 + lane;
+    int e = (s < wend) ? idx[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    const uint64_t m = peers_of(e, valid, nbits);
+    if (s < wend) {
+      if (valid) {
+        const int before = cnt[wave][e];
+        const int rank = __popcll(m & lt);
+        const int row = base[(int64_t)e * nchunk + blockIdx.x] + before + rank;
+        slot_to_row[s] = row;
+        row_to_slot[row] = (int32_t)s;
+        if (rank == 0) cnt[wave][e] = before + __popcll(m);
+      } else {
+        slot_to_row[s] = -1;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ rows
+//
+// One wave per token; lanes stride over the row in 16-byte chunks.  A token
+// row is read once and written to its k rows (forward permute, combine bwd),
+// or its k rows are gathered and summed in fp32, j ascending (combine,
+// permute bwd).
+
+template <typename T>
+struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+__device__ __forceinline__ void unpack16(const u32x4_t v, float *f, const bf16_t *) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(v[i] & 0xffffu);
+    f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+  }
+}
+__device__ __forceinline__ void unpack16(const u32x4_t v, float *f, const float *) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+}
+__device__ __forceinline__ u32x4_t pack16(const float *f, const bf16_t *) {
+  u32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+__device__ __forceinline__ u32x4_t pack16(const float *f, const float *) {
+  u32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+  return v;
+}
+
+// token served by this wave (wave-uniform, so per-token loads become scalar)
+__device__ __forceinline__ int64_t wave_token() {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  return (int64_t)blockIdx.x * 4 + w;
+}
+
+// src[t] -> dst[slot_to_row[t*k+j]] for j < k (src may be NULL: no rows);
+// optional w_dst[row] = w_src[t*k+j]
+template <typename T>
+__global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
+                                                      const int32_t *__restrict__ slot_to_row,
+                                                      const float *__restrict__ w_src, int64_t ntok,
+                                                      int d, int k, T *__restrict__ dst,
+                                                      float *__restrict__ w_dst) {
+  const int64_t t = wave_token();
+  if (t >= ntok) return;
+  const int lane = threadIdx.x & 63;
+  if (w_dst && lane < k) {
+    const int r = slot_to_row[t * k + lane];
+    if (r >= 0) w_dst[r] = w_src[t * k + lane];
+  }
+  if (!src) return;
+  const int nvec = d * (int)sizeof(T) / 16;
+  const u32x4_t *s = reinterpret_cast<const u32x4_t *>(src + t * d);
+  for (int c = lane; c < nvec; c += 64 * 2) {
+    const int c2 = c + 64;
+    const u32x4_t v0 = s[c];
+    u32x4_t v1 = {0, 0, 0, 0};
+    if (c2 < nvec) v1 = s[c2];
+    for (int j = 0; j < k; ++j) {
+      const int r = slot_to_row[t * k + j];
+      if (r < 0) continue;
+      u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + (int64_t)r * d);
+      o[c] = v0;
+      if (c2 < nvec) o[c2] = v1;
+    }
+  }
+}
+
+// dst[t] = store(sum_j src[slot_to_row[t*k+j]] (+ add[t]))
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
+                                                    const int32_t *__restrict__ slot_to_row,
+                                                    const float *__restrict__ add, int64_t ntok,
+                                                    int d, int k, T *__restrict__ dst) {
+  constexpr int N = Vec16<T>::N;
+  const int64_t t = wave_token();
+  if (t >= ntok) return;
+  const int lane = threadIdx.x & 63;
+  const int nvec = d * (int)sizeof(T) / 16;
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = slot_to_row[t * k + j];
+      if (r < 0) continue;
+      const u32x4_t v = reinterpret_cast<const u32x4_t *>(src + (int64_t)r * d)[c];
+      float f[N];
+      unpack16(v, f, (const T *)nullptr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += f[i];
+    }
+    if (add) {
+      const float *a = add + t * d + (int64_t)c * N;
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(a + i);
+        acc[i] += a4.x;
+        acc[i + 1] += a4.y;
+        acc[i + 2] += a4.z;
+        acc[i + 3] += a4.w;
+      }
+    }
+    reinterpret_cast<u32x4_t *>(dst + t * d)[c] = pack16(acc, (const T *)nullptr);
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+// ====================================================================== C ABI
+
+static int check_rows(const char *fn, int dtype, int64_t T, int d, int k) {
+  MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "%s: T < 0", fn);
+  MOE_REQUIRE(dtype == MOE_BF16 || dtype == MOE_F32, MOE_ERR_UNSUPPORTED, "%s: dtype %d", fn,
+              dtype);
+  MOE_REQUIRE(d > 0 && d % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: d=%d not a positive multiple of 8",
+              fn, d);
+  MOE_REQUIRE(k >= 1 && k <= kMaxTopK, MOE_ERR_UNSUPPORTED, "%s: k=%d", fn, k);
+  MOE_REQUIRE(T * (int64_t)k < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "%s: T*k >= 2^31", fn);
+  return MOE_OK;
+}
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  PermPlan p = perm_plan(T, k);
+  const size_t n = (size_t)E * (size_t)p.nchunk;
+  return align_up(2 * n * sizeof(int32_t), 256);
+}
+
+extern "C" int moe_permute(const void *x, const int32_t *topk_idx, const float *topk_w, int dtype,
+                           int64_t T, int d, int E, int k, int32_t *counts, int32_t *offsets,
+                           int32_t *slot_to_row, int32_t *row_to_slot, void *x_perm,
+                           float *w_perm, void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_rows("moe_permute", dtype, T, d, k);
+  if (rc) return rc;
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts && k <= E, MOE_ERR_UNSUPPORTED, "moe_permute: E=%d k=%d",
+              E, k);
+  MOE_REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "moe_permute: null counts/offsets");
+  const size_t need = moe_permute_workspace_size(T, E, k);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu",
+              ws_bytes, need);
+  if (T > 0) {
+    MOE_REQUIRE(topk_idx && slot_to_row && row_to_slot, MOE_ERR_INVALID_ARG,
+                "moe_permute: null map pointer");
+    MOE_REQUIRE(!x || (x_perm && aligned16(x) && aligned16(x_perm)), MOE_ERR_INVALID_ARG,
+                "moe_permute: x / x_perm");
+    MOE_REQUIRE(!w_perm || topk_w, MOE_ERR_INVALID_ARG, "moe_permute: w_perm needs topk_w");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  PermPlan p = perm_plan(T, k);
+  int32_t *hist = (int32_t *)ws;
+  int32_t *base = hist + (size_t)E * p.nchunk;
+  if (T == 0) {
+    // zero counts and offsets with the scan kernel over an all-zero histogram
+    MOE_LAUNCH("permute_hist", s,
+               k_hist<<<p.nchunk, 256, 0, s>>>(topk_idx, 0, E, p.chunk, p.nchunk, hist));
+    MOE_LAUNCH("permute_scan", s,
+               k_scan<<<1, 1024, 0, s>>>(hist, E, p.nchunk, base, counts, offsets));
+    return check_launch("moe_permute");
+  }
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  MOE_LAUNCH("permute_hist", s,
+             k_hist<<<p.nchunk, 256, 0, s>>>(topk_idx, p.R, E, p.chunk, p.nchunk, hist));
+  MOE_LAUNCH("permute_scan", s, k_scan<<<1, 1024, 0, s>>>(hist, E, p.nchunk, base, counts, offsets));
+  MOE_LAUNCH("permute_place", s,
+             k_place<<<p.nchunk, 256, 0, s>>>(topk_idx, p.R, E, p.chunk, p.nchunk, nbits, base,
+                                              slot_to_row, row_to_slot));
+  rc = check_launch("moe_permute(maps)");
+  if (rc) return rc;
+  if (x || w_perm) {
+    const unsigned blocks = (unsigned)((T + 3) / 4);
+    if (dtype == MOE_BF16)
+      MOE_LAUNCH("permute_rows", s,
+                 k_scatter_rows<bf16_t><<<blocks, 256, 0, s>>>(
+                     (const bf16_t *)x, slot_to_row, topk_w, T, d, k, (bf16_t *)x_perm,
+                     w_perm));
+    else
+      MOE_LAUNCH("permute_rows", s,
+                 k_scatter_rows<float><<<blocks, 256, 0, s>>>((const float *)x, slot_to_row,
+                                                              topk_w, T, d, k,
+                                                              (float *)x_perm, w_perm));
+    rc = check_launch("moe_permute(rows)");
+  }
+  return rc;
+}
+
+extern "C" int moe_combine(const void *y_perm, const int32_t *slot_to_row, int dtype, int64_t T,
+                           int d, int k, void *y, void *stream) {
+  clear_error();
+  int rc = check_rows("moe_combine", dtype, T, d, k);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(y_perm && slot_to_row && y && aligned16(y_perm) && aligned16(y), MOE_ERR_INVALID_ARG,
+              "moe_combine: null or misaligned pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    MOE_LAUNCH("combine", s,
+               k_gather_sum<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)y_perm, slot_to_row,
+                                                           nullptr, T, d, k, (bf16_t *)y));
+  else
+    MOE_LAUNCH("combine", s,
+               k_gather_sum<float><<<blocks, 256, 0, s>>>((const float *)y_perm, slot_to_row,
+                                                          nullptr, T, d, k, (float *)y));
+  return check_launch("moe_combine");
+}
+
+extern "C" int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int dtype, int64_t T,
+                               int d, int k, void *dy_perm, void *stream) {
+  clear_error();
+  int rc = check_rows("moe_combine_bwd", dtype, T, d, k);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(dy && slot_to_row && dy_perm && aligned16(dy) && aligned16(dy_perm),
+              MOE_ERR_INVALID_ARG, "moe_combine_bwd: null or misaligned pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    MOE_LAUNCH("combine_bwd", s,
+               k_scatter_rows<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)dy, slot_to_row,
+                                                             nullptr, T, d, k, (bf16_t *)dy_perm,
+                                                             nullptr));
+  else
+    MOE_LAUNCH("combine_bwd", s,
+               k_scatter_rows<float><<<blocks, 256, 0, s>>>((const float *)dy, slot_to_row,
+                                                            nullptr, T, d, k, (float *)dy_perm,
+                                                            nullptr));
+  return check_launch("moe_combine_bwd");
+}
+
+extern "C" int moe_permute_bwd(const void *dx_perm, const int32_t *slot_to_row, const float *dx_add,
+                               int dtype, int64_t T, int d, int k, void *dx, void *stream) {
+  clear_error();
+  int rc = check_rows("moe_permute_bwd", dtype, T, d, k);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(dx_perm && slot_to_row && dx && aligned16(dx_perm) && aligned16(dx) &&
+                  (!dx_add || aligned16(dx_add)),
+              MOE_ERR_INVALID_ARG, "moe_permute_bwd: null or misaligned pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    MOE_LAUNCH("permute_bwd", s,
+               k_gather_sum<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)dx_perm, slot_to_row,
+                                                           dx_add, T, d, k, (bf16_t *)dx));
+  else
+    MOE_LAUNCH("permute_bwd", s,
+               k_gather_sum<float><<<blocks, 256, 0, s>>>((const float *)dx_perm, slot_to_row,
+                                                          dx_add, T, d, k, (float *)dx));
+  return check_launch("moe_permute_bwd");
+}

@@ -1,0 +1,488 @@
+// Router: fp32 logits, wavefront top-k + softmax over the selected k, and
+// their adjoints.
+//
+// The pages: the EP forward path starts from "fp32 router logits" and a
+// per-token top-k router whose probabilities weight the returned rows ("Halo's
+// 2.8x over TRL is not a kernel, and its own benchmark proves it", section
+// "Where the gap actually is").  Routers are trained, so they get gradients.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ logits
+//
+// Block: 256 threads = 4 waves; tile = 64 tokens x (4*EPT) experts.  Lane =
+// token, wave = group of EPT experts, so a wave reads the same router weights
+// (LDS broadcast) and its own token column.  Each (t,e) output is ONE fp32
+// fma chain over c = 0..d-1 in order, then + bias, then + noise.
+constexpr int kLogitTok = 64;
+constexpr int kLogitCk = 64;
+
+template <typename T, int EPT>
+__global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
+                                                       const T *__restrict__ wr,
+                                                       const float *__restrict__ bias,
+                                                       const float *__restrict__ noise,
+                                                       int64_t ntok, int d, int E,
+                                                       float *__restrict__ logits) {
+  constexpr int EB = 4 * EPT;
+  __shared__ float xs[kLogitCk][kLogitTok + 1];
+  __shared__ __attribute__((aligned(16))) float ws[kLogitCk][EB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kLogitTok;
+  const int e0 = blockIdx.y * EB;
+  float acc[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) acc[i] = 0.0f;
+
+  for (int c0 = 0; c0 < d; c0 += kLogitCk) {
+    // x tile -> xs[c][t] (transposed)
+    for (int i = tid; i < kLogitTok * kLogitCk; i += 256) {
+      const int tt = i / kLogitCk, cc = i % kLogitCk;
+      const int64_t t = t0 + tt;
+      const int c = c0 + cc;
+      float v = 0.0f;
+      if (t < ntok && c < d) v = Store<T>::load(x + t * d + c);
+      xs[cc][tt] = v;
+    }
+    for (int i = tid; i < EB * kLogitCk; i += 256) {
+      const int ee = i / kLogitCk, cc = i % kLogitCk;
+      const int e = e0 + ee, c = c0 + cc;
+      float v = 0.0f;
+      if (e < E && c < d) v = Store<T>::load(wr + (int64_t)e * d + c);
+      ws[cc][ee] = v;
+    }
+    __syncthreads();
+    const int cn = min(kLogitCk, d - c0);
+    for (int cc = 0; cc < cn; ++cc) {
+      const float xv = xs[cc][lane];
+#pragma unroll
+      for (int i = 0; i < EPT; i += 4) {
+        const float4 w4 = *reinterpret_cast<const float4 *>(&ws[cc][wave * EPT + i]);
+        acc[i + 0] = fmaf(xv, w4.x, acc[i + 0]);
+        acc[i + 1] = fmaf(xv, w4.y, acc[i + 1]);
+        acc[i + 2] = fmaf(xv, w4.z, acc[i + 2]);
+        acc[i + 3] = fmaf(xv, w4.w, acc[i + 3]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t t = t0 + lane;
+  if (t >= ntok) return;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = e0 + wave * EPT + i;
+    if (e >= E) continue;
+    float v = acc[i];
+    if (bias) v = v + bias[e];
+    if (noise) v = v + noise[t * E + e];
+    logits[t * E + e] = v;
+  }
+}
+
+// ------------------------------------------------------------------ top-k
+//
+// A group of G = min(64, pow2ceil(E)) lanes serves one token; a wave serves
+// 64/G tokens.  Lane s of a group holds experts s, s+G, s+2G, ...  Each of the
+// k rounds takes the best unselected value of every lane and reduces it over
+// the group with xor-shuffles (greater value wins; equal values -> lower id).
+// The winner of round j is kept by lane j of the group.
+constexpr int kMaxPerLane = kMaxExperts / 64;   // 16
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int64_t ntok,
+                                               int E, int k, int32_t *__restrict__ topk_idx,
+                                               float *__restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int s = lane % G;
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G;
+  const bool live = t < ntok;
+  const int vpl = (E + G - 1) / G;
+  float val[kMaxPerLane];
+  unsigned taken = 0u;
+#pragma unroll
+  for (int v = 0; v < kMaxPerLane; ++v) {
+    const int e = s + v * G;
+    val[v] = (live && v < vpl && e < E) ? logits[t * E + e] : 0.0f;
+    if (!(v < vpl && e < E)) taken |= 1u << v;   // padding never wins
+  }
+  float my_val = 0.0f, top0 = 0.0f;
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < kMaxPerLane; ++v) {
+      if (taken & (1u << v)) continue;
+      const int e = s + v * G;
+      if (bi == 0x7fffffff || better(val[v], e, bv, bi)) {
+        bv = val[v];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oi = __shfl_xor(bi, m, 64);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi % G == s) taken |= 1u << (bi / G);
+    if (j == 0) top0 = bv;
+    if (s == j) {
+      my_val = bv;
+      my_idx = bi;
+    }
+  }
+  // softmax over the k selected values (max is the first selected)
+  float ex = (s < k) ? __expf(my_val - top0) : 0.0f;
+  float sum = ex;
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) sum += __shfl_xor(sum, m, 64);
+  if (live && s < k) {
+    topk_idx[t * k + s] = my_idx;
+    topk_w[t * k + s] = ex / sum;
+  }
+}
+
+// ------------------------------------------------------------------ route bwd
+//
+// Same grouping.  Lane j < k holds selection j: g_j = d_row_scale at its row,
+// w_j.  S = sum_i w_i g_i by a fixed xor-butterfly; each lane then writes the
+// experts it owns: w_j (g_j - S) if selected, else 0.
+template <int G>
+__global__ __launch_bounds__(256) void k_route_bwd(const int32_t *__restrict__ topk_idx,
+                                                   const float *__restrict__ topk_w,
+                                                   const float *__restrict__ d_row_scale,
+                                                   const int32_t *__restrict__ slot_to_row,
+                                                   int64_t ntok, int E, int k,
+                                                   float *__restrict__ d_topk_w,
+                                                   float *__restrict__ d_logits) {
+  const int lane = threadIdx.x & 63;
+  const int s = lane % G;
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G;
+  const bool live = t < ntok;
+  int idx = -1;
+  float w = 0.0f, g = 0.0f;
+  if (live && s < k) {
+    const int64_t slot = t * k + s;
+    idx = topk_idx[slot];
+    w = topk_w[slot];
+    const int row = slot_to_row[slot];
+    g = row >= 0 ? d_row_scale[row] : 0.0f;   // a dropped slot has no row
+    if (d_topk_w) d_topk_w[slot] = g;
+  }
+  float S = w * g;
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) S += __shfl_xor(S, m, 64);
+  const float dl = w * (g - S);
+  const int base = lane - s;   // first lane of the group
+  const int vpl = (E + G - 1) / G;
+  for (int v = 0; v < vpl; ++v) {
+    const int e = s + v * G;
+    float out = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int ij = __shfl(idx, base + j, 64);
+      const float dj = __shfl(dl, base + j, 64);
+      if (ij == e) out = dj;
+    }
+    if (live && e < E) d_logits[t * E + e] = out;
+  }
+}
+
+// ------------------------------------------------------------------ router bwd
+//
+// dx_router[t,:] = sum_e d_logits[t,e] * w_r[e,:] (e ascending, fp32 fma;
+// terms with d_logits == 0 are skipped, they add exact zeros).  One block per
+// token, each thread owns column pairs.
+template <typename T>
+__global__ __launch_bounds__(256) void k_router_dx(const float *__restrict__ d_logits,
+                                                   const T *__restrict__ wr, int64_t ntok, int d,
+                                                   int E, float *__restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  const float *dl = d_logits + t * E;
+  constexpr int kMaxPairs = 8;   // d <= 256*2*8 = 4096 per pass
+  for (int cbase = 0; cbase < d; cbase += 256 * 2 * kMaxPairs) {
+    float acc[kMaxPairs][2];
+#pragma unroll
+    for (int i = 0; i < kMaxPairs; ++i) acc[i][0] = acc[i][1] = 0.0f;
+    for (int e = 0; e < E; ++e) {
+      const float a = dl[e];
+      if (a == 0.0f) continue;
+      const T *row = wr + (int64_t)e * d;
+#pragma unroll
+      for (int i = 0; i < kMaxPairs; ++i) {
+        const int c = cbase + (i * 256 + threadIdx.x) * 2;
+        if (c < d) {
+          acc[i][0] = fmaf(a, Store<T>::load(row + c), acc[i][0]);
+          acc[i][1] = fmaf(a, Store<T>::load(row + c + 1), acc[i][1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPairs; ++i) {
+      const int c = cbase + (i * 256 + threadIdx.x) * 2;
+      if (c < d) *reinterpret_cast<float2 *>(dx + t * d + c) = make_float2(acc[i][0], acc[i][1]);
+    }
+  }
+}
+
+// dw_r partials: block (e, column tile of 512, token chunk of 1024).  The
+// nonzero entries of d_logits[:,e] inside the chunk are found with a ballot
+// and visited in token order.
+constexpr int kDwTokChunk = 1024;
+constexpr int kDwCols = 512;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_router_dw_partial(const float *__restrict__ d_logits,
+                                                           const T *__restrict__ x, int64_t ntok,
+                                                           int d, int E,
+                                                           float *__restrict__ partial) {
+  const int e = blockIdx.z;
+  const int chunk = blockIdx.y;
+  const int c = blockIdx.x * kDwCols + threadIdx.x * 2;
+  const int64_t tbeg = (int64_t)chunk * kDwTokChunk;
+  __shared__ int s_tok[kDwTokChunk];
+  __shared__ float s_val[kDwTokChunk];
+  __shared__ int s_cnt[4];
+  // compact the nonzero entries of this chunk, keeping token order
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int nz[4];
+  float vals[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // wave w scans tokens [w*256, w*256+256)
+    const int64_t t = tbeg + wave * 256 + i * 64 + lane;
+    const float v = (t < ntok) ? d_logits[t * E + e] : 0.0f;
+    vals[i] = v;
+    nz[i] = v != 0.0f;
+  }
+  int wave_tot = 0;
+  int pos[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t m = __ballot(nz[i]);
+    pos[i] = wave_tot + __popcll(m & ((1ull << lane) - 1ull));
+    wave_tot += __popcll(m);
+  }
+  if (lane == 0) s_cnt[wave] = wave_tot;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += s_cnt[w];
+  const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (nz[i]) {
+      s_tok[wbase + pos[i]] = (int)(wave * 256 + i * 64 + lane);
+      s_val[wbase + pos[i]] = vals[i];
+    }
+  }
+  __syncthreads();
+  float a0 = 0.0f, a1 = 0.0f;
+  if (c < d) {
+    for (int n = 0; n < total; ++n) {
+      const int64_t t = tbeg + s_tok[n];
+      const float a = s_val[n];
+      a0 = fmaf(a, Store<T>::load(x + t * d + c), a0);
+      a1 = fmaf(a, Store<T>::load(x + t * d + c + 1), a1);
+    }
+    float *out = partial + ((int64_t)e * gridDim.y + chunk) * d + c;
+    *reinterpret_cast<float2 *>(out) = make_float2(a0, a1);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_dw_reduce(const float *__restrict__ partial,
+                                                          int nchunk, int d, int E,
+                                                          float *__restrict__ dw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)E * d) return;
+  const int64_t e = i / d, c = i % d;
+  float s = 0.0f;
+  for (int ch = 0; ch < nchunk; ++ch) s += partial[(e * nchunk + ch) * d + c];
+  dw[i] = s;
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+// ====================================================================== C ABI
+
+static int check_common(int64_t T, int E, const char *fn) {
+  MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "%s: T < 0", fn);
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1,%d]", fn, E,
+              kMaxExperts);
+  return MOE_OK;
+}
+
+extern "C" int moe_router_logits(const void *x, const void *w_r, const float *bias,
+                                 const float *logit_add, int dtype, int64_t T, int d, int E,
+                                 float *logits, void *stream) {
+  clear_error();
+  int rc = check_common(T, E, "moe_router_logits");
+  if (rc) return rc;
+  MOE_REQUIRE(dtype == MOE_BF16 || dtype == MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_router_logits: dtype %d", dtype);
+  MOE_REQUIRE(d > 0 && d % 8 == 0, MOE_ERR_UNSUPPORTED, "moe_router_logits: d=%d", d);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(x && w_r && logits, MOE_ERR_INVALID_ARG, "moe_router_logits: null pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(w_r) && aligned16(logits), MOE_ERR_INVALID_ARG,
+              "moe_router_logits: pointers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int ept = E <= 16 ? 4 : (E <= 32 ? 8 : 16);
+  const int eb = 4 * ept;
+  dim3 grid((unsigned)((T + kLogitTok - 1) / kLogitTok), (unsigned)((E + eb - 1) / eb));
+#define LOGITS_CASE(TY, EPTV)                                                                   \
+  MOE_LAUNCH("router_logits", s,                                                                \
+             k_router_logits<TY, EPTV><<<grid, 256, 0, s>>>((const TY *)x, (const TY *)w_r, bias, \
+                                                             logit_add, T, d, E, logits))
+  if (dtype == MOE_BF16) {
+    if (ept == 4) LOGITS_CASE(bf16_t, 4);
+    else if (ept == 8) LOGITS_CASE(bf16_t, 8);
+    else LOGITS_CASE(bf16_t, 16);
+  } else {
+    if (ept == 4) LOGITS_CASE(float, 4);
+    else if (ept == 8) LOGITS_CASE(float, 8);
+    else LOGITS_CASE(float, 16);
+  }
+#undef LOGITS_CASE
+  return check_launch("moe_router_logits");
+}
+
+extern "C" int moe_route(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
+                         float *topk_w, void *stream) {
+  clear_error();
+  int rc = check_common(T, E, "moe_route");
+  if (rc) return rc;
+  MOE_REQUIRE(k >= 1 && k <= E && k <= kMaxTopK, MOE_ERR_UNSUPPORTED, "moe_route: k=%d E=%d", k,
+              E);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  int G = 1;
+  while (G < E && G < 64) G <<= 1;
+  const int64_t threads = T * G;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+#define ROUTE_CASE(GV)                                                                   \
+  case GV:                                                                               \
+    MOE_LAUNCH("route_topk", s,                                                          \
+               k_route<GV><<<blocks, 256, 0, s>>>(logits, T, E, k, topk_idx, topk_w)); \
+    break
+  switch (G) {
+    ROUTE_CASE(1); ROUTE_CASE(2); ROUTE_CASE(4); ROUTE_CASE(8);
+    ROUTE_CASE(16); ROUTE_CASE(32); ROUTE_CASE(64);
+  }
+#undef ROUTE_CASE
+  return check_launch("moe_route");
+}
+
+extern "C" int moe_route_bwd(const int32_t *topk_idx, const float *topk_w,
+                             const float *d_row_scale, const int32_t *slot_to_row, int64_t T,
+                             int E, int k, float *d_topk_w, float *d_logits, void *stream) {
+  clear_error();
+  int rc = check_common(T, E, "moe_route_bwd");
+  if (rc) return rc;
+  MOE_REQUIRE(k >= 1 && k <= E && k <= kMaxTopK, MOE_ERR_UNSUPPORTED, "moe_route_bwd: k=%d E=%d",
+              k, E);
+  MOE_REQUIRE((int64_t)T * k < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "moe_route_bwd: T*k too big");
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(topk_idx && topk_w && d_row_scale && slot_to_row && d_logits, MOE_ERR_INVALID_ARG,
+              "moe_route_bwd: null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  int G = 1;
+  while (G < E && G < 64) G <<= 1;
+  const unsigned blocks = (unsigned)((T * G + 255) / 256);
+#define RB_CASE(GV)                                                                             \
+  case GV:                                                                                      \
+    MOE_LAUNCH("route_bwd", s,                                                                  \
+               k_route_bwd<GV><<<blocks, 256, 0, s>>>(topk_idx, topk_w, d_row_scale, slot_to_row, \
+                                                      T, E, k, d_topk_w, d_logits));            \
+    break
+  switch (G) {
+    RB_CASE(1); RB_CASE(2); RB_CASE(4); RB_CASE(8); RB_CASE(16); RB_CASE(32); RB_CASE(64);
+  }
+#undef RB_CASE
+  return check_launch("moe_route_bwd");
+}
+
+extern "C" size_t moe_router_logits_bwd_workspace_size(int64_t T, int d, int E) {
+  if (T <= 0 || d <= 0 || E <= 0) return 256;
+  const int64_t nchunk = (T + kDwTokChunk - 1) / kDwTokChunk;
+  return align_up((size_t)E * (size_t)nchunk * (size_t)d * sizeof(float), 256);
+}
+
+extern "C" int moe_router_logits_bwd(const void *x, const void *w_r, const float *d_logits,
+                                     int dtype, int64_t T, int d, int E, float *dx_router,
+                                     float *dw_r, void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_common(T, E, "moe_router_logits_bwd");
+  if (rc) return rc;
+  MOE_REQUIRE(dtype == MOE_BF16 || dtype == MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_router_logits_bwd: dtype %d", dtype);
+  MOE_REQUIRE(d > 0 && d % 8 == 0 && d <= 65536, MOE_ERR_UNSUPPORTED, "moe_router_logits_bwd: d=%d", d);
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    if (dw_r) {
+      MOE_REQUIRE(aligned16(dw_r), MOE_ERR_INVALID_ARG, "moe_router_logits_bwd: dw_r alignment");
+      const int64_t n = (int64_t)E * d;
+      MOE_LAUNCH("router_dw_zero", s,
+                 k_fill_zero<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(dw_r, n));
+      return check_launch("moe_router_logits_bwd(zero)");
+    }
+    return MOE_OK;
+  }
+  MOE_REQUIRE(d_logits, MOE_ERR_INVALID_ARG, "moe_router_logits_bwd: null d_logits");
+  if (dx_router) {
+    MOE_REQUIRE(w_r && aligned16(w_r) && aligned16(dx_router), MOE_ERR_INVALID_ARG,
+                "moe_router_logits_bwd: w_r / dx_router");
+    const unsigned blocks = (unsigned)T;
+    if (dtype == MOE_BF16)
+      MOE_LAUNCH("router_dx", s,
+                 k_router_dx<bf16_t><<<blocks, 256, 0, s>>>(d_logits, (const bf16_t *)w_r, T, d, E,
+                                                            dx_router));
+    else
+      MOE_LAUNCH("router_dx", s,
+                 k_router_dx<float><<<blocks, 256, 0, s>>>(d_logits, (const float *)w_r, T, d, E,
+                                                           dx_router));
+    rc = check_launch("moe_router_logits_bwd(dx)");
+    if (rc) return rc;
+  }
+  if (dw_r) {
+    MOE_REQUIRE(x && aligned16(x) && aligned16(dw_r), MOE_ERR_INVALID_ARG,
+                "moe_router_logits_bwd: x / dw_r");
+    const size_t need = moe_router_logits_bwd_workspace_size(T, d, E);
+    MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
+                "moe_router_logits_bwd: workspace %zu < %zu", ws_bytes, need);
+    const int nchunk = (int)((T + kDwTokChunk - 1) / kDwTokChunk);
+    dim3 grid((unsigned)((d + kDwCols - 1) / kDwCols), (unsigned)nchunk, (unsigned)E);
+    float *partial = (float *)ws;
+    if (dtype == MOE_BF16)
+      MOE_LAUNCH("router_dw_partial", s,
+                 k_router_dw_partial<bf16_t><<<grid, 256, 0, s>>>(d_logits, (const bf16_t *)x, T,
+                                                                  d, E, partial));
+    else
+      MOE_LAUNCH("router_dw_partial", s,
+                 k_router_dw_partial<float><<<grid, 256, 0, s>>>(d_logits, (const float *)x, T, d,
+                                                                 E, partial));
+    rc = check_launch("moe_router_logits_bwd(dw partial)");
+    if (rc) return rc;
+    const unsigned rblocks = (unsigned)(((int64_t)E * d + 255) / 256);
+    MOE_LAUNCH("router_dw_reduce", s,
+               k_router_dw_reduce<<<rblocks, 256, 0, s>>>(partial, nchunk, d, E, dw_r));
+    rc = check_launch("moe_router_logits_bwd(dw reduce)");
+    if (rc) return rc;
+  }
+  return MOE_OK;
+}

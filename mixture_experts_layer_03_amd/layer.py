@@ -1,0 +1,138 @@
+"""The MoE expert block as a sequence of C-ABI calls.
+
+``MoEBlock`` owns the device buffers of one problem size (torch allocations)
+and issues the library calls of the forward and backward passes in order, all
+on one stream, with no host synchronisation in between:
+
+  forward : moe_router_logits -> moe_route -> moe_permute ->
+            moe_grouped_ffn_fwd -> moe_combine
+  backward: moe_combine_bwd -> moe_grouped_ffn_bwd -> moe_route_bwd ->
+            moe_router_logits_bwd -> moe_permute_bwd
+
+This mirrors the EP forward path the pages describe (router logits in fp32,
+per-token top-k, tokens sorted by expert, grouped matmul, rows returned and
+weighted by the top-k probabilities: "Halo's 2.8x over TRL is not a kernel,
+and its own benchmark proves it", section "Where the gap actually is"), with
+the dispatch and combine all-to-alls reduced to on-GPU row permutations.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import abi
+
+
+class MoEBlock:
+    def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype=torch.bfloat16,
+                 device="cuda", backward: bool = True):
+        self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
+        self.R = T * k
+        self.dtype = dtype
+        self.device = device
+        dc = abi.MOE_BF16 if dtype == torch.bfloat16 else abi.MOE_F32
+        self.dcode = dc
+        R = self.R
+        z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=device)
+        i32 = torch.int32
+        f32 = torch.float32
+        self.logits = z(T, E, dt=f32)
+        self.topk_idx = z(T, k, dt=i32)
+        self.topk_w = z(T, k, dt=f32)
+        self.counts = z(E, dt=i32)
+        self.offsets = z(E + 1, dt=i32)
+        self.slot_to_row = z(R, dt=i32)
+        self.row_to_slot = z(R, dt=i32)
+        self.x_perm = z(R, d)
+        self.w_perm = z(R, dt=f32)
+        self.gu = z(R, 2 * f)
+        self.h = z(R, f)
+        self.y_perm = z(R, d)
+        self.y = z(T, d)
+        ws_perm = abi.moe_permute_workspace_size(T, E, k)
+        ws_ffn = abi.moe_grouped_ffn_workspace_size(R, E, d, f, dc)
+        ws_rtr = abi.moe_router_logits_bwd_workspace_size(T, d, E) if backward else 0
+        self.ws = torch.empty(max(ws_perm, ws_ffn, ws_rtr, 256), dtype=torch.uint8, device=device)
+        self.has_bwd = backward
+        if backward:
+            self.dy_perm = z(R, d)
+            self.dgu = z(R, 2 * f)
+            self.dx_perm = z(R, d)
+            self.d_row_scale = z(R, dt=f32)
+            self.d_topk_w = z(T, k, dt=f32)
+            self.d_logits = z(T, E, dt=f32)
+            self.dx_router = z(T, d, dt=f32)
+            self.dw_r = z(E, d, dt=f32)
+            self.dw_gu = z(E, 2 * f, d, dt=f32)
+            self.dw_down = z(E, d, f, dt=f32)
+            self.dx = z(T, d)
+
+    # ------------------------------------------------------------ forward
+    def forward(self, x, w_r, w_gu, w_down, bias=None, noise=None, stream=None):
+        abi.moe_router_logits(x, w_r, bias, noise, self.logits, stream)
+        abi.moe_route(self.logits, self.k, self.topk_idx, self.topk_w, stream)
+        self.permute(x, stream)
+        self.experts_forward(w_gu, w_down, stream)
+        abi.moe_combine(self.y_perm, self.slot_to_row, self.T, self.k, self.y, stream)
+        return self.y
+
+    def permute(self, x, stream=None):
+        abi.moe_permute(x, self.topk_idx, self.topk_w, self.T, self.d, self.E, self.k,
+                        self.counts, self.offsets, self.slot_to_row, self.row_to_slot,
+                        self.x_perm, self.w_perm, self.ws, dtype=self.dcode, stream=stream)
+
+    def experts_forward(self, w_gu, w_down, stream=None):
+        abi.moe_grouped_ffn_fwd(self.x_perm, self.offsets, self.E, w_gu, w_down, self.w_perm,
+                                self.gu, self.h, self.y_perm, self.ws, stream)
+
+    # ------------------------------------------------------------ backward
+    def backward(self, x, w_r, w_gu, w_down, dy, stream=None):
+        assert self.has_bwd
+        abi.moe_combine_bwd(dy, self.slot_to_row, self.k, self.dy_perm, stream)
+        self.experts_backward(w_gu, w_down, stream)
+        abi.moe_route_bwd(self.topk_idx, self.topk_w, self.d_row_scale, self.slot_to_row,
+                          self.E, self.d_topk_w, self.d_logits, stream)
+        abi.moe_router_logits_bwd(x, w_r, self.d_logits, self.dx_router, self.dw_r, self.ws,
+                                  stream)
+        abi.moe_permute_bwd(self.dx_perm, self.slot_to_row, self.dx_router, self.T, self.k,
+                            self.dx, stream)
+        return self.dx
+
+    def experts_backward(self, w_gu, w_down, stream=None):
+        abi.moe_grouped_ffn_bwd(self.x_perm, self.gu, self.h, self.offsets, self.E, w_gu,
+                                w_down, self.w_perm, self.dy_perm, self.dgu, self.dx_perm,
+                                self.dw_gu, self.dw_down, self.d_row_scale, self.ws, stream)
+
+
+class ExpertShare:
+    """Grouped FFN alone over rows that arrive already sorted by expert (one
+    expert-parallel rank's local share: its experts and the rows dispatched to
+    it)."""
+
+    def __init__(self, R: int, d: int, E: int, f: int, dtype=torch.bfloat16, device="cuda"):
+        self.R, self.d, self.E, self.f = R, d, E, f
+        z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=device)
+        f32 = torch.float32
+        self.gu = z(R, 2 * f)
+        self.h = z(R, f)
+        self.y_perm = z(R, d)
+        self.dgu = z(R, 2 * f)
+        self.dx_perm = z(R, d)
+        self.d_row_scale = z(R, dt=f32)
+        self.dw_gu = z(E, 2 * f, d, dt=f32)
+        self.dw_down = z(E, d, f, dt=f32)
+        dc = abi.MOE_BF16 if dtype == torch.bfloat16 else abi.MOE_F32
+        self.ws = torch.empty(max(256, abi.moe_grouped_ffn_workspace_size(R, E, d, f, dc)),
+                              dtype=torch.uint8, device=device)
+
+    def forward(self, x_perm, offsets, w_gu, w_down, w_perm, stream=None):
+        abi.moe_grouped_ffn_fwd(x_perm, offsets, self.E, w_gu, w_down, w_perm, self.gu, self.h,
+                                self.y_perm, self.ws, stream)
+        return self.y_perm
+
+    def backward(self, x_perm, offsets, w_gu, w_down, w_perm, dy_perm, stream=None):
+        abi.moe_grouped_ffn_bwd(x_perm, self.gu, self.h, offsets, self.E, w_gu, w_down, w_perm,
+                                dy_perm, self.dgu, self.dx_perm, self.dw_gu, self.dw_down,
+                                self.d_row_scale, self.ws, stream)
+        return self.dx_perm
