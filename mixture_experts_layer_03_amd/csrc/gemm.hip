@@ -38,7 +38,7 @@ constexpr int kBK = 64;   // k per LDS stage: 64 bf16 = 128 bytes = 8 chunks per
 
 struct GemmArgs {
   // operands
-  const bf16_t *x_perm, *w_gu, *w_down, *h, *gu, *dy_perm, *dgu;
+  const bf16_t *x_perm, *w_gu, *w_down, *h, *gu, *dy_perm, *dgu, *s_perm;
   const float *row_scale;      // [R] or null
   const int32_t *offsets;      // [E+1]
   const int32_t *tile_start;   // [E+1] (token-tiled kinds)
@@ -53,121 +53,138 @@ struct GemmArgs {
 
 // ------------------------------------------------------------------ helpers
 
+#define LDS_AS __attribute__((address_space(3)))
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__device__ __forceinline__ u32x4_t ld16(const bf16_t *p) {
-  return *reinterpret_cast<const u32x4_t *>(p);
+// Raw buffer resource (gfx9 V#) over [base, base + bytes): loads at offsets
+// >= bytes return zeros, so tile edges and K tails need no branches.
+__device__ __forceinline__ u32x4_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32) & 0xffffu;   // stride 0
+  r[2] = bytes;                           // num_records
+  r[3] = 0x00020000u;                     // raw dword access
+  return r;
+}
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past any resource: reads zero
+
+// One 16-byte chunk per lane from global memory straight into LDS; the wave's
+// 64 chunks land contiguously at dst (lane l at dst + 16*l).  Written as
+// inline assembly so that the compiler does not guard later LDS reads of
+// other buffers with waits for these loads; the kernel waits for them itself
+// (wait_vm_lgkm0) before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(u32x4_t rs, u32x4_t *dst, uint32_t voff) {
+  const uint32_t lds = (uint32_t)(uintptr_t)((LDS_AS void *)dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs)
+               : "memory", "m0");
 }
 
-// chunk slot of (row, chunk) in a [rows][8 chunks] LDS tile, xor-swizzled so
-// that 8 consecutive rows reading the same chunk hit 8 different bank groups
-__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
-
-// 8x8 transpose of bf16: in[i] = 8 values of k-row i (cols 0..7);
-// out[c] = 8 values of column c (k rows 0..7).
-__device__ __forceinline__ void transpose8x8(const u32x4_t in[8], u32x4_t out[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t a = in[2 * m][w], b = in[2 * m + 1][w];
-      out[c][m] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
+// s_waitcnt with vmcnt <= n (n < 64) and lgkmcnt = 0 (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
-// scale the 8 bf16 of v by s and round back to bf16
-__device__ __forceinline__ u32x4_t scale_bf16x8(u32x4_t v, float s) {
-  u32x4_t o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = bf16_bits_to_f32(v[i] & 0xffffu) * s;
-    const float hi = bf16_bits_to_f32(v[i] >> 16) * s;
-    o[i] = pack_bf16x2(lo, hi);
-  }
-  return o;
-}
-
-// ------------------------------------------------------------------ loaders
+// ---------------------------------------------------------------- LDS layouts
 //
-// KContig operand tile: ROWS rows x 64 k, element (i,k) at base[i*ld + k]
-// (paired: rows >= ROWS/2 come from base2).  Unit u = (row u/8, chunk u%8).
-template <int ROWS, int NTHR>
-struct KContigLoader {
-  static constexpr int UNITS = ROWS * 8;
-  static constexpr int NU = (UNITS + NTHR - 1) / NTHR;
-  u32x4_t v[NU];
+// K-contiguous operand tile: ROWS rows x 64 k (128 bytes per row, 8 chunks of
+// 16 bytes).  Chunk ch of row r sits at slot r*8 + (ch ^ ((r >> 1) & 7)):
+// any 16 consecutive rows reading one chunk touch 16 distinct 16-byte bank
+// groups (two rows share a 256-byte bank line only when their parity differs).
+__device__ __forceinline__ int kc_slot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
 
-  __device__ __forceinline__ void load(const bf16_t *base, const bf16_t *base2, int64_t ld,
-                                       int rows_valid, int k0, int kvalid, int tid) {
-#pragma unroll
-    for (int n = 0; n < NU; ++n) {
-      const int u = tid + n * NTHR;
-      v[n] = u32x4_t{0, 0, 0, 0};
-      if (UNITS % NTHR == 0 || u < UNITS) {
-        int row = u >> 3;
-        const int k = k0 + (u & 7) * 8;
-        const bf16_t *b = base;
-        if (base2 && row >= ROWS / 2) {
-          b = base2;
-          row -= ROWS / 2;
-        }
-        if (row < rows_valid && k < kvalid) v[n] = ld16(b + (int64_t)row * ld + k);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(u32x4_t *lds, int tid) const {
-#pragma unroll
-    for (int n = 0; n < NU; ++n) {
-      const int u = tid + n * NTHR;
-      if (UNITS % NTHR == 0 || u < UNITS) lds[swz(u >> 3, u & 7)] = v[n];
-    }
-  }
-};
+// Transposed operand tile: 64 k-rows x COLS columns (COLS*2 bytes per k-row).
+// The 32-byte column block cb of k-row r sits at cb ^ tr_swz(r): the 16 k-rows
+// that one transpose read of a wave touches (8g + 0..3 for g = 0..3, or +4)
+// land on 8 distinct 32-byte bank groups per half-wave.
+__device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
-// Transposed operand tile: ROWS output rows x 64 k, element (i,k) at
-// base[k*ld + i].  Unit u = (k block u%8, row block u/8); optional per-k
-// scale (the row weight of the down-projection weight gradient).
-template <int ROWS, int NTHR>
-struct TransLoader {
-  static constexpr int UNITS = ROWS;   // (ROWS/8) row blocks x 8 k blocks
-  static constexpr int NU = (UNITS + NTHR - 1) / NTHR;
-  u32x4_t v[NU][8];
+// Issue the direct-to-LDS loads of one 64-wide K stage of a ROWS-row operand
+// tile; every thread issues ROWS/32 instructions.  All arguments but lane are
+// wave-uniform.
+//   K-contiguous: element (row i, k) at base[i*ld + k] (rows >= ROWS/2 of a
+//     paired tile from base2); rows_valid rows and kvalid k exist.
+//   transposed:   element (row i, k) at base[k*ld + i]; rows_valid columns
+//     and kvalid k-rows exist.
+template <int ROWS, bool TRANS, bool PAIRED>
+__device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *base2, int ld,
+                                            int rows_valid, int kvalid, int k0, u32x4_t *tile,
+                                            int wave, int lane) {
+  constexpr int NI = ROWS / 32;
+  if (!TRANS) {
+    constexpr int half_rows = PAIRED ? ROWS / 2 : ROWS;
+    const int rv = min(rows_valid, half_rows);
+    const uint32_t bytes = rv > 0 ? (uint32_t)rv * (uint32_t)ld * 2u : 0u;
+    // a wave's NI instructions cover 8*NI consecutive rows, all in one half
+    static_assert(!PAIRED || (ROWS / 16) % NI == 0, "paired halves align with waves");
+    const bool second = PAIRED && wave * NI >= ROWS / 16;
+    const u32x4_t rs = make_rsrc(second ? base2 : base, bytes);
+    const int row_shift = second ? ROWS / 2 : 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = wave * NI + i;          // rows 8q .. 8q+7
+      const int row = 8 * q + (lane >> 3);
+      const int ch = (lane & 7) ^ ((row >> 1) & 7);
+      const int k = k0 + ch * 8;
+      const uint32_t off =
+          k < kvalid ? ((uint32_t)(row - row_shift) * (uint32_t)ld + (uint32_t)k) * 2u : kOOB;
+      dma16(rs, tile + q * 64, off);
+    }
+  } else {
+    constexpr int C16 = ROWS / 8;           // 16-byte chunks per k-row
+    // The resource ends right after the tile's last valid element (column
+    // cols-1 of k-row krows-1): columns past the valid ones read the next
+    // k-row's data (finite values feeding only masked outputs) or zeros past
+    // the end, never memory beyond the tensor.
+    const int krows = min(kBK, kvalid - k0);
+    const int cols = min(rows_valid, ROWS);
+    const uint32_t bytes = (krows > 0 && cols > 0)
+                               ? ((uint32_t)(krows - 1) * (uint32_t)ld + (uint32_t)cols) * 2u
+                               : 0u;
+    const u32x4_t r1 = make_rsrc(base + (int64_t)k0 * ld, bytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = wave * NI + i;
+      const int lin = q * 64 + lane;        // 16-byte slot inside the tile
+      const int kr = lin / C16;
+      const int pc = lin % C16;
+      const int c16 = pc ^ (tr_swz(kr) << 1);
+      const uint32_t off = ((uint32_t)kr * (uint32_t)ld + (uint32_t)c16 * 8u) * 2u;
+      dma16(r1, tile + q * 64, off);
+    }
+  }
+}
 
-  __device__ __forceinline__ void load(const bf16_t *base, int64_t ld, int rows_valid, int k0,
-                                       int kvalid, const float *kscale, int tid) {
-#pragma unroll
-    for (int n = 0; n < NU; ++n) {
-      const int u = tid + n * NTHR;
-      const bool live = (UNITS % NTHR == 0) || u < UNITS;
-      const int kb = u & 7, rb = u >> 3;
-      const bool colok = live && rb * 8 < rows_valid;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + kb * 8 + i;
-        v[n][i] = u32x4_t{0, 0, 0, 0};
-        if (colok && k < kvalid) {
-          v[n][i] = ld16(base + (int64_t)k * ld + rb * 8);
-          if (kscale) v[n][i] = scale_bf16x8(v[n][i], kscale[k]);
-        }
-      }
-    }
+// MFMA operand fragment: rows r0..r0+15 of the tile, k step ks (32 wide);
+// lane l gets row r0 + l%16 with the 8 k-values of chunk 4*ks + l/16.
+template <int ROWS, bool TRANS>
+__device__ __forceinline__ bf16x8_t read_frag(const u32x4_t *tile, int r0, int ks, int lane) {
+  if (!TRANS) {
+    return as_bf16x8(tile[kc_slot(r0 + (lane & 15), ks * 4 + (lane >> 4))]);
+  } else {
+    // two transpose reads: k-rows kb + j/4 (+4), columns r0 + 4*(j%4) .. +3
+    const int j = lane & 15, g = lane >> 4;
+    const int c = r0 + 4 * (j & 3);
+    const int cb = c >> 4;                  // 32-byte column block
+    const int within = (c & 15) * 2;        // byte offset inside the block
+    const char *base = reinterpret_cast<const char *>(tile);
+    const int kr0 = ks * 32 + 8 * g + (j >> 2);
+    const int kr1 = kr0 + 4;
+    const char *a0 = base + kr0 * (ROWS * 2) + ((cb ^ tr_swz(kr0)) << 5) + within;
+    const char *a1 = base + kr1 * (ROWS * 2) + ((cb ^ tr_swz(kr1)) << 5) + within;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t *)(a0));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t *)(a1));
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
   }
-  __device__ __forceinline__ void store(u32x4_t *lds, int tid) const {
-#pragma unroll
-    for (int n = 0; n < NU; ++n) {
-      const int u = tid + n * NTHR;
-      if ((UNITS % NTHR == 0) || u < UNITS) {
-        const int kb = u & 7, rb = u >> 3;
-        u32x4_t t[8];
-        transpose8x8(v[n], t);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) lds[swz(rb * 8 + c, kb)] = t[c];
-      }
-    }
-  }
-};
+}
 
 template <int KIND> struct KindTraits;
 template <> struct KindTraits<FWD_GU>     { static constexpr bool PT_ = false, QT_ = false, PAIRED = true,  WG = false; };
@@ -177,51 +194,32 @@ template <> struct KindTraits<BWD_DX>     { static constexpr bool PT_ = true,  Q
 template <> struct KindTraits<BWD_DWDOWN> { static constexpr bool PT_ = true,  QT_ = true,  PAIRED = false, WG = true; };
 template <> struct KindTraits<BWD_DWGU>   { static constexpr bool PT_ = true,  QT_ = true,  PAIRED = false, WG = true; };
 
-template <bool TRANS, int ROWS, int NTHR> struct LoaderSel;
-template <int ROWS, int NTHR> struct LoaderSel<false, ROWS, NTHR> { typedef KContigLoader<ROWS, NTHR> type; };
-template <int ROWS, int NTHR> struct LoaderSel<true, ROWS, NTHR>  { typedef TransLoader<ROWS, NTHR> type; };
-
-// Operand description for one tile.
-struct Opnd {
-  const bf16_t *base;
-  const bf16_t *base2;   // paired second half (KContig only)
-  int64_t ld;
-  int rows_valid;
-  int kvalid;
-  const float *kscale;   // transposed only
-};
-
-template <typename L>
-__device__ __forceinline__ void load_op(L &l, const Opnd &o, int k0, int tid);
-template <int R, int N>
-__device__ __forceinline__ void load_op(KContigLoader<R, N> &l, const Opnd &o, int k0, int tid) {
-  l.load(o.base, o.base2, o.ld, o.rows_valid, k0, o.kvalid, tid);
-}
-template <int R, int N>
-__device__ __forceinline__ void load_op(TransLoader<R, N> &l, const Opnd &o, int k0, int tid) {
-  l.load(o.base + (int64_t)k0 * o.ld, o.ld, o.rows_valid, 0, o.kvalid - k0, o.kscale ? o.kscale + k0 : nullptr, tid);
-}
-
 // ------------------------------------------------------------------ kernel
+//
+// 256 threads = 4 waves (WP x WQ); tile BP x BQ; K in stages of 64 through a
+// ring of 3 LDS buffers filled by direct-to-LDS loads two stages ahead.  One
+// barrier per stage: after it every wave's loads of the current stage have
+// landed and every wave has finished the stage before, whose buffer then
+// receives the loads of stage + 2.
+constexpr int kStages = 3;
 
 template <int KIND, int BP, int BQ, int WP, int WQ>
 __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   using KT = KindTraits<KIND>;
-  constexpr int NTHR = WP * WQ * 64;
+  static_assert(WP * WQ == 4, "four waves");
   constexpr int FP = BP / WP / 16;
   constexpr int FQ = BQ / WQ / 16;
   static_assert(FP >= 1 && FQ >= 1, "tile too small");
   static_assert(!KT::PAIRED || (FP % 2 == 0), "paired tiles need an even fragment count");
-  using PL = typename LoaderSel<KT::PT_, BP, NTHR>::type;
-  using QL = typename LoaderSel<KT::QT_, BQ, NTHR>::type;
+  static_assert(BP % 128 == 0 && BQ % 128 == 0, "tiles are multiples of 128 rows");
+  constexpr int LOADS = BP / 32 + BQ / 32;   // direct loads per thread per stage
 
-  __shared__ u32x4_t lds[2][(BP + BQ) * 8];
+  __shared__ u32x4_t sP0[BP * 8], sQ0[BQ * 8], sP1[BP * 8], sQ1[BQ * 8], sP2[BP * 8], sQ2[BQ * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave % WP, wq = wave / WP;
-  const int qtid = tid ^ (NTHR / 2);   // spread the Q loader over the other half first
 
   // ---- XCD-aware tile order: workgroups are dealt round-robin over the 8
   // XCDs; give each XCD a contiguous range of logical tiles.
@@ -255,44 +253,52 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     p_tile = rem / qt_e;
     q_tile = rem - p_tile * qt_e;
   }
+  // the tile decode is wave-uniform; say so, so that buffer resources and
+  // LDS addresses stay in scalar registers
+  e = __builtin_amdgcn_readfirstlane(e);
+  p_tile = __builtin_amdgcn_readfirstlane(p_tile);
+  q_tile = __builtin_amdgcn_readfirstlane(q_tile);
+  seg0 = __builtin_amdgcn_readfirstlane(seg0);
+  Me = __builtin_amdgcn_readfirstlane(Me);
   const int d = a.d, f = a.f;
   const int64_t f2 = 2 * (int64_t)f;
 
   // ---- operands of this tile
-  Opnd P{}, Q{};
+  const bf16_t *pb = nullptr, *pb2 = nullptr, *qb = nullptr;
+  int pld = 0, prv = 0, pkv = 0, qld = 0, qrv = 0, qkv = 0;
   int K = 0;
   const int p0 = p_tile * (KT::PAIRED ? BP / 2 : BP);
   const int q0 = q_tile * BQ;
   if (KIND == FWD_GU) {
     const bf16_t *W = a.w_gu + (int64_t)e * f2 * d;
-    P = Opnd{W + (int64_t)p0 * d, W + ((int64_t)f + p0) * d, d, f - p0, d, nullptr};
-    Q = Opnd{a.x_perm + ((int64_t)seg0 + q0) * d, nullptr, d, Me - q0, d, nullptr};
+    pb = W + (int64_t)p0 * d; pb2 = W + ((int64_t)f + p0) * d; pld = d; prv = f - p0; pkv = d;
+    qb = a.x_perm + ((int64_t)seg0 + q0) * d; qld = d; qrv = Me - q0; qkv = d;
     K = d;
   } else if (KIND == FWD_DOWN) {
     const bf16_t *W = a.w_down + (int64_t)e * d * f;
-    P = Opnd{W + (int64_t)p0 * f, nullptr, f, d - p0, f, nullptr};
-    Q = Opnd{a.h + ((int64_t)seg0 + q0) * f, nullptr, f, Me - q0, f, nullptr};
+    pb = W + (int64_t)p0 * f; pld = f; prv = d - p0; pkv = f;
+    qb = a.h + ((int64_t)seg0 + q0) * f; qld = f; qrv = Me - q0; qkv = f;
     K = f;
   } else if (KIND == BWD_DH) {
     const bf16_t *W = a.w_down + (int64_t)e * d * f;
-    P = Opnd{W + p0, nullptr, f, f - p0, d, nullptr};
-    Q = Opnd{a.dy_perm + ((int64_t)seg0 + q0) * d, nullptr, d, Me - q0, d, nullptr};
+    pb = W + p0; pld = f; prv = f - p0; pkv = d;
+    qb = a.dy_perm + ((int64_t)seg0 + q0) * d; qld = d; qrv = Me - q0; qkv = d;
     K = d;
   } else if (KIND == BWD_DX) {
     const bf16_t *W = a.w_gu + (int64_t)e * f2 * d;
-    P = Opnd{W + p0, nullptr, d, d - p0, (int)f2, nullptr};
-    Q = Opnd{a.dgu + ((int64_t)seg0 + q0) * f2, nullptr, f2, Me - q0, (int)f2, nullptr};
+    pb = W + p0; pld = d; prv = d - p0; pkv = (int)f2;
+    qb = a.dgu + ((int64_t)seg0 + q0) * f2; qld = (int)f2; qrv = Me - q0; qkv = (int)f2;
     K = (int)f2;
   } else if (KIND == BWD_DWDOWN) {
-    P = Opnd{a.h + (int64_t)seg0 * f + p0, nullptr, f, f - p0, Me, nullptr};
-    Q = Opnd{a.dy_perm + (int64_t)seg0 * d + q0, nullptr, d, d - q0, Me,
-             a.row_scale ? a.row_scale + seg0 : nullptr};
+    pb = a.h + (int64_t)seg0 * f + p0; pld = f; prv = f - p0; pkv = Me;
+    qb = a.s_perm + (int64_t)seg0 * d + q0; qld = d; qrv = d - q0; qkv = Me;
     K = Me;
   } else {   // BWD_DWGU
-    P = Opnd{a.x_perm + (int64_t)seg0 * d + p0, nullptr, d, d - p0, Me, nullptr};
-    Q = Opnd{a.dgu + (int64_t)seg0 * f2 + q0, nullptr, f2, (int)(f2 - q0), Me, nullptr};
+    pb = a.x_perm + (int64_t)seg0 * d + p0; pld = d; prv = d - p0; pkv = Me;
+    qb = a.dgu + (int64_t)seg0 * f2 + q0; qld = (int)f2; qrv = (int)(f2 - q0); qkv = Me;
     K = Me;
   }
+  if (!pb2) pb2 = pb;
 
   f32x4_t acc[FP][FQ];
 #pragma unroll
@@ -314,44 +320,42 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < FQ; ++j) qrow[j] = wq * (BQ / WQ) + j * 16;
 
+#define MOE_ISSUE(kt, SP, SQ)                                                                  \
+  do {                                                                                       \
+    issue_stage<BP, KT::PT_, KT::PAIRED>(pb, pb2, pld, prv, pkv, (kt) * kBK, SP, wave, lane); \
+    issue_stage<BQ, KT::QT_, false>(qb, qb, qld, qrv, qkv, (kt) * kBK, SQ, wave, lane);       \
+  } while (0)
+#define MOE_STEP(kt, SP, SQ, NP, NQ)                                                    \
+  do {                                                                                \
+    if ((kt) + 1 < nk) wait_vm_lgkm0<LOADS>(); else wait_vm_lgkm0<0>();              \
+    __builtin_amdgcn_s_barrier();                                                     \
+    if ((kt) + 2 < nk) MOE_ISSUE((kt) + 2, NP, NQ);                                   \
+    _Pragma("unroll") for (int ks = 0; ks < kBK / 32; ++ks) {                         \
+      bf16x8_t pf[FP], qf[FQ];                                                        \
+      _Pragma("unroll") for (int i = 0; i < FP; ++i)                                  \
+        pf[i] = read_frag<BP, KT::PT_>(SP, prow[i], ks, lane);                        \
+      _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                  \
+        qf[j] = read_frag<BQ, KT::QT_>(SQ, qrow[j], ks, lane);                        \
+      _Pragma("unroll") for (int i = 0; i < FP; ++i)                                  \
+        _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
+    }                                                                                 \
+  } while (0)
+
+  // stage kt lives in buffer kt % 3; before it is used, the loads of stage
+  // kt+1 (if any) may still be in flight.
   const int nk = (K + kBK - 1) / kBK;
   if (nk > 0) {
-    PL pl;
-    QL ql;
-    load_op(pl, P, 0, tid);
-    load_op(ql, Q, 0, qtid);
-    pl.store(&lds[0][0], tid);
-    ql.store(&lds[0][BP * 8], qtid);
-    __syncthreads();
-    const int fr = lane & 15, fg = lane >> 4;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        load_op(pl, P, (kt + 1) * kBK, tid);
-        load_op(ql, Q, (kt + 1) * kBK, qtid);
-      }
-      const u32x4_t *lp = &lds[cur][0];
-      const u32x4_t *lq = &lds[cur][BP * 8];
-#pragma unroll
-      for (int ks = 0; ks < kBK / 32; ++ks) {
-        bf16x8_t pf[FP], qf[FQ];
-#pragma unroll
-        for (int i = 0; i < FP; ++i) pf[i] = as_bf16x8(lp[swz(prow[i] + fr, ks * 4 + fg)]);
-#pragma unroll
-        for (int j = 0; j < FQ; ++j) qf[j] = as_bf16x8(lq[swz(qrow[j] + fr, ks * 4 + fg)]);
-#pragma unroll
-        for (int i = 0; i < FP; ++i)
-#pragma unroll
-          for (int j = 0; j < FQ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) {
-        pl.store(&lds[cur ^ 1][0], tid);
-        ql.store(&lds[cur ^ 1][BP * 8], qtid);
-      }
-      __syncthreads();
+    MOE_ISSUE(0, sP0, sQ0);
+    if (nk > 1) MOE_ISSUE(1, sP1, sQ1);
+    for (int kt = 0; kt < nk; kt += 3) {
+      MOE_STEP(kt, sP0, sQ0, sP2, sQ2);
+      if (kt + 1 < nk) MOE_STEP(kt + 1, sP1, sQ1, sP0, sQ0);
+      if (kt + 2 < nk) MOE_STEP(kt + 2, sP2, sQ2, sP1, sQ1);
     }
   }
+#undef MOE_STEP
+#undef MOE_ISSUE
 
   // ---- epilogues.  Lane holds D[prow+4*(lane/16)+v][qrow+lane%16].
   const int er = 4 * (lane >> 4);
@@ -572,8 +576,26 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
 // tile configurations
 constexpr int FWD_BP = 256, FWD_BQ = 128, FWD_WP = 2, FWD_WQ = 2;   // FWD_GU (P = gate|up pairs)
 constexpr int DN_BP = 256, DN_BQ = 128, DN_WP = 2, DN_WQ = 2;       // FWD_DOWN, BWD_DX
-constexpr int DH_BP = 128, DH_BQ = 128, DH_WP = 2, DH_WQ = 2;       // BWD_DH
-constexpr int WG_BP = 128, WG_BQ = 128, WG_WP = 2, WG_WQ = 2;       // weight gradients
+constexpr int DH_BP = 256, DH_BQ = 128, DH_WP = 2, DH_WQ = 2;       // BWD_DH
+constexpr int WG_BP = 256, WG_BQ = 128, WG_WP = 2, WG_WQ = 2;       // weight gradients
+
+// S = store(w * dY_perm): the row-scaled upstream gradient of the
+// down-projection weight gradient (bf16 rounding of the fp32 product).
+__global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy,
+                                                   const float *__restrict__ w, int64_t R, int d,
+                                                   bf16_t *__restrict__ s) {
+  const int nvec = d / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * nvec) return;
+  const int64_t r = i / nvec;
+  const float wr = w ? w[r] : 1.0f;
+  const u32x4_t v = reinterpret_cast<const u32x4_t *>(dy)[i];
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = pack_bf16x2(bf16_bits_to_f32(v[j] & 0xffffu) * wr, bf16_bits_to_f32(v[j] >> 16) * wr);
+  reinterpret_cast<u32x4_t *>(s)[i] = o;
+}
 
 static inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
@@ -619,12 +641,16 @@ static int check_ffn(const char *fn, int E, int64_t R, int d, int f, int dtype) 
 
 static size_t tile_start_bytes(int E) { return align_up(sizeof(int32_t) * (size_t)(E + 1), 256); }
 
-extern "C" size_t moe_grouped_ffn_workspace_size(int64_t R, int E, int d, int f, int dtype) {
-  (void)d;
-  (void)dtype;
-  if (R < 0 || E < 1 || f < 1) return 0;
+static size_t drs_bytes(int64_t R, int f) {
   const int nparts = (f + DH_BP - 1) / DH_BP * DH_WP;
-  return 2 * tile_start_bytes(E) + align_up(sizeof(float) * (size_t)R * nparts, 256);
+  return align_up(sizeof(float) * (size_t)R * nparts, 256);
+}
+
+extern "C" size_t moe_grouped_ffn_workspace_size(int64_t R, int E, int d, int f, int dtype) {
+  (void)dtype;
+  if (R < 0 || E < 1 || f < 1 || d < 1) return 0;
+  // tile prefixes, d_row_scale partials, S = w * dY_perm (bf16)
+  return 2 * tile_start_bytes(E) + drs_bytes(R, f) + align_up(2 * (size_t)R * d, 256);
 }
 
 extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, int E, int64_t R,
@@ -705,6 +731,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   int32_t *ts0 = (int32_t *)ws;
   int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
   float *drs_part = (float *)((char *)ws + 2 * tile_start_bytes(E));
+  bf16_t *s_perm = (bf16_t *)((char *)ws + 2 * tile_start_bytes(E) + drs_bytes(R, f));
   GemmArgs a{};
   a.x_perm = (const bf16_t *)x_perm;
   a.w_gu = (const bf16_t *)w_gu;
@@ -737,7 +764,16 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   rc = launch_token_gemm<BWD_DX, DN_BP, DN_BQ, DN_WP, DN_WQ>(a, R, (d + DN_BP - 1) / DN_BP, ts1,
                                                              "gg_bwd_dx", s);
   if (rc) return rc;
-  // 3. dW_down[e] = (w*dY_perm)^T H   -> [E, d, f]
+  // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
+  if (R > 0) {
+    const int64_t n = R * (d / 8);
+    MOE_LAUNCH("row_scale", s,
+               k_row_scale<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+                   (const bf16_t *)dy_perm, row_scale, R, d, s_perm));
+    rc = check_launch("moe_grouped_ffn_bwd(row scale)");
+    if (rc) return rc;
+  }
+  a.s_perm = s_perm;
   a.o_dw = dw_down;
   rc = launch_wgrad_gemm<BWD_DWDOWN, WG_BP, WG_BQ, WG_WP, WG_WQ>(a, f, d, "gg_bwd_dw_down", s);
   if (rc) return rc;

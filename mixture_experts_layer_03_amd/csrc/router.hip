@@ -11,12 +11,30 @@ namespace moe {
 
 // ------------------------------------------------------------------ logits
 //
-// Block: 256 threads = 4 waves; tile = 64 tokens x (4*EPT) experts.  Lane =
-// token, wave = group of EPT experts, so a wave reads the same router weights
-// (LDS broadcast) and its own token column.  Each (t,e) output is ONE fp32
-// fma chain over c = 0..d-1 in order, then + bias, then + noise.
-constexpr int kLogitTok = 64;
+// Block: 256 threads, tile = 16 tokens x EB experts (EB = 16*EPT).  Thread
+// (tok = tid%16, grp = tid/16) owns experts grp, grp+16, ...: EPT independent
+// chains.  Each (t,e) output is ONE fp32 fma chain over c = 0..d-1 in order,
+// then + bias, then + noise.  x and w_r tiles of 64 columns are staged in LDS
+// as fp32; the next tile's loads are issued before the current tile is used.
+constexpr int kLogitTok = 16;
 constexpr int kLogitCk = 64;
+constexpr int kLogitPad = kLogitCk + 4;
+
+// 8 consecutive elements as fp32
+__device__ __forceinline__ void load8(const bf16_t *p, float *f) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(v[i] & 0xffffu);
+    f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float *f) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
 
 template <typename T, int EPT>
 __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
@@ -25,55 +43,83 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
                                                        const float *__restrict__ noise,
                                                        int64_t ntok, int d, int E,
                                                        float *__restrict__ logits) {
-  constexpr int EB = 4 * EPT;
-  __shared__ float xs[kLogitCk][kLogitTok + 1];
-  __shared__ __attribute__((aligned(16))) float ws[kLogitCk][EB];
+  constexpr int EB = 16 * EPT;
+  constexpr int XU = kLogitTok * (kLogitCk / 8);          // 8-element units in the x tile
+  constexpr int WU = EB * (kLogitCk / 8);                 // ... in the w tile
+  constexpr int WPT = (WU + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float xs[kLogitTok][kLogitPad];
+  __shared__ __attribute__((aligned(16))) float ws[EB][kLogitPad];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int tok = tid & 15, grp = tid >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * kLogitTok;
   const int e0 = blockIdx.y * EB;
   float acc[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) acc[i] = 0.0f;
 
-  for (int c0 = 0; c0 < d; c0 += kLogitCk) {
-    // x tile -> xs[c][t] (transposed)
-    for (int i = tid; i < kLogitTok * kLogitCk; i += 256) {
-      const int tt = i / kLogitCk, cc = i % kLogitCk;
-      const int64_t t = t0 + tt;
-      const int c = c0 + cc;
-      float v = 0.0f;
-      if (t < ntok && c < d) v = Store<T>::load(x + t * d + c);
-      xs[cc][tt] = v;
-    }
-    for (int i = tid; i < EB * kLogitCk; i += 256) {
-      const int ee = i / kLogitCk, cc = i % kLogitCk;
-      const int e = e0 + ee, c = c0 + cc;
-      float v = 0.0f;
-      if (e < E && c < d) v = Store<T>::load(wr + (int64_t)e * d + c);
-      ws[cc][ee] = v;
-    }
-    __syncthreads();
-    const int cn = min(kLogitCk, d - c0);
-    for (int cc = 0; cc < cn; ++cc) {
-      const float xv = xs[cc][lane];
+  float xr[8], wrg[WPT][8];
+  auto fetch = [&](int c0) {
+    if (tid < XU) {
+      const int r = tid >> 3, c = c0 + (tid & 7) * 8;
+      const int64_t t = t0 + r;
 #pragma unroll
-      for (int i = 0; i < EPT; i += 4) {
-        const float4 w4 = *reinterpret_cast<const float4 *>(&ws[cc][wave * EPT + i]);
-        acc[i + 0] = fmaf(xv, w4.x, acc[i + 0]);
-        acc[i + 1] = fmaf(xv, w4.y, acc[i + 1]);
-        acc[i + 2] = fmaf(xv, w4.z, acc[i + 2]);
-        acc[i + 3] = fmaf(xv, w4.w, acc[i + 3]);
+      for (int i = 0; i < 8; ++i) xr[i] = 0.0f;
+      if (t < ntok && c < d) load8(x + t * d + c, xr);
+    }
+#pragma unroll
+    for (int n = 0; n < WPT; ++n) {
+      const int u = tid + n * 256;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wrg[n][i] = 0.0f;
+      if (u < WU) {
+        const int r = u >> 3, c = c0 + (u & 7) * 8;
+        const int e = e0 + r;
+        if (e < E && c < d) load8(wr + (int64_t)e * d + c, wrg[n]);
+      }
+    }
+  };
+  auto stage = [&]() {
+    if (tid < XU) {
+      float *dst = &xs[tid >> 3][(tid & 7) * 8];
+      *reinterpret_cast<float4 *>(dst) = make_float4(xr[0], xr[1], xr[2], xr[3]);
+      *reinterpret_cast<float4 *>(dst + 4) = make_float4(xr[4], xr[5], xr[6], xr[7]);
+    }
+#pragma unroll
+    for (int n = 0; n < WPT; ++n) {
+      const int u = tid + n * 256;
+      if (u < WU) {
+        float *dst = &ws[u >> 3][(u & 7) * 8];
+        *reinterpret_cast<float4 *>(dst) = make_float4(wrg[n][0], wrg[n][1], wrg[n][2], wrg[n][3]);
+        *reinterpret_cast<float4 *>(dst + 4) =
+            make_float4(wrg[n][4], wrg[n][5], wrg[n][6], wrg[n][7]);
+      }
+    }
+  };
+
+  fetch(0);
+  for (int c0 = 0; c0 < d; c0 += kLogitCk) {
+    stage();
+    __syncthreads();
+    if (c0 + kLogitCk < d) fetch(c0 + kLogitCk);
+    const int cn = min(kLogitCk, d - c0);   // a multiple of 8
+    for (int cc = 0; cc < cn; cc += 4) {
+      const float4 xv = *reinterpret_cast<const float4 *>(&xs[tok][cc]);
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float4 wv = *reinterpret_cast<const float4 *>(&ws[grp + 16 * i][cc]);
+        acc[i] = fmaf(xv.x, wv.x, acc[i]);
+        acc[i] = fmaf(xv.y, wv.y, acc[i]);
+        acc[i] = fmaf(xv.z, wv.z, acc[i]);
+        acc[i] = fmaf(xv.w, wv.w, acc[i]);
       }
     }
     __syncthreads();
   }
-  const int64_t t = t0 + lane;
+  const int64_t t = t0 + tok;
   if (t >= ntok) return;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int e = e0 + wave * EPT + i;
+    const int e = e0 + grp + 16 * i;
     if (e >= E) continue;
     float v = acc[i];
     if (bias) v = v + bias[e];
@@ -341,21 +387,21 @@ extern "C" int moe_router_logits(const void *x, const void *w_r, const float *bi
   MOE_REQUIRE(aligned16(x) && aligned16(w_r) && aligned16(logits), MOE_ERR_INVALID_ARG,
               "moe_router_logits: pointers must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  const int ept = E <= 16 ? 4 : (E <= 32 ? 8 : 16);
-  const int eb = 4 * ept;
+  const int ept = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
+  const int eb = 16 * ept;
   dim3 grid((unsigned)((T + kLogitTok - 1) / kLogitTok), (unsigned)((E + eb - 1) / eb));
 #define LOGITS_CASE(TY, EPTV)                                                                   \
   MOE_LAUNCH("router_logits", s,                                                                \
              k_router_logits<TY, EPTV><<<grid, 256, 0, s>>>((const TY *)x, (const TY *)w_r, bias, \
                                                              logit_add, T, d, E, logits))
   if (dtype == MOE_BF16) {
-    if (ept == 4) LOGITS_CASE(bf16_t, 4);
-    else if (ept == 8) LOGITS_CASE(bf16_t, 8);
-    else LOGITS_CASE(bf16_t, 16);
+    if (ept == 1) LOGITS_CASE(bf16_t, 1);
+    else if (ept == 2) LOGITS_CASE(bf16_t, 2);
+    else LOGITS_CASE(bf16_t, 4);
   } else {
-    if (ept == 4) LOGITS_CASE(float, 4);
-    else if (ept == 8) LOGITS_CASE(float, 8);
-    else LOGITS_CASE(float, 16);
+    if (ept == 1) LOGITS_CASE(float, 1);
+    else if (ept == 2) LOGITS_CASE(float, 2);
+    else LOGITS_CASE(float, 4);
   }
 #undef LOGITS_CASE
   return check_launch("moe_router_logits");

@@ -1,0 +1,126 @@
+"""CPU model of the grouped GEMM's global reads (no GPU).
+
+The GEMM kernel (csrc/gemm.hip) loads operand tiles straight into LDS with
+buffer loads; a lane's load is in range only below the resource's byte count,
+and the kernel sizes each resource so that in-range reads stay inside the
+operand tensor.  This test restates those bounds (tile origins, leading
+dimensions, row/column/k validity, the byte count of each resource and the
+largest offset a lane generates) and checks, for every kind, tile and K stage
+of each workload, that no in-range read ends past the tensor -- and that a
+resource sized by whole k-rows would (the model catches the over-read a full
+size problem exposes).
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_layer_03_amd import inputs as I
+
+BK = 64
+TILES = {  # kind: (BP, BQ, P transposed, Q transposed, paired)
+    "FWD_GU": (256, 128, False, False, True),
+    "FWD_DOWN": (256, 128, False, False, False),
+    "BWD_DH": (256, 128, True, False, False),
+    "BWD_DX": (256, 128, True, False, False),
+    "BWD_DWDOWN": (256, 128, True, True, False),
+    "BWD_DWGU": (256, 128, True, True, False),
+}
+
+
+def kc_end(base, ld, rows_valid, rows, kvalid):
+    """Largest readable byte (exclusive) of a K-contiguous tile, in elements*2."""
+    rv = min(rows_valid, rows)
+    if rv <= 0:
+        return base * 2
+    nbytes = rv * ld * 2
+    gen = ((rows - 1) * ld + min(kvalid, ld)) * 2          # largest generated offset + 16
+    return base * 2 + min(nbytes, gen)
+
+
+def tr_end(base, ld, cols_valid, rows, kvalid, k0, whole_rows=False):
+    krows = min(BK, kvalid - k0)
+    cols = min(cols_valid, rows)
+    if krows <= 0 or cols <= 0:
+        return base * 2
+    nbytes = krows * ld * 2 if whole_rows else ((krows - 1) * ld + cols) * 2
+    gen = ((BK - 1) * ld + rows) * 2
+    return (base + k0 * ld) * 2 + min(nbytes, gen)
+
+
+def worst_overrun(T, d, E, k, f, offsets, whole_rows=False):
+    R = int(offsets[-1])
+    f2 = 2 * f
+    worst = -np.inf
+    for kind, (BP, BQ, pt, qt, paired) in TILES.items():
+        for e in range(E):
+            seg0, Me = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+            ends = []
+            if kind == "FWD_GU":
+                for p0 in range(0, f, BP // 2):
+                    ends.append((kc_end(e * f2 * d + p0 * d, d, f - p0, BP // 2, d), E * f2 * d))
+                    ends.append((kc_end(e * f2 * d + (f + p0) * d, d, f - p0, BP // 2, d),
+                                 E * f2 * d))
+                for q0 in range(0, Me, BQ):
+                    ends.append((kc_end((seg0 + q0) * d, d, Me - q0, BQ, d), R * d))
+            elif kind == "FWD_DOWN":
+                for p0 in range(0, d, BP):
+                    ends.append((kc_end(e * d * f + p0 * f, f, d - p0, BP, f), E * d * f))
+                for q0 in range(0, Me, BQ):
+                    ends.append((kc_end((seg0 + q0) * f, f, Me - q0, BQ, f), R * f))
+            elif kind == "BWD_DH":
+                for p0 in range(0, f, BP):
+                    for k0 in range(0, d, BK):
+                        ends.append((tr_end(e * d * f + p0, f, f - p0, BP, d, k0, whole_rows),
+                                     E * d * f))
+                for q0 in range(0, Me, BQ):
+                    ends.append((kc_end((seg0 + q0) * d, d, Me - q0, BQ, d), R * d))
+            elif kind == "BWD_DX":
+                for p0 in range(0, d, BP):
+                    for k0 in range(0, f2, BK):
+                        ends.append((tr_end(e * f2 * d + p0, d, d - p0, BP, f2, k0, whole_rows),
+                                     E * f2 * d))
+                for q0 in range(0, Me, BQ):
+                    ends.append((kc_end((seg0 + q0) * f2, f2, Me - q0, BQ, f2), R * f2))
+            else:
+                Pdim, Qdim = (f, d) if kind == "BWD_DWDOWN" else (d, f2)
+                Pld, Qld = (f, d) if kind == "BWD_DWDOWN" else (d, f2)
+                for k0 in range(0, Me, BK):
+                    for p0 in range(0, Pdim, BP):
+                        ends.append((tr_end(seg0 * Pld + p0, Pld, Pdim - p0, BP, Me, k0,
+                                            whole_rows), R * Pld))
+                    for q0 in range(0, Qdim, BQ):
+                        ends.append((tr_end(seg0 * Qld + q0, Qld, Qdim - q0, BQ, Me, k0,
+                                            whole_rows), R * Qld))
+            for end, n in ends:
+                worst = max(worst, end - 2 * n)
+    return worst
+
+
+def _offsets(R, E, seed, skew=False):
+    rng = np.random.default_rng(seed)
+    p = np.full(E, 1.0 / E)
+    if skew:
+        p = np.exp(-2.2 * np.log(np.arange(E) + 1.0))
+        p /= p.sum()
+    counts = rng.multinomial(R, p)
+    return np.concatenate([[0], np.cumsum(counts)])
+
+
+CASES = [
+    ("gpt-oss-20b-like", 4096, 2880, 32, 4, 2880, False),
+    ("gpt-oss-20b-like zipf", 16384, 2880, 32, 4, 2880, True),
+    ("qwen3-30b-a3b-like", 32768, 2048, 128, 8, 768, False),
+    ("ragged small", 300, 328, 6, 2, 200, False),
+    ("narrow", 64, 64, 3, 1, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_in_range_reads_stay_inside_tensors(case):
+    name, T, d, E, k, f, skew = case
+    off = _offsets(T * k, E, 5, skew)
+    assert worst_overrun(T, d, E, k, f, off) <= 0
+
+
+def test_whole_row_resources_would_overrun():
+    off = _offsets(4096 * 4, 32, 5)
+    assert worst_overrun(4096, 2880, 32, 4, 2880, off, whole_rows=True) > 0
