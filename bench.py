@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--profile-steps", type=int, default=5,
                     help="extra steps with per-kernel event timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (reference for HBM "
+                         "byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -148,6 +151,15 @@ def main():
         for n, v in kernels.items():
             v["avg_us"] = 1e3 * v["ms_total"] / max(1, v["launches"])
         abi.moe_timing_reset()
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     R = w.R
     flops = gemm_flops(R, w.d, w.f)

@@ -106,17 +106,18 @@ __device__ __forceinline__ int kc_slot(int row, int ch) { return row * 8 + (ch ^
 __device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
 // Issue the direct-to-LDS loads of one 64-wide K stage of a ROWS-row operand
-// tile; every thread issues ROWS/32 instructions.  All arguments but lane are
+// tile; every wave issues ROWS/(8*NW) instructions.  All arguments but lane are
 // wave-uniform.
 //   K-contiguous: element (row i, k) at base[i*ld + k] (rows >= ROWS/2 of a
 //     paired tile from base2); rows_valid rows and kvalid k exist.
 //   transposed:   element (row i, k) at base[k*ld + i]; rows_valid columns
 //     and kvalid k-rows exist.
-template <int ROWS, bool TRANS, bool PAIRED>
+template <int ROWS, bool TRANS, bool PAIRED, int NW>
 __device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *base2, int ld,
                                             int rows_valid, int kvalid, int k0, u32x4_t *tile,
                                             int wave, int lane) {
-  constexpr int NI = ROWS / 32;
+  constexpr int NI = ROWS / 8 / NW;
+  static_assert(NI >= 1 && NI * 8 * NW == ROWS, "tile rows split evenly over the waves");
   if (!TRANS) {
     constexpr int half_rows = PAIRED ? ROWS / 2 : ROWS;
     const int rv = min(rows_valid, half_rows);
@@ -196,23 +197,25 @@ template <> struct KindTraits<BWD_DWGU>   { static constexpr bool PT_ = true,  Q
 
 // ------------------------------------------------------------------ kernel
 //
-// 256 threads = 4 waves (WP x WQ); tile BP x BQ; K in stages of 64 through a
+// 4 or 8 waves (WP x WQ); tile BP x BQ; K in stages of 64 through a
 // ring of 3 LDS buffers filled by direct-to-LDS loads two stages ahead.  One
 // barrier per stage: after it every wave's loads of the current stage have
 // landed and every wave has finished the stage before, whose buffer then
 // receives the loads of stage + 2.
 constexpr int kStages = 3;
+constexpr int kBandP = 4;   // P-tiles per band in the weight-gradient tile order
 
 template <int KIND, int BP, int BQ, int WP, int WQ>
 __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   using KT = KindTraits<KIND>;
-  static_assert(WP * WQ == 4, "four waves");
+  constexpr int NW = WP * WQ;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int FP = BP / WP / 16;
   constexpr int FQ = BQ / WQ / 16;
   static_assert(FP >= 1 && FQ >= 1, "tile too small");
   static_assert(!KT::PAIRED || (FP % 2 == 0), "paired tiles need an even fragment count");
   static_assert(BP % 128 == 0 && BQ % 128 == 0, "tiles are multiples of 128 rows");
-  constexpr int LOADS = BP / 32 + BQ / 32;   // direct loads per thread per stage
+  constexpr int LOADS = (BP + BQ) / 8 / NW;   // direct loads per thread per stage
 
   __shared__ u32x4_t sP0[BP * 8], sQ0[BQ * 8], sP1[BP * 8], sQ1[BQ * 8], sP2[BP * 8], sQ2[BQ * 8];
 
@@ -229,12 +232,19 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
 
   int e, p_tile, q_tile, seg0, Me;
   if (KT::WG) {
+    // Weight gradients: an expert's PT x QT tiles are walked in bands of
+    // kBandP P-tiles; inside a band the P-tile index runs fastest, so the
+    // tiles in flight on one XCD share a few P and Q operand slabs in its L2
+    // (each P slab is read once per expert, each Q slab once per band).
     if (L >= a.nlogical) return;
     const int per_e = a.PT * a.QT;
     e = L / per_e;
     const int rem = L - e * per_e;
-    p_tile = rem / a.QT;
-    q_tile = rem - p_tile * a.QT;
+    const int band = rem / (kBandP * a.QT);
+    const int in_band = rem - band * kBandP * a.QT;
+    const int bp = min(kBandP, a.PT - band * kBandP);
+    q_tile = in_band / bp;
+    p_tile = band * kBandP + (in_band - q_tile * bp);
     seg0 = a.offsets[e];
     Me = a.offsets[e + 1] - seg0;
   } else {
@@ -319,11 +329,16 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < FQ; ++j) qrow[j] = wq * (BQ / WQ) + j * 16;
+  // token-row fragments past the end of the expert's rows hold only zeros:
+  // skip their MFMAs (wave-uniform); weight-gradient tiles have no such rows
+  bool qlive[FQ];
+#pragma unroll
+  for (int j = 0; j < FQ; ++j) qlive[j] = KT::WG || (q0 + qrow[j] < Me);
 
 #define MOE_ISSUE(kt, SP, SQ)                                                                  \
   do {                                                                                       \
-    issue_stage<BP, KT::PT_, KT::PAIRED>(pb, pb2, pld, prv, pkv, (kt) * kBK, SP, wave, lane); \
-    issue_stage<BQ, KT::QT_, false>(qb, qb, qld, qrv, qkv, (kt) * kBK, SQ, wave, lane);       \
+    issue_stage<BP, KT::PT_, KT::PAIRED, NW>(pb, pb2, pld, prv, pkv, (kt) * kBK, SP, wave, lane); \
+    issue_stage<BQ, KT::QT_, false, NW>(qb, qb, qld, qrv, qkv, (kt) * kBK, SQ, wave, lane);       \
   } while (0)
 #define MOE_STEP(kt, SP, SQ, NP, NQ)                                                    \
   do {                                                                                \
@@ -336,9 +351,11 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
         pf[i] = read_frag<BP, KT::PT_>(SP, prow[i], ks, lane);                        \
       _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                  \
         qf[j] = read_frag<BQ, KT::QT_>(SQ, qrow[j], ks, lane);                        \
-      _Pragma("unroll") for (int i = 0; i < FP; ++i)                                  \
-        _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                \
+      _Pragma("unroll") for (int j = 0; j < FQ; ++j) {                                \
+        if (!qlive[j]) continue;                                                      \
+        _Pragma("unroll") for (int i = 0; i < FP; ++i)                                \
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
+      }                                                                               \
     }                                                                                 \
   } while (0)
 
@@ -574,10 +591,10 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
 // ------------------------------------------------------------------ launch
 
 // tile configurations
-constexpr int FWD_BP = 256, FWD_BQ = 128, FWD_WP = 2, FWD_WQ = 2;   // FWD_GU (P = gate|up pairs)
-constexpr int DN_BP = 256, DN_BQ = 128, DN_WP = 2, DN_WQ = 2;       // FWD_DOWN, BWD_DX
-constexpr int DH_BP = 256, DH_BQ = 128, DH_WP = 2, DH_WQ = 2;       // BWD_DH
-constexpr int WG_BP = 256, WG_BQ = 128, WG_WP = 2, WG_WQ = 2;       // weight gradients
+constexpr int FWD_BP = 256, FWD_BQ = 128, FWD_WP = 4, FWD_WQ = 2;   // FWD_GU (P = gate|up pairs)
+constexpr int DN_BP = 256, DN_BQ = 128, DN_WP = 4, DN_WQ = 2;       // FWD_DOWN, BWD_DX
+constexpr int DH_BP = 256, DH_BQ = 128, DH_WP = 4, DH_WQ = 2;       // BWD_DH
+constexpr int WG_BP = 256, WG_BQ = 128, WG_WP = 4, WG_WQ = 2;       // weight gradients
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
 // down-projection weight gradient (bf16 rounding of the fp32 product).
