@@ -45,6 +45,25 @@ def gemm_flops(R, d, f):
     }
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic.json), or None if the summary is for another
+    workload or the GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            j = json.load(fh)
+        with open(os.path.join(ROOT, j["source"]), "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, ValueError, KeyError):
+        return None
+    if sha != j.get("source_sha256") or j.get("workload") != workload:
+        return None
+    b = j.get("bytes_per_launch", {}).get(kernel)
+    return None if b is None else round(b["read"] + b["write"])
+
+
 def cpu_baseline(w, a, sample_tokens):
     """Oracle fwd+bwd on the first `sample_tokens` tokens of the same inputs."""
     import numpy as np
@@ -74,7 +93,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--profile-steps", type=int, default=5,
                     help="extra steps with per-kernel event timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -171,7 +190,8 @@ def main():
         achieved = flops[dom] / (gemm_us[dom] * 1e-6) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(dom, w.name),
                     "avg_launch_us": round(gemm_us[dom], 1),
                     "algorithmic_flop_per_launch": flops[dom]}
         tot_f = sum(flops[n] for n in gemm_us)
