@@ -34,7 +34,6 @@ namespace moe {
 
 enum GemmKind { FWD_GU = 0, FWD_DOWN = 1, BWD_DH = 2, BWD_DX = 3, BWD_DWDOWN = 4, BWD_DWGU = 5 };
 
-constexpr int kBK = 64;   // k per LDS stage: 64 bf16 = 128 bytes = 8 chunks per row
 
 struct GemmArgs {
   // operands
@@ -93,45 +92,51 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // ---------------------------------------------------------------- LDS layouts
 //
-// K-contiguous operand tile: ROWS rows x 64 k (128 bytes per row, 8 chunks of
-// 16 bytes).  Chunk ch of row r sits at slot r*8 + (ch ^ ((r >> 1) & 7)):
-// any 16 consecutive rows reading one chunk touch 16 distinct 16-byte bank
-// groups (two rows share a 256-byte bank line only when their parity differs).
-__device__ __forceinline__ int kc_slot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+// K-contiguous operand tile: ROWS rows x BK k (BK/8 chunks of 16 bytes per
+// row).  Chunk ch of row r sits at slot r*CPR + (ch ^ ((r / RPL) % CPR)),
+// RPL = rows per 256-byte bank line: any 16 consecutive rows reading one
+// chunk touch 16 distinct 16-byte bank groups.
+template <int BK>
+__device__ __forceinline__ int kc_slot(int row, int ch) {
+  constexpr int CPR = BK / 8, RPL = 16 / CPR;
+  return row * CPR + (ch ^ ((row / RPL) % CPR));
+}
 
-// Transposed operand tile: 64 k-rows x COLS columns (COLS*2 bytes per k-row).
+// Transposed operand tile: BK k-rows x COLS columns (COLS*2 bytes per k-row).
 // The 32-byte column block cb of k-row r sits at cb ^ tr_swz(r): the 16 k-rows
 // that one transpose read of a wave touches (8g + 0..3 for g = 0..3, or +4)
 // land on 8 distinct 32-byte bank groups per half-wave.
 __device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
-// Issue the direct-to-LDS loads of one 64-wide K stage of a ROWS-row operand
-// tile; every wave issues ROWS/(8*NW) instructions.  All arguments but lane are
-// wave-uniform.
+// Issue the direct-to-LDS loads of one BK-wide K stage of a ROWS-row operand
+// tile; every wave issues ROWS*BK/(512*NW) instructions of 1 KB.  All
+// arguments but lane are wave-uniform.
 //   K-contiguous: element (row i, k) at base[i*ld + k] (rows >= ROWS/2 of a
 //     paired tile from base2); rows_valid rows and kvalid k exist.
 //   transposed:   element (row i, k) at base[k*ld + i]; rows_valid columns
 //     and kvalid k-rows exist.
-template <int ROWS, bool TRANS, bool PAIRED, int NW>
+template <int ROWS, bool TRANS, bool PAIRED, int NW, int BK>
 __device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *base2, int ld,
                                             int rows_valid, int kvalid, int k0, u32x4_t *tile,
                                             int wave, int lane) {
-  constexpr int NI = ROWS / 8 / NW;
-  static_assert(NI >= 1 && NI * 8 * NW == ROWS, "tile rows split evenly over the waves");
+  constexpr int NI = ROWS * BK / 512 / NW;
+  static_assert(NI >= 1 && NI * 512 * NW == ROWS * BK, "tile splits evenly over the waves");
   if (!TRANS) {
+    constexpr int CPR = BK / 8;             // chunks per row
+    constexpr int RPI = 64 / CPR;           // rows per instruction
     constexpr int half_rows = PAIRED ? ROWS / 2 : ROWS;
+    // a wave's NI instructions cover RPI*NI consecutive rows, all in one half
+    static_assert(!PAIRED || (ROWS / 2 / RPI) % NI == 0, "paired halves align with waves");
+    const bool second = PAIRED && wave * NI >= ROWS / 2 / RPI;
     const int rv = min(rows_valid, half_rows);
     const uint32_t bytes = rv > 0 ? (uint32_t)rv * (uint32_t)ld * 2u : 0u;
-    // a wave's NI instructions cover 8*NI consecutive rows, all in one half
-    static_assert(!PAIRED || (ROWS / 16) % NI == 0, "paired halves align with waves");
-    const bool second = PAIRED && wave * NI >= ROWS / 16;
     const u32x4_t rs = make_rsrc(second ? base2 : base, bytes);
     const int row_shift = second ? ROWS / 2 : 0;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = wave * NI + i;          // rows 8q .. 8q+7
-      const int row = 8 * q + (lane >> 3);
-      const int ch = (lane & 7) ^ ((row >> 1) & 7);
+      const int q = wave * NI + i;          // rows RPI*q .. RPI*q + RPI-1
+      const int row = RPI * q + lane / CPR;
+      const int ch = (lane % CPR) ^ ((row / (16 / CPR)) % CPR);
       const int k = k0 + ch * 8;
       const uint32_t off =
           k < kvalid ? ((uint32_t)(row - row_shift) * (uint32_t)ld + (uint32_t)k) * 2u : kOOB;
@@ -143,7 +148,7 @@ __device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *ba
     // cols-1 of k-row krows-1): columns past the valid ones read the next
     // k-row's data (finite values feeding only masked outputs) or zeros past
     // the end, never memory beyond the tensor.
-    const int krows = min(kBK, kvalid - k0);
+    const int krows = min(BK, kvalid - k0);
     const int cols = min(rows_valid, ROWS);
     const uint32_t bytes = (krows > 0 && cols > 0)
                                ? ((uint32_t)(krows - 1) * (uint32_t)ld + (uint32_t)cols) * 2u
@@ -164,10 +169,10 @@ __device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *ba
 
 // MFMA operand fragment: rows r0..r0+15 of the tile, k step ks (32 wide);
 // lane l gets row r0 + l%16 with the 8 k-values of chunk 4*ks + l/16.
-template <int ROWS, bool TRANS>
+template <int ROWS, bool TRANS, int BK>
 __device__ __forceinline__ bf16x8_t read_frag(const u32x4_t *tile, int r0, int ks, int lane) {
   if (!TRANS) {
-    return as_bf16x8(tile[kc_slot(r0 + (lane & 15), ks * 4 + (lane >> 4))]);
+    return as_bf16x8(tile[kc_slot<BK>(r0 + (lane & 15), ks * 4 + (lane >> 4))]);
   } else {
     // two transpose reads: k-rows kb + j/4 (+4), columns r0 + 4*(j%4) .. +3
     const int j = lane & 15, g = lane >> 4;
@@ -195,188 +200,114 @@ template <> struct KindTraits<BWD_DX>     { static constexpr bool PT_ = true,  Q
 template <> struct KindTraits<BWD_DWDOWN> { static constexpr bool PT_ = true,  QT_ = true,  PAIRED = false, WG = true; };
 template <> struct KindTraits<BWD_DWGU>   { static constexpr bool PT_ = true,  QT_ = true,  PAIRED = false, WG = true; };
 
-// ------------------------------------------------------------------ kernel
+// ------------------------------------------------------------------ tiles
 //
-// 4 or 8 waves (WP x WQ); tile BP x BQ; K in stages of 64 through a
-// ring of 3 LDS buffers filled by direct-to-LDS loads two stages ahead.  One
-// barrier per stage: after it every wave's loads of the current stage have
-// landed and every wave has finished the stage before, whose buffer then
-// receives the loads of stage + 2.
-constexpr int kStages = 3;
+// One output tile of a grouped GEMM and the operands that feed it.  All fields
+// are wave-uniform.
+struct Tile {
+  int e, seg0, Me, p_tile, q_tile, p0, q0, nk;
+  const bf16_t *pb, *pb2, *qb;
+  int pld, prv, pkv, qld, qrv, qkv;
+};
+
 constexpr int kBandP = 4;   // P-tiles per band in the weight-gradient tile order
 
-template <int KIND, int BP, int BQ, int WP, int WQ>
-__global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
+// Logical tile L -> Tile.  s_off / s_ts: offsets[E+1] and tile_start[E+1]
+// staged in LDS.
+template <int KIND, int BP, int BQ, int BK>
+__device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, const int *s_ts,
+                                          int L) {
   using KT = KindTraits<KIND>;
-  constexpr int NW = WP * WQ;
-  static_assert(NW == 4 || NW == 8, "four or eight waves");
-  constexpr int FP = BP / WP / 16;
-  constexpr int FQ = BQ / WQ / 16;
-  static_assert(FP >= 1 && FQ >= 1, "tile too small");
-  static_assert(!KT::PAIRED || (FP % 2 == 0), "paired tiles need an even fragment count");
-  static_assert(BP % 128 == 0 && BQ % 128 == 0, "tiles are multiples of 128 rows");
-  constexpr int LOADS = (BP + BQ) / 8 / NW;   // direct loads per thread per stage
-
-  __shared__ u32x4_t sP0[BP * 8], sQ0[BQ * 8], sP1[BP * 8], sQ1[BQ * 8], sP2[BP * 8], sQ2[BQ * 8];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wp = wave % WP, wq = wave / WP;
-
-  // ---- XCD-aware tile order: workgroups are dealt round-robin over the 8
-  // XCDs; give each XCD a contiguous range of logical tiles.
-  const int nb = gridDim.x;
-  const int b = blockIdx.x;
-  const int L = (b & 7) * (nb >> 3) + (b >> 3);
-
-  int e, p_tile, q_tile, seg0, Me;
+  Tile t;
   if (KT::WG) {
     // Weight gradients: an expert's PT x QT tiles are walked in bands of
     // kBandP P-tiles; inside a band the P-tile index runs fastest, so the
     // tiles in flight on one XCD share a few P and Q operand slabs in its L2
     // (each P slab is read once per expert, each Q slab once per band).
-    if (L >= a.nlogical) return;
     const int per_e = a.PT * a.QT;
-    e = L / per_e;
-    const int rem = L - e * per_e;
+    t.e = L / per_e;
+    const int rem = L - t.e * per_e;
     const int band = rem / (kBandP * a.QT);
     const int in_band = rem - band * kBandP * a.QT;
     const int bp = min(kBandP, a.PT - band * kBandP);
-    q_tile = in_band / bp;
-    p_tile = band * kBandP + (in_band - q_tile * bp);
-    seg0 = a.offsets[e];
-    Me = a.offsets[e + 1] - seg0;
+    t.q_tile = in_band / bp;
+    t.p_tile = band * kBandP + (in_band - t.q_tile * bp);
+    t.seg0 = s_off[t.e];
+    t.Me = s_off[t.e + 1] - t.seg0;
   } else {
-    const int total = a.tile_start[a.E];
-    if (L >= total) return;
+    // Token GEMMs: (expert, P-tile, Q-tile) with the expert's token tiles
+    // fastest, so they share each weight slab in L2.
     int lo = 0, hi = a.E;   // largest e with tile_start[e] <= L
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.tile_start[mid] <= L) lo = mid; else hi = mid;
+      if (s_ts[mid] <= L) lo = mid; else hi = mid;
     }
-    e = lo;
-    seg0 = a.offsets[e];
-    Me = a.offsets[e + 1] - seg0;
-    const int qt_e = (Me + BQ - 1) / BQ;
-    const int rem = L - a.tile_start[e];
-    p_tile = rem / qt_e;
-    q_tile = rem - p_tile * qt_e;
+    t.e = lo;
+    t.seg0 = s_off[t.e];
+    t.Me = s_off[t.e + 1] - t.seg0;
+    const int qt_e = (t.Me + BQ - 1) / BQ;
+    const int rem = L - s_ts[t.e];
+    t.p_tile = rem / qt_e;
+    t.q_tile = rem - t.p_tile * qt_e;
   }
-  // the tile decode is wave-uniform; say so, so that buffer resources and
-  // LDS addresses stay in scalar registers
-  e = __builtin_amdgcn_readfirstlane(e);
-  p_tile = __builtin_amdgcn_readfirstlane(p_tile);
-  q_tile = __builtin_amdgcn_readfirstlane(q_tile);
-  seg0 = __builtin_amdgcn_readfirstlane(seg0);
-  Me = __builtin_amdgcn_readfirstlane(Me);
-  const int d = a.d, f = a.f;
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.p_tile = __builtin_amdgcn_readfirstlane(t.p_tile);
+  t.q_tile = __builtin_amdgcn_readfirstlane(t.q_tile);
+  t.seg0 = __builtin_amdgcn_readfirstlane(t.seg0);
+  t.Me = __builtin_amdgcn_readfirstlane(t.Me);
+  const int d = a.d, f = a.f, e = t.e, seg0 = t.seg0, Me = t.Me;
   const int64_t f2 = 2 * (int64_t)f;
-
-  // ---- operands of this tile
-  const bf16_t *pb = nullptr, *pb2 = nullptr, *qb = nullptr;
-  int pld = 0, prv = 0, pkv = 0, qld = 0, qrv = 0, qkv = 0;
+  t.p0 = t.p_tile * (KT::PAIRED ? BP / 2 : BP);
+  t.q0 = t.q_tile * BQ;
+  const int p0 = t.p0, q0 = t.q0;
+  t.pb2 = nullptr;
   int K = 0;
-  const int p0 = p_tile * (KT::PAIRED ? BP / 2 : BP);
-  const int q0 = q_tile * BQ;
   if (KIND == FWD_GU) {
     const bf16_t *W = a.w_gu + (int64_t)e * f2 * d;
-    pb = W + (int64_t)p0 * d; pb2 = W + ((int64_t)f + p0) * d; pld = d; prv = f - p0; pkv = d;
-    qb = a.x_perm + ((int64_t)seg0 + q0) * d; qld = d; qrv = Me - q0; qkv = d;
+    t.pb = W + (int64_t)p0 * d; t.pb2 = W + ((int64_t)f + p0) * d; t.pld = d; t.prv = f - p0; t.pkv = d;
+    t.qb = a.x_perm + ((int64_t)seg0 + q0) * d; t.qld = d; t.qrv = Me - q0; t.qkv = d;
     K = d;
   } else if (KIND == FWD_DOWN) {
     const bf16_t *W = a.w_down + (int64_t)e * d * f;
-    pb = W + (int64_t)p0 * f; pld = f; prv = d - p0; pkv = f;
-    qb = a.h + ((int64_t)seg0 + q0) * f; qld = f; qrv = Me - q0; qkv = f;
+    t.pb = W + (int64_t)p0 * f; t.pld = f; t.prv = d - p0; t.pkv = f;
+    t.qb = a.h + ((int64_t)seg0 + q0) * f; t.qld = f; t.qrv = Me - q0; t.qkv = f;
     K = f;
   } else if (KIND == BWD_DH) {
     const bf16_t *W = a.w_down + (int64_t)e * d * f;
-    pb = W + p0; pld = f; prv = f - p0; pkv = d;
-    qb = a.dy_perm + ((int64_t)seg0 + q0) * d; qld = d; qrv = Me - q0; qkv = d;
+    t.pb = W + p0; t.pld = f; t.prv = f - p0; t.pkv = d;
+    t.qb = a.dy_perm + ((int64_t)seg0 + q0) * d; t.qld = d; t.qrv = Me - q0; t.qkv = d;
     K = d;
   } else if (KIND == BWD_DX) {
     const bf16_t *W = a.w_gu + (int64_t)e * f2 * d;
-    pb = W + p0; pld = d; prv = d - p0; pkv = (int)f2;
-    qb = a.dgu + ((int64_t)seg0 + q0) * f2; qld = (int)f2; qrv = Me - q0; qkv = (int)f2;
+    t.pb = W + p0; t.pld = d; t.prv = d - p0; t.pkv = (int)f2;
+    t.qb = a.dgu + ((int64_t)seg0 + q0) * f2; t.qld = (int)f2; t.qrv = Me - q0; t.qkv = (int)f2;
     K = (int)f2;
   } else if (KIND == BWD_DWDOWN) {
-    pb = a.h + (int64_t)seg0 * f + p0; pld = f; prv = f - p0; pkv = Me;
-    qb = a.s_perm + (int64_t)seg0 * d + q0; qld = d; qrv = d - q0; qkv = Me;
+    t.pb = a.h + (int64_t)seg0 * f + p0; t.pld = f; t.prv = f - p0; t.pkv = Me;
+    t.qb = a.s_perm + (int64_t)seg0 * d + q0; t.qld = d; t.qrv = d - q0; t.qkv = Me;
     K = Me;
   } else {   // BWD_DWGU
-    pb = a.x_perm + (int64_t)seg0 * d + p0; pld = d; prv = d - p0; pkv = Me;
-    qb = a.dgu + (int64_t)seg0 * f2 + q0; qld = (int)f2; qrv = (int)(f2 - q0); qkv = Me;
+    t.pb = a.x_perm + (int64_t)seg0 * d + p0; t.pld = d; t.prv = d - p0; t.pkv = Me;
+    t.qb = a.dgu + (int64_t)seg0 * f2 + q0; t.qld = (int)f2; t.qrv = (int)(f2 - q0); t.qkv = Me;
     K = Me;
   }
-  if (!pb2) pb2 = pb;
+  if (!t.pb2) t.pb2 = t.pb;
+  t.nk = (K + BK - 1) / BK;
+  return t;
+}
 
-  f32x4_t acc[FP][FQ];
-#pragma unroll
-  for (int i = 0; i < FP; ++i)
-#pragma unroll
-    for (int j = 0; j < FQ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // fragment rows inside the LDS tiles
-  int prow[FP], qrow[FQ];
-#pragma unroll
-  for (int i = 0; i < FP; ++i) {
-    if (KT::PAIRED) {
-      constexpr int HALF = BP / 2, PW = BP / 2 / WP;
-      prow[i] = (i < FP / 2) ? wp * PW + i * 16 : HALF + wp * PW + (i - FP / 2) * 16;
-    } else {
-      prow[i] = wp * (BP / WP) + i * 16;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < FQ; ++j) qrow[j] = wq * (BQ / WQ) + j * 16;
-  // token-row fragments past the end of the expert's rows hold only zeros:
-  // skip their MFMAs (wave-uniform); weight-gradient tiles have no such rows
-  bool qlive[FQ];
-#pragma unroll
-  for (int j = 0; j < FQ; ++j) qlive[j] = KT::WG || (q0 + qrow[j] < Me);
-
-#define MOE_ISSUE(kt, SP, SQ)                                                                  \
-  do {                                                                                       \
-    issue_stage<BP, KT::PT_, KT::PAIRED, NW>(pb, pb2, pld, prv, pkv, (kt) * kBK, SP, wave, lane); \
-    issue_stage<BQ, KT::QT_, false, NW>(qb, qb, qld, qrv, qkv, (kt) * kBK, SQ, wave, lane);       \
-  } while (0)
-#define MOE_STEP(kt, SP, SQ, NP, NQ)                                                    \
-  do {                                                                                \
-    if ((kt) + 1 < nk) wait_vm_lgkm0<LOADS>(); else wait_vm_lgkm0<0>();              \
-    __builtin_amdgcn_s_barrier();                                                     \
-    if ((kt) + 2 < nk) MOE_ISSUE((kt) + 2, NP, NQ);                                   \
-    _Pragma("unroll") for (int ks = 0; ks < kBK / 32; ++ks) {                         \
-      bf16x8_t pf[FP], qf[FQ];                                                        \
-      _Pragma("unroll") for (int i = 0; i < FP; ++i)                                  \
-        pf[i] = read_frag<BP, KT::PT_>(SP, prow[i], ks, lane);                        \
-      _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                  \
-        qf[j] = read_frag<BQ, KT::QT_>(SQ, qrow[j], ks, lane);                        \
-      _Pragma("unroll") for (int j = 0; j < FQ; ++j) {                                \
-        if (!qlive[j]) continue;                                                      \
-        _Pragma("unroll") for (int i = 0; i < FP; ++i)                                \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
-      }                                                                               \
-    }                                                                                 \
-  } while (0)
-
-  // stage kt lives in buffer kt % 3; before it is used, the loads of stage
-  // kt+1 (if any) may still be in flight.
-  const int nk = (K + kBK - 1) / kBK;
-  if (nk > 0) {
-    MOE_ISSUE(0, sP0, sQ0);
-    if (nk > 1) MOE_ISSUE(1, sP1, sQ1);
-    for (int kt = 0; kt < nk; kt += 3) {
-      MOE_STEP(kt, sP0, sQ0, sP2, sQ2);
-      if (kt + 1 < nk) MOE_STEP(kt + 1, sP1, sQ1, sP0, sQ0);
-      if (kt + 2 < nk) MOE_STEP(kt + 2, sP2, sQ2, sP1, sQ1);
-    }
-  }
-#undef MOE_STEP
-#undef MOE_ISSUE
-
-  // ---- epilogues.  Lane holds D[prow+4*(lane/16)+v][qrow+lane%16].
+// ------------------------------------------------------------------ epilogues
+//
+// Lane holds D[prow[i] + 4*(lane/16) + v][qrow[j] + lane%16].
+template <int KIND, int FP, int FQ, int WP>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const f32x4_t (&acc)[FP][FQ],
+                                         const int (&prow)[FP], const int (&qrow)[FQ], int lane,
+                                         int wp) {
+  const int d = a.d, f = a.f;
+  const int64_t f2 = 2 * (int64_t)f;
   const int er = 4 * (lane >> 4);
   const int ec = lane & 15;
+  const int seg0 = t.seg0, Me = t.Me, p0 = t.p0, q0 = t.q0;
   if (KIND == FWD_GU) {
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
@@ -461,12 +392,12 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
       if (a.o_drs && rowok && lane < 16)
-        a.o_drs[r * nparts + p_tile * WP + wp] = part;
+        a.o_drs[r * nparts + t.p_tile * WP + wp] = part;
     }
   } else {   // weight gradients: dw[e][q][p]
     const int Pdim = (KIND == BWD_DWDOWN) ? f : d;
     const int Qdim = (KIND == BWD_DWDOWN) ? d : (int)f2;
-    float *out = a.o_dw + (int64_t)e * Pdim * Qdim;
+    float *out = a.o_dw + (int64_t)t.e * Pdim * Qdim;
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       const int q = q0 + qrow[j] + ec;
@@ -479,6 +410,182 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ kernel
+//
+// Persistent: the grid has one block per CU (a multiple of 8).  The logical
+// tiles are split into 8 contiguous chunks, one per XCD (workgroups are dealt
+// round-robin over the XCDs), and the blocks of an XCD take its chunk's tiles
+// round-robin.  A block runs its tiles as one flat sequence of 64-wide K
+// stages through a ring of NS LDS buffers filled by direct-to-LDS loads NS-1
+// stages ahead, across tile boundaries, so the next tile's first stages are
+// in flight while a tile's epilogue runs.  One barrier per stage: after it
+// every wave's loads of the current stage have landed and every wave has
+// finished the stage before, whose buffer then receives stage + NS - 1.
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
+__global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
+  using KT = KindTraits<KIND>;
+  constexpr int NW = WP * WQ;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int FP = BP / WP / 16;
+  constexpr int FQ = BQ / WQ / 16;
+  static_assert(FP >= 1 && FQ >= 1, "tile too small");
+  static_assert(!KT::PAIRED || (FP % 2 == 0), "paired tiles need an even fragment count");
+  static_assert(BP % 128 == 0 && BQ % 128 == 0, "tiles are multiples of 128 rows");
+  constexpr int LOADS = (BP + BQ) * BK / 512 / NW;   // direct loads per thread per stage
+  constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;   // 16-byte slots: P part, stage
+  static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
+  static_assert(BK == 32 || BK == 64, "K stage of 32 or 64");
+  static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+
+  __shared__ u32x4_t smem[NS * SS];
+  __shared__ int s_off[kMaxExperts + 1], s_ts[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wp = wave % WP, wq = wave / WP;
+
+  // routing maps into LDS: tile decodes then never wait on vector memory
+  for (int i = tid; i <= a.E; i += NW * 64) {
+    s_off[i] = a.offsets[i];
+    if (!KT::WG) s_ts[i] = a.tile_start[i];
+  }
+  __syncthreads();
+
+  const int total = __builtin_amdgcn_readfirstlane(KT::WG ? a.nlogical : s_ts[a.E]);
+  const int per = gridDim.x >> 3;                  // blocks per XCD
+  const int chunk = (total + 7) >> 3;
+  const int cbeg = (blockIdx.x & 7) * chunk;
+  const int cend = min(total, cbeg + chunk);
+  const int first = cbeg + (blockIdx.x >> 3);
+
+  // fragment rows inside the LDS tiles (fixed per wave)
+  int prow[FP], qrow[FQ];
+#pragma unroll
+  for (int i = 0; i < FP; ++i) {
+    if (KT::PAIRED) {
+      constexpr int HALF = BP / 2, PW = BP / 2 / WP;
+      prow[i] = (i < FP / 2) ? wp * PW + i * 16 : HALF + wp * PW + (i - FP / 2) * 16;
+    } else {
+      prow[i] = wp * (BP / WP) + i * 16;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FQ; ++j) qrow[j] = wq * (BQ / WQ) + j * 16;
+
+  f32x4_t acc[FP][FQ];
+#pragma unroll
+  for (int i = 0; i < FP; ++i)
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // ---- issue cursor: next stage to load
+  int iL = first, ikt = 0;
+  bool ivalid = iL < cend;
+  Tile it{};
+  if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);
+  while (ivalid && it.nk == 0) {
+    iL += per;
+    ivalid = iL < cend;
+    if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);
+  }
+  int s_issued = 0, s_done = 0;
+
+#define MOE_ISSUE_NEXT()                                                                      \
+  do {                                                                                        \
+    u32x4_t *st_ = smem + (s_issued % NS) * SS;                                               \
+    issue_stage<BP, KT::PT_, KT::PAIRED, NW, BK>(it.pb, it.pb2, it.pld, it.prv, it.pkv,       \
+                                                 ikt * BK, st_, wave, lane);                  \
+    issue_stage<BQ, KT::QT_, false, NW, BK>(it.qb, it.qb, it.qld, it.qrv, it.qkv, ikt * BK,  \
+                                            st_ + SP, wave, lane);                            \
+    ++s_issued;                                                                               \
+    if (++ikt >= it.nk) {                                                                     \
+      ikt = 0;                                                                                \
+      do {                                                                                    \
+        iL += per;                                                                            \
+        ivalid = iL < cend;                                                                   \
+        if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);                         \
+      } while (ivalid && it.nk == 0);                                                         \
+    }                                                                                         \
+  } while (0)
+
+  // prologue: the first NS-1 stages
+#pragma unroll
+  for (int n = 0; n < NS - 1; ++n)
+    if (ivalid) MOE_ISSUE_NEXT();
+
+  // ---- compute cursor
+  int cL = first, ckt = 0;
+  bool cvalid = cL < cend;
+  Tile ct{};
+  if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+  while (cvalid && ct.nk == 0) {   // experts with no rows: zero weight gradients
+    epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
+    cL += per;
+    cvalid = cL < cend;
+    if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+  }
+  bool qlive[FQ];
+#pragma unroll
+  for (int j = 0; j < FQ; ++j) qlive[j] = KT::WG || (ct.q0 + qrow[j] < ct.Me);
+
+  // After an epilogue, stores are in flight among the loads.  Vector-memory
+  // loads and stores need not retire in issue order relative to each other,
+  // so the first wait after an epilogue waits for everything.
+  bool stores_pending = false;
+  while (cvalid) {
+    // the stage about to be used landed; up to NS-2 later stages may still
+    // be in flight
+    {
+      const int later = stores_pending ? 0 : min(s_issued - s_done - 1, NS - 2);
+      if (NS > 3 && later >= 2) wait_vm_lgkm0<(NS > 3 ? 2 : 0) * LOADS>();
+      else if (NS > 2 && later == 1) wait_vm_lgkm0<(NS > 2 ? 1 : 0) * LOADS>();
+      else wait_vm_lgkm0<0>();
+    }
+    stores_pending = false;
+    __builtin_amdgcn_s_barrier();
+    if (ivalid) MOE_ISSUE_NEXT();
+    const u32x4_t *sp = smem + (s_done % NS) * SS;
+    const u32x4_t *sq = sp + SP;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8_t pf[FP], qf[FQ];
+#pragma unroll
+      for (int i = 0; i < FP; ++i) pf[i] = read_frag<BP, KT::PT_, BK>(sp, prow[i], ks, lane);
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) qf[j] = read_frag<BQ, KT::QT_, BK>(sq, qrow[j], ks, lane);
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) {
+        if (!qlive[j]) continue;   // token rows past the expert's end: zeros
+#pragma unroll
+        for (int i = 0; i < FP; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    ++s_done;
+    if (++ckt >= ct.nk) {
+      epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
+      stores_pending = true;
+#pragma unroll
+      for (int i = 0; i < FP; ++i)
+#pragma unroll
+        for (int j = 0; j < FQ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      ckt = 0;
+      do {
+        cL += per;
+        cvalid = cL < cend;
+        if (cvalid) {
+          ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+          if (ct.nk == 0) epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
+        }
+      } while (cvalid && ct.nk == 0);
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) qlive[j] = KT::WG || (ct.q0 + qrow[j] < ct.Me);
+    }
+  }
+#undef MOE_ISSUE_NEXT
 }
 
 // tile_start[e] = sum over e' < e of ceil(M_e' / BQ) * PT  (one block)
@@ -591,10 +698,12 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
 // ------------------------------------------------------------------ launch
 
 // tile configurations
-constexpr int FWD_BP = 256, FWD_BQ = 128, FWD_WP = 4, FWD_WQ = 2;   // FWD_GU (P = gate|up pairs)
-constexpr int DN_BP = 256, DN_BQ = 128, DN_WP = 4, DN_WQ = 2;       // FWD_DOWN, BWD_DX
-constexpr int DH_BP = 256, DH_BQ = 128, DH_WP = 4, DH_WQ = 2;       // BWD_DH
-constexpr int WG_BP = 256, WG_BQ = 128, WG_WP = 4, WG_WQ = 2;       // weight gradients
+// 256 x 256 tiles, 8 waves of 128 x 64 (two per SIMD), K in stages of 32
+// through 4 LDS buffers of 32 KB: three stages (96 KB) in flight.
+constexpr int FWD_BP = 256, FWD_BQ = 256, FWD_WP = 2, FWD_WQ = 4, FWD_NS = 4, FWD_BK = 32;  // FWD_GU
+constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 4, DN_BK = 32;  // FWD_DOWN, BWD_DX
+constexpr int DH_BP = 256, DH_BQ = 256, DH_WP = 2, DH_WQ = 4, DH_NS = 4, DH_BK = 32;  // BWD_DH
+constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK = 32;  // weight grads
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
 // down-projection weight gradient (bf16 rounding of the fp32 product).
@@ -616,7 +725,25 @@ __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy
 
 static inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
-template <int KIND, int BP, int BQ, int WP, int WQ>
+// Persistent grid: one block per CU of the current device (a multiple of 8),
+// never more blocks than tiles (rounded up to 8).
+static int persistent_grid(int64_t tiles) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  int g = cus[dev] / 8 * 8;
+  if (g < 8) g = 8;
+  const int64_t t = pad8(tiles < 1 ? 1 : tiles);
+  return (int)(t < g ? t : g);
+}
+
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
 static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start, const char *name,
                              hipStream_t s) {
   if (R == 0) return MOE_OK;
@@ -625,18 +752,18 @@ static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start,
   MOE_LAUNCH("tile_prefix", s,
              k_tile_prefix<<<1, 1024, 0, s>>>(a.offsets, a.E, BQ, PT, tile_start));
   const int64_t bound = ((R + BQ - 1) / BQ + a.E) * (int64_t)PT;
-  const int grid = pad8(bound);
-  MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ><<<grid, WP * WQ * 64, 0, s>>>(a)));
+  const int grid = persistent_grid(bound);
+  MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK><<<grid, WP * WQ * 64, 0, s>>>(a)));
   return check_launch(name);
 }
 
-template <int KIND, int BP, int BQ, int WP, int WQ>
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
 static int launch_wgrad_gemm(GemmArgs a, int Pdim, int Qdim, const char *name, hipStream_t s) {
   a.PT = (Pdim + BP - 1) / BP;
   a.QT = (Qdim + BQ - 1) / BQ;
   a.nlogical = a.E * a.PT * a.QT;
-  const int grid = pad8(a.nlogical);
-  MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ><<<grid, WP * WQ * 64, 0, s>>>(a)));
+  const int grid = persistent_grid(a.nlogical);
+  MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK><<<grid, WP * WQ * 64, 0, s>>>(a)));
   return check_launch(name);
 }
 
@@ -716,10 +843,10 @@ extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, i
   a.E = E;
   a.d = d;
   a.f = f;
-  rc = launch_token_gemm<FWD_GU, FWD_BP, FWD_BQ, FWD_WP, FWD_WQ>(
+  rc = launch_token_gemm<FWD_GU, FWD_BP, FWD_BQ, FWD_WP, FWD_WQ, FWD_NS, FWD_BK>(
       a, R, (f + FWD_BP / 2 - 1) / (FWD_BP / 2), ts0, "gg_fwd_gate_up_swiglu", s);
   if (rc) return rc;
-  return launch_token_gemm<FWD_DOWN, DN_BP, DN_BQ, DN_WP, DN_WQ>(
+  return launch_token_gemm<FWD_DOWN, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK>(
       a, R, (d + DN_BP - 1) / DN_BP, ts1, "gg_fwd_down_scale", s);
 }
 
@@ -767,7 +894,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   a.f = f;
   const int pt_dh = (f + DH_BP - 1) / DH_BP;
   // 1. dGU (and d_row_scale partials) from dY_perm and W_down
-  rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ>(a, R, pt_dh, ts0,
+  rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ, DH_NS, DH_BK>(a, R, pt_dh, ts0,
                                                              "gg_bwd_dh_dswiglu", s);
   if (rc) return rc;
   if (d_row_scale && R > 0) {
@@ -778,7 +905,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
     if (rc) return rc;
   }
   // 2. dX_perm = dGU . W_gu
-  rc = launch_token_gemm<BWD_DX, DN_BP, DN_BQ, DN_WP, DN_WQ>(a, R, (d + DN_BP - 1) / DN_BP, ts1,
+  rc = launch_token_gemm<BWD_DX, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK>(a, R, (d + DN_BP - 1) / DN_BP, ts1,
                                                              "gg_bwd_dx", s);
   if (rc) return rc;
   // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
@@ -792,10 +919,10 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   }
   a.s_perm = s_perm;
   a.o_dw = dw_down;
-  rc = launch_wgrad_gemm<BWD_DWDOWN, WG_BP, WG_BQ, WG_WP, WG_WQ>(a, f, d, "gg_bwd_dw_down", s);
+  rc = launch_wgrad_gemm<BWD_DWDOWN, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, f, d, "gg_bwd_dw_down", s);
   if (rc) return rc;
   // 4. dW_gu[e] = dGU^T X_perm        -> [E, 2f, d]
   a.o_dw = dw_gu;
-  return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ>(a, d, 2 * f, "gg_bwd_dw_gate_up",
+  return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, d, 2 * f, "gg_bwd_dw_gate_up",
                                                                 s);
 }

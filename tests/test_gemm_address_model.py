@@ -15,14 +15,14 @@ import pytest
 
 from mixture_experts_layer_03_amd import inputs as I
 
-BK = 64
+BK = 32   # K stage width of the kernels
 TILES = {  # kind: (BP, BQ, P transposed, Q transposed, paired)
-    "FWD_GU": (256, 128, False, False, True),
-    "FWD_DOWN": (256, 128, False, False, False),
-    "BWD_DH": (256, 128, True, False, False),
-    "BWD_DX": (256, 128, True, False, False),
-    "BWD_DWDOWN": (256, 128, True, True, False),
-    "BWD_DWGU": (256, 128, True, True, False),
+    "FWD_GU": (256, 256, False, False, True),
+    "FWD_DOWN": (256, 256, False, False, False),
+    "BWD_DH": (256, 256, True, False, False),
+    "BWD_DX": (256, 256, True, False, False),
+    "BWD_DWDOWN": (256, 256, True, True, False),
+    "BWD_DWGU": (256, 256, True, True, False),
 }
 
 
