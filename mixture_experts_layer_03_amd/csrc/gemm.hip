@@ -41,6 +41,7 @@ struct GemmArgs {
   const float *row_scale;      // [R] or null
   const int32_t *offsets;      // [E+1]
   const int32_t *tile_start;   // [E+1] (token-tiled kinds)
+  int32_t *counters;           // [8] per-XCD tile counters, zero at launch (token-tiled kinds)
   // outputs
   bf16_t *o_gu, *o_h, *o_y, *o_dgu, *o_dx;
   float *o_dw, *o_drs;         // dw: [E, Qdim, Pdim]; drs partials [R, PT*WP]
@@ -75,12 +76,17 @@ constexpr uint32_t kOOB = 0x80000000u;   // an offset past any resource: reads z
 // inline assembly so that the compiler does not guard later LDS reads of
 // other buffers with waits for these loads; the kernel waits for them itself
 // (wait_vm_lgkm0) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(u32x4_t rs, u32x4_t *dst, uint32_t voff) {
-  const uint32_t lds = (uint32_t)(uintptr_t)((LDS_AS void *)dst);
+__device__ __forceinline__ void dma16_at(u32x4_t rs, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(rs)
                : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)((const LDS_AS void *)p);
+}
+__device__ __forceinline__ void dma16(u32x4_t rs, u32x4_t *dst, uint32_t voff) {
+  dma16_at(rs, lds_addr(dst), voff);
 }
 
 // s_waitcnt with vmcnt <= n (n < 64) and lgkmcnt = 0 (gfx9 encoding).
@@ -93,13 +99,17 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // ---------------------------------------------------------------- LDS layouts
 //
 // K-contiguous operand tile: ROWS rows x BK k (BK/8 chunks of 16 bytes per
-// row).  Chunk ch of row r sits at slot r*CPR + (ch ^ ((r / RPL) % CPR)),
-// RPL = rows per 256-byte bank line: any 16 consecutive rows reading one
-// chunk touch 16 distinct 16-byte bank groups.
+// row).  Chunk ch of row r sits at slot r*CPR + (ch ^ kc_swz(r)), with the
+// swizzle taken from row bits 1.. : measured on gfx950, 16-byte reads of 16
+// consecutive rows (one chunk each) then run at the conflict-free rate, which
+// a swizzle on bits 2.. (one 256-byte line per XOR value) does not reach.
+// The swizzle repeats every 16 rows.
+template <int BK>
+__device__ __forceinline__ int kc_swz(int row) { return (row >> 1) % (BK / 8); }
+
 template <int BK>
 __device__ __forceinline__ int kc_slot(int row, int ch) {
-  constexpr int CPR = BK / 8, RPL = 16 / CPR;
-  return row * CPR + (ch ^ ((row / RPL) % CPR));
+  return row * (BK / 8) + (ch ^ kc_swz<BK>(row));
 }
 
 // Transposed operand tile: BK k-rows x COLS columns (COLS*2 bytes per k-row).
@@ -136,7 +146,7 @@ __device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *ba
     for (int i = 0; i < NI; ++i) {
       const int q = wave * NI + i;          // rows RPI*q .. RPI*q + RPI-1
       const int row = RPI * q + lane / CPR;
-      const int ch = (lane % CPR) ^ ((row / (16 / CPR)) % CPR);
+      const int ch = (lane % CPR) ^ kc_swz<BK>(row);
       const int k = k0 + ch * 8;
       const uint32_t off =
           k < kvalid ? ((uint32_t)(row - row_shift) * (uint32_t)ld + (uint32_t)k) * 2u : kOOB;
@@ -167,28 +177,142 @@ __device__ __forceinline__ void issue_stage(const bf16_t *base, const bf16_t *ba
   }
 }
 
-// MFMA operand fragment: rows r0..r0+15 of the tile, k step ks (32 wide);
-// lane l gets row r0 + l%16 with the 8 k-values of chunk 4*ks + l/16.
-template <int ROWS, bool TRANS, int BK>
-__device__ __forceinline__ bf16x8_t read_frag(const u32x4_t *tile, int r0, int ks, int lane) {
+// Loop-invariant byte offsets of one wave's direct-to-LDS loads of an
+// operand, for every stage and tile of a kind (the leading dimension ld is
+// fixed per kind); the stage's k0 moves the resource base instead.
+//   K-contiguous: row part + swizzled 16-byte chunk of the stage's k range.
+//   transposed:   k-row part + swizzled 16-byte column chunk.
+// Instruction i + 2 covers the rows (k-rows) 2*RPI (2*64/C16) further on,
+// where both swizzles repeat, so its offset is instruction i's plus `stride`:
+// only the first two offsets are kept.
+template <int ROWS, bool TRANS, bool PAIRED, int NW, int BK>
+__device__ __forceinline__ void init_voff(int ld, int wave, int lane,
+                                          uint32_t (&voff)[(ROWS * BK / 512 / NW) < 2
+                                                               ? (ROWS * BK / 512 / NW)
+                                                               : 2],
+                                          uint32_t &stride) {
+  constexpr int NI = ROWS * BK / 512 / NW;
+  constexpr int NV = NI < 2 ? NI : 2;
   if (!TRANS) {
-    return as_bf16x8(tile[kc_slot<BK>(r0 + (lane & 15), ks * 4 + (lane >> 4))]);
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;
+    static_assert((2 * RPI) % (2 * CPR) == 0, "chunk swizzle repeats after two instructions");
+    const bool second = PAIRED && wave * NI >= ROWS / 2 / RPI;
+    const int row_shift = second ? ROWS / 2 : 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int q = wave * NI + i;
+      const int row = RPI * q + lane / CPR;
+      const int ch = (lane % CPR) ^ kc_swz<BK>(row);
+      voff[i] = ((uint32_t)(row - row_shift) * (uint32_t)ld + (uint32_t)ch * 8u) * 2u;
+    }
+    stride = (uint32_t)(2 * RPI) * (uint32_t)ld * 2u;
   } else {
-    // two transpose reads: k-rows kb + j/4 (+4), columns r0 + 4*(j%4) .. +3
-    const int j = lane & 15, g = lane >> 4;
-    const int c = r0 + 4 * (j & 3);
-    const int cb = c >> 4;                  // 32-byte column block
-    const int within = (c & 15) * 2;        // byte offset inside the block
-    const char *base = reinterpret_cast<const char *>(tile);
-    const int kr0 = ks * 32 + 8 * g + (j >> 2);
-    const int kr1 = kr0 + 4;
-    const char *a0 = base + kr0 * (ROWS * 2) + ((cb ^ tr_swz(kr0)) << 5) + within;
-    const char *a1 = base + kr1 * (ROWS * 2) + ((cb ^ tr_swz(kr1)) << 5) + within;
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t *)(a0));
-    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t *)(a1));
+    constexpr int C16 = ROWS / 8;
+    // k-rows 8w + 2i + lane/32 (i < 4): adding 4 keeps bits 0, 1 and 3
+    static_assert(ROWS == 256 && NI <= 4, "column swizzle repeats after two instructions");
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int lin = (wave * NI + i) * 64 + lane;
+      const int kr = lin / C16;
+      const int c16 = (lin % C16) ^ (tr_swz(kr) << 1);
+      voff[i] = ((uint32_t)kr * (uint32_t)ld + (uint32_t)c16 * 8u) * 2u;
+    }
+    stride = (uint32_t)(128 / C16) * (uint32_t)ld * 2u;
+  }
+}
+
+// Plan one operand's loads for the stage at k0, with the offsets of
+// init_voff: this wave's instruction i then loads with resource rs into LDS
+// address m + i*step.  Only the resource (base and byte count, wave-uniform)
+// changes per stage.  A K-contiguous stage that ends past kvalid (a K tail)
+// is issued here by issue_stage, which masks each lane's chunk; its planned
+// loads then read nothing (byte count 0) into the spare LDS slot `dummy`.
+template <int ROWS, bool TRANS, bool PAIRED, int NW, int BK>
+__device__ __forceinline__ void plan_operand(const bf16_t *base, const bf16_t *base2, int ld,
+                                             int rows_valid, int kvalid, int k0, u32x4_t *tile,
+                                             int wave, int lane, uint32_t dummy, u32x4_t &rs,
+                                             uint32_t &m, uint32_t &step) {
+  constexpr int NI = ROWS * BK / 512 / NW;
+  m = lds_addr(tile + wave * NI * 64);
+  step = 1024;
+  if (!TRANS) {
+    if (k0 + BK > kvalid) {
+      issue_stage<ROWS, TRANS, PAIRED, NW, BK>(base, base2, ld, rows_valid, kvalid, k0, tile, wave,
+                                               lane);
+      rs = make_rsrc(base, 0);
+      m = dummy;
+      step = 0;
+      return;
+    }
+    // Rows past rows_valid start at or beyond the byte count and read zeros;
+    // valid rows end inside it (k0 + BK <= kvalid = ld).
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;
+    constexpr int half_rows = PAIRED ? ROWS / 2 : ROWS;
+    const bool second = PAIRED && wave * NI >= ROWS / 2 / RPI;
+    const int rv = min(rows_valid, half_rows);
+    const uint32_t bytes = rv > 0 ? ((uint32_t)rv * (uint32_t)ld - (uint32_t)k0) * 2u : 0u;
+    rs = make_rsrc((second ? base2 : base) + k0, bytes);
+  } else {
+    // k-rows past the K range start at or beyond the byte count (ld >= cols)
+    const int krows = min(BK, kvalid - k0);
+    const int cols = min(rows_valid, ROWS);
+    const uint32_t bytes = (krows > 0 && cols > 0)
+                               ? ((uint32_t)(krows - 1) * (uint32_t)ld + (uint32_t)cols) * 2u
+                               : 0u;
+    rs = make_rsrc(base + (int64_t)k0 * ld, bytes);
+  }
+}
+
+// MFMA operand fragments (v_mfma_f32_16x16x32_bf16 A/B layout): rows
+// r0..r0+15 of a tile, lane l gets row r0 + l%16 with the 8 k-values of
+// 16-byte chunk l/16 of the 32-wide k step.
+//
+// K-contiguous tile: byte offset of the lane's chunk for rows r0.. at k step
+// ks.  Fragments 16*m rows further sit 16*m*CPR slots further (the chunk
+// swizzle repeats every 16 rows).
+template <int BK>
+__device__ __forceinline__ uint32_t kc_frag_off(int r0, int ks, int lane) {
+  return (uint32_t)kc_slot<BK>(r0 + (lane & 15), ks * 4 + (lane >> 4)) * 16u;
+}
+
+// Transposed tile: byte offset of the lane's first transpose read for
+// columns c0..c0+15 (c0 a multiple of 16) at k step 0.  Lane j of each
+// 16-lane group g reads k-row 8g + j/4, columns c0 + 4*(j%4) .. +3; after the
+// transpose, lane j holds column c0 + j for those 4 k-rows.  The second read
+// is 4 k-rows further (same swizzle), k step ks is 32 k-rows further.
+template <int ROWS>
+__device__ __forceinline__ uint32_t tr_frag_off(int c0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int kr = 8 * g + (j >> 2);
+  return (uint32_t)(kr * (ROWS * 2) + (((c0 >> 4) ^ tr_swz(kr)) << 5) + (j & 3) * 8);
+}
+
+// Row offset of fragment i from the wave's first fragment (paired tiles put
+// the wave's up-projection fragments in the second half).
+template <bool PAIRED, int ROWS, int F>
+__device__ constexpr int frag_delta(int i) {
+  return PAIRED ? (i < F / 2 ? 16 * i : ROWS / 2 + 16 * (i - F / 2)) : 16 * i;
+}
+
+// Fragment i at k step ks of the operand region sb of a stage; rd holds the
+// lane offsets (per k step if K-contiguous, per fragment if transposed).
+template <bool TRANS, bool PAIRED, int ROWS, int BK, int F, int NR>
+__device__ __forceinline__ bf16x8_t frag_at(const LDS_AS char *sb, const uint32_t (&rd)[NR], int i,
+                                            int ks) {
+  if constexpr (TRANS) {
+    const LDS_AS char *p = sb + rd[i] + ks * (32 * ROWS * 2);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t *)(p));
+    const s16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t *)(p + 4 * (ROWS * 2)));
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
     const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
+  } else {
+    constexpr int CPR = BK / 8;
+    static_assert(NR <= 2, "one or two k steps per stage");
+    const int delta = frag_delta<PAIRED, ROWS, F>(i);
+    const uint32_t r = (NR == 2 && ks) ? rd[NR - 1] : rd[0];
+    return as_bf16x8(*(const LDS_AS u32x4_t *)(sb + r + delta * (CPR * 16)));
   }
 }
 
@@ -413,16 +537,56 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
 }
 
 // ------------------------------------------------------------------ kernel
-//
+
+// s_waitcnt for the loads of the stage that has `younger` stages of LOADS
+// loads each issued after it (loads complete in issue order; stores in
+// flight only make the count conservative), and for all LDS reads.
+template <int LOADS>
+__device__ __forceinline__ void wait_stage(int younger) {
+  if (younger >= 3) wait_vm_lgkm0<3 * LOADS>();
+  else if (younger == 2) wait_vm_lgkm0<2 * LOADS>();
+  else if (younger == 1) wait_vm_lgkm0<LOADS>();
+  else wait_vm_lgkm0<0>();
+}
+
+// Number of a wave's Q fragments (16 token rows each, from token row q)
+// that hold tokens of an expert with Me rows; weight-gradient tiles are
+// always whole.
+template <bool WG, int FQ>
+__device__ __forceinline__ int live_frags(int q, int Me) {
+  if (WG) return FQ;
+  const int rows = Me - q;
+  return rows <= 0 ? 0 : min(FQ, (rows + 15) >> 4);
+}
+
+// acc[i][j] += P-fragment i x Q-fragment j for the live Q fragments (token
+// rows past an expert's end are zeros; their products are skipped).
+template <int FP, int FQ>
+__device__ __forceinline__ void mfma_block(f32x4_t (&acc)[FP][FQ], const bf16x8_t (&pf)[FP],
+                                           const bf16x8_t (&qf)[FQ], int nlive) {
+#pragma unroll
+  for (int j = 0; j < FQ; ++j) {
+    if (j < nlive) {
+#pragma unroll
+      for (int i = 0; i < FP; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
 // Persistent: the grid has one block per CU (a multiple of 8).  The logical
 // tiles are split into 8 contiguous chunks, one per XCD (workgroups are dealt
 // round-robin over the XCDs), and the blocks of an XCD take its chunk's tiles
-// round-robin.  A block runs its tiles as one flat sequence of 64-wide K
-// stages through a ring of NS LDS buffers filled by direct-to-LDS loads NS-1
-// stages ahead, across tile boundaries, so the next tile's first stages are
-// in flight while a tile's epilogue runs.  One barrier per stage: after it
-// every wave's loads of the current stage have landed and every wave has
-// finished the stage before, whose buffer then receives stage + NS - 1.
+// round-robin.  A block runs its tiles as one flat sequence of 32-wide K
+// stages through a ring of NS LDS buffers filled by direct-to-LDS loads NS
+// stages ahead, across tile boundaries.
+//
+// Each wave keeps the MFMA fragments of the stage it computes in registers:
+// after the barrier that publishes stage n+1 (every wave's loads of it have
+// landed, every wave's reads of stage n are done, so stage n's buffer takes
+// the loads of stage n+NS), the wave reads stage n+1's fragments between the
+// MFMAs of stage n.  After a tile's epilogue, the next tile's first MFMAs are
+// issued before the wait, so the epilogue's stores drain under them.
 template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
 __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   using KT = KindTraits<KIND>;
@@ -430,50 +594,97 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int FP = BP / WP / 16;
   constexpr int FQ = BQ / WQ / 16;
-  static_assert(FP >= 1 && FQ >= 1, "tile too small");
+  static_assert(FP >= 1 && FQ >= 1 && FQ <= FP, "fragment counts");
   static_assert(!KT::PAIRED || (FP % 2 == 0), "paired tiles need an even fragment count");
   static_assert(BP % 128 == 0 && BQ % 128 == 0, "tiles are multiples of 128 rows");
-  constexpr int LOADS = (BP + BQ) * BK / 512 / NW;   // direct loads per thread per stage
+  static_assert(BK == 32 || BK == 64, "stages of one or two 32-wide k steps");
+  constexpr int KS = BK / 32;                                // k steps per stage
+  constexpr int NIP = BP * BK / 512 / NW, NIQ = BQ * BK / 512 / NW;
+  constexpr int LOADS = NIP + NIQ;                           // direct loads per thread per stage
   constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;   // 16-byte slots: P part, stage
   static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
-  static_assert(BK == 32 || BK == 64, "K stage of 32 or 64");
-  static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+  static_assert(3 * LOADS < 64, "vmcnt range");
+  static_assert(LOADS <= FP, "one load per P-fragment row of the interleaved stage");
+  constexpr int RP = KT::PT_ ? 2 : 1, RQ = KT::QT_ ? 2 : 1;  // LDS reads per fragment
 
   __shared__ u32x4_t smem[NS * SS];
   __shared__ int s_off[kMaxExperts + 1], s_ts[kMaxExperts + 1];
+  __shared__ u32x4_t sdummy[64];   // target of loads that read nothing
+  __shared__ int s_ring[16];       // token GEMMs: the block's tile sequence
+  const LDS_AS char *lds = (const LDS_AS char *)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave % WP, wq = wave / WP;
 
+  const int per = gridDim.x >> 3;                  // blocks per XCD
+  // Token GEMMs: tiles differ in cost (an expert's last token tile is
+  // partly empty), so after its first tile a block takes the next free tile
+  // of its XCD's chunk from that XCD's counter.  The block's sequence of
+  // tiles goes through the LDS ring s_ring: wave 0 fetches tile number
+  // n + NS of the sequence when the loads reach tile n, at least one
+  // barrier before any wave needs it.  Weight-gradient tiles all cost the
+  // same per expert: blocks take them round-robin.
+  int total = 0;
+  if (KT::WG) {
+    total = a.nlogical;
+  } else {
+    total = a.tile_start[a.E];
+  }
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int chunk = (total + 7) >> 3;
+  const int cbeg = (blockIdx.x & 7) * chunk;
+  const int cend = min(total, cbeg + chunk);
+  const int first = cbeg + (blockIdx.x >> 3);
+  int32_t *const ctr = KT::WG ? nullptr : a.counters + (blockIdx.x & 7);
+#define MOE_FETCH() ({                                                                        \
+    const int t_ = cbeg + per + atomicAdd(ctr, 1);                                            \
+    t_ < cend ? t_ : -1;                                                                      \
+  })
+
   // routing maps into LDS: tile decodes then never wait on vector memory
   for (int i = tid; i <= a.E; i += NW * 64) {
     s_off[i] = a.offsets[i];
     if (!KT::WG) s_ts[i] = a.tile_start[i];
   }
+  if (!KT::WG && tid == 0) {
+    s_ring[0] = first < cend ? first : -1;
+    for (int n = 1; n <= NS; ++n) s_ring[n] = first < cend ? MOE_FETCH() : -1;
+  }
   __syncthreads();
 
-  const int total = __builtin_amdgcn_readfirstlane(KT::WG ? a.nlogical : s_ts[a.E]);
-  const int per = gridDim.x >> 3;                  // blocks per XCD
-  const int chunk = (total + 7) >> 3;
-  const int cbeg = (blockIdx.x & 7) * chunk;
-  const int cend = min(total, cbeg + chunk);
-  const int first = cbeg + (blockIdx.x >> 3);
-
   // fragment rows inside the LDS tiles (fixed per wave)
+  const int prow0 = KT::PAIRED ? wp * (BP / 2 / WP) : wp * (BP / WP);
+  const int qrow0 = wq * (BQ / WQ);
   int prow[FP], qrow[FQ];
 #pragma unroll
-  for (int i = 0; i < FP; ++i) {
-    if (KT::PAIRED) {
-      constexpr int HALF = BP / 2, PW = BP / 2 / WP;
-      prow[i] = (i < FP / 2) ? wp * PW + i * 16 : HALF + wp * PW + (i - FP / 2) * 16;
-    } else {
-      prow[i] = wp * (BP / WP) + i * 16;
-    }
-  }
+  for (int i = 0; i < FP; ++i) prow[i] = prow0 + frag_delta<KT::PAIRED, BP, FP>(i);
 #pragma unroll
-  for (int j = 0; j < FQ; ++j) qrow[j] = wq * (BQ / WQ) + j * 16;
+  for (int j = 0; j < FQ; ++j) qrow[j] = qrow0 + 16 * j;
+
+  // loop-invariant load and read offsets
+  const int d = a.d, f = a.f;
+  const int pld = (KIND == FWD_GU || KIND == BWD_DX || KIND == BWD_DWGU) ? d : f;
+  const int qld = (KIND == FWD_DOWN) ? f : (KIND == BWD_DX || KIND == BWD_DWGU) ? 2 * f : d;
+  uint32_t voffP[NIP < 2 ? NIP : 2], voffQ[NIQ < 2 ? NIQ : 2], vstrP, vstrQ;
+  init_voff<BP, KT::PT_, KT::PAIRED, NW, BK>(pld, wave, lane, voffP, vstrP);
+  init_voff<BQ, KT::QT_, false, NW, BK>(qld, wave, lane, voffQ, vstrQ);
+  uint32_t rdP[KT::PT_ ? FP : KS], rdQ[KT::QT_ ? FQ : KS];
+  if constexpr (KT::PT_) {
+#pragma unroll
+    for (int i = 0; i < FP; ++i) rdP[i] = tr_frag_off<BP>(prow[i], lane);
+  } else {
+#pragma unroll
+    for (int h = 0; h < KS; ++h) rdP[h] = kc_frag_off<BK>(prow0, h, lane);
+  }
+  if constexpr (KT::QT_) {
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) rdQ[j] = (uint32_t)(SP * 16) + tr_frag_off<BQ>(qrow[j], lane);
+  } else {
+#pragma unroll
+    for (int h = 0; h < KS; ++h) rdQ[h] = (uint32_t)(SP * 16) + kc_frag_off<BK>(qrow0, h, lane);
+  }
 
   f32x4_t acc[FP][FQ];
 #pragma unroll
@@ -482,7 +693,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     for (int j = 0; j < FQ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // ---- issue cursor: next stage to load
-  int iL = first, ikt = 0;
+  int iL = first, ikt = 0, iseq = 0;
   bool ivalid = iL < cend;
   Tile it{};
   if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);
@@ -493,31 +704,75 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   }
   int s_issued = 0, s_done = 0;
 
-#define MOE_ISSUE_NEXT()                                                                      \
+  // Loads of stage s_issued: planned once per stage (resources and LDS
+  // destinations in scalar registers), issued one instruction at a time,
+  // then the cursor moves on.  With every stage issued, planned loads read
+  // nothing into the spare slot.
+  const uint32_t dummy = lds_addr(sdummy);
+  u32x4_t rsP = make_rsrc(a.offsets, 0), rsQ = rsP;
+  uint32_t mP = dummy, mQ = dummy, stepP = 0, stepQ = 0;
+#define MOE_PLAN()                                                                            \
   do {                                                                                        \
-    u32x4_t *st_ = smem + (s_issued % NS) * SS;                                               \
-    issue_stage<BP, KT::PT_, KT::PAIRED, NW, BK>(it.pb, it.pb2, it.pld, it.prv, it.pkv,       \
-                                                 ikt * BK, st_, wave, lane);                  \
-    issue_stage<BQ, KT::QT_, false, NW, BK>(it.qb, it.qb, it.qld, it.qrv, it.qkv, ikt * BK,  \
-                                            st_ + SP, wave, lane);                            \
-    ++s_issued;                                                                               \
-    if (++ikt >= it.nk) {                                                                     \
-      ikt = 0;                                                                                \
-      do {                                                                                    \
-        iL += per;                                                                            \
-        ivalid = iL < cend;                                                                   \
-        if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);                         \
-      } while (ivalid && it.nk == 0);                                                         \
+    if (ivalid) {                                                                             \
+      u32x4_t *st_ = smem + ((unsigned)s_issued % NS) * SS;                                   \
+      plan_operand<BP, KT::PT_, KT::PAIRED, NW, BK>(it.pb, it.pb2, pld, it.prv, it.pkv,       \
+                                                    ikt * BK, st_, wave, lane, dummy, rsP,    \
+                                                    mP, stepP);                               \
+      plan_operand<BQ, KT::QT_, false, NW, BK>(it.qb, it.qb, qld, it.qrv, it.qkv, ikt * BK,   \
+                                               st_ + SP, wave, lane, dummy, rsQ, mQ, stepQ);  \
+    } else {                                                                                  \
+      rsP = make_rsrc(a.offsets, 0);                                                          \
+      rsQ = rsP;                                                                              \
+      mP = mQ = dummy;                                                                        \
+      stepP = stepQ = 0;                                                                      \
     }                                                                                         \
   } while (0)
+#define MOE_DMA(n)                                                                            \
+  do {                                                                                        \
+    if ((n) < NIP)                                                                            \
+      dma16_at(rsP, mP + (n) * stepP, voffP[(n) % 2] + ((n) / 2) * vstrP);                    \
+    else                                                                                      \
+      dma16_at(rsQ, mQ + ((n) - NIP) * stepQ,                                                 \
+               voffQ[((n) - NIP) % 2] + (((n) - NIP) / 2) * vstrQ);                           \
+  } while (0)
+#define MOE_ADVANCE()                                                                         \
+  do {                                                                                        \
+    if (ivalid) {                                                                             \
+      ++s_issued;                                                                             \
+      if (++ikt >= it.nk) {                                                                   \
+        ikt = 0;                                                                              \
+        if (KT::WG) {                                                                         \
+          do {                                                                                \
+            iL += per;                                                                        \
+            ivalid = iL < cend;                                                               \
+            if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);                 \
+          } while (ivalid && it.nk == 0);                                                     \
+        } else {                                                                              \
+          ++iseq;                                                                             \
+          iL = __builtin_amdgcn_readfirstlane(s_ring[iseq & 15]);                             \
+          ivalid = iL >= 0;                                                                   \
+          if (ivalid) {                                                                       \
+            it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);                             \
+            if (tid == 0) s_ring[(iseq + NS) & 15] = MOE_FETCH();                             \
+          }                                                                                   \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
+#define MOE_ISSUE_ALL()                                                                       \
+  do {                                                                                        \
+    MOE_PLAN();                                                                               \
+    _Pragma("unroll") for (int n_ = 0; n_ < LOADS; ++n_) MOE_DMA(n_);                         \
+    MOE_ADVANCE();                                                                            \
+  } while (0)
 
-  // prologue: the first NS-1 stages
+  // prologue: the first NS stages
 #pragma unroll
-  for (int n = 0; n < NS - 1; ++n)
-    if (ivalid) MOE_ISSUE_NEXT();
+  for (int n = 0; n < NS; ++n)
+    if (ivalid) MOE_ISSUE_ALL();
 
   // ---- compute cursor
-  int cL = first, ckt = 0;
+  int cL = first, cseq = 0;
   bool cvalid = cL < cend;
   Tile ct{};
   if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
@@ -527,52 +782,132 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     cvalid = cL < cend;
     if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
   }
-  bool qlive[FQ];
-#pragma unroll
-  for (int j = 0; j < FQ; ++j) qlive[j] = KT::WG || (ct.q0 + qrow[j] < ct.Me);
+  // live Q fragments of this wave in the current tile (a prefix)
+  int nlive = cvalid ? live_frags<KT::WG, FQ>(ct.q0 + qrow0, ct.Me) : 0;
 
-  // After an epilogue, stores are in flight among the loads.  Vector-memory
-  // loads and stores need not retire in issue order relative to each other,
-  // so the first wait after an epilogue waits for everything.
-  bool stores_pending = false;
-  while (cvalid) {
-    // the stage about to be used landed; up to NS-2 later stages may still
-    // be in flight
-    {
-      const int later = stores_pending ? 0 : min(s_issued - s_done - 1, NS - 2);
-      if (NS > 3 && later >= 2) wait_vm_lgkm0<(NS > 3 ? 2 : 0) * LOADS>();
-      else if (NS > 2 && later == 1) wait_vm_lgkm0<(NS > 2 ? 1 : 0) * LOADS>();
-      else wait_vm_lgkm0<0>();
-    }
-    stores_pending = false;
+  // All fragments of k step `half` of the stage in LDS buffer (stage % NS)
+  // into registers.
+#define MOE_READ_STEP(stage, half)                                                            \
+  do {                                                                                        \
+    const LDS_AS char *rb_ = lds + ((unsigned)(stage) % NS) * (SS * 16);                      \
+    _Pragma("unroll") for (int i = 0; i < FP; ++i)                                            \
+        pf[i] = frag_at<KT::PT_, KT::PAIRED, BP, BK, FP>(rb_, rdP, i, (half));                \
+    _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                            \
+        qf[j] = frag_at<KT::QT_, false, BQ, BK, FQ>(rb_, rdQ, j, (half));                     \
+  } while (0)
+
+  // MFMAs of the fragments in registers with the fragments of k step rh of
+  // stage rs read in between: after P-fragment i's MFMAs its register takes
+  // the new P-fragment i; the new Q-fragments arrive in spare registers
+  // during the first FQ rows.  With LD, the loads planned by MOE_PLAN go out
+  // one per P-fragment row.
+#define MOE_WARM(rs, rh, LD)                                                                  \
+  do {                                                                                        \
+    const LDS_AS char *nb_ = lds + ((unsigned)(rs) % NS) * (SS * 16);                         \
+    bf16x8_t qn_[FQ];                                                                         \
+    _Pragma("unroll") for (int i = 0; i < FQ; ++i) {                                          \
+      _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                          \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
+      pf[i] = frag_at<KT::PT_, KT::PAIRED, BP, BK, FP>(nb_, rdP, i, (rh));                    \
+      qn_[i] = frag_at<KT::QT_, false, BQ, BK, FQ>(nb_, rdQ, i, (rh));                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, FQ, 0);                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, RP + RQ, 0);                                \
+      if ((LD) && i < LOADS) MOE_DMA(i);                                                      \
+    }                                                                                         \
+    _Pragma("unroll") for (int i = FQ; i < FP; ++i) {                                         \
+      _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                          \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
+      pf[i] = frag_at<KT::PT_, KT::PAIRED, BP, BK, FP>(nb_, rdP, i, (rh));                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, FQ, 0);                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, RP, 0);                                     \
+      if ((LD) && i < LOADS) MOE_DMA(i);                                                      \
+    }                                                                                         \
+    _Pragma("unroll") for (int j = 0; j < FQ; ++j) qf[j] = qn_[j];                            \
+  } while (0)
+
+  // Wait until stage s_done + 1 has landed and every wave is done reading
+  // stage s_done; stage s_done's buffer then takes the next loads.
+#define MOE_SYNC()                                                                            \
+  do {                                                                                        \
+    const bool has_next_ = s_done + 1 < s_issued;                                             \
+    wait_stage<LOADS>(has_next_ ? s_issued - s_done - 2 : 0);                                 \
+    __builtin_amdgcn_s_barrier();                                                             \
+  } while (0)
+
+  bf16x8_t pf[FP], qf[FQ];
+  if (cvalid) {
+    wait_stage<LOADS>(s_issued - 1);
     __builtin_amdgcn_s_barrier();
-    if (ivalid) MOE_ISSUE_NEXT();
-    const u32x4_t *sp = smem + (s_done % NS) * SS;
-    const u32x4_t *sq = sp + SP;
+    MOE_READ_STEP(0, 0);
+  }
+
+  // One tile per pass; the fragments of its first k step are in registers.
+  // Each stage holds KS k steps of 32; the barrier that publishes stage n+1
+  // (and frees stage n's buffer for the loads of stage n + NS) comes before
+  // the last k step of stage n.  A tile's first and last k steps issue their
+  // MFMAs before that wait (the first ones overlap the previous tile's
+  // stores); in between, whole tiles read the next k step between the MFMAs,
+  // and tiles with token rows missing read it after them.
+  while (cvalid) {
+    const int nk = ct.nk;
+    if (nlive >= FQ) {
+      mfma_block<FP, FQ>(acc, pf, qf, FQ);
+      if constexpr (KS == 1) {
+        MOE_SYNC();
+        if (ivalid) MOE_ISSUE_ALL();
+        if (nk > 1) MOE_READ_STEP(s_done + 1, 0);
+        ++s_done;
+        for (int kt = 1; kt < nk - 1; ++kt) {
+          MOE_SYNC();
+          MOE_PLAN();
+          MOE_WARM(s_done + 1, 0, true);
+          MOE_ADVANCE();
+          ++s_done;
+        }
+        if (nk > 1) {
+          mfma_block<FP, FQ>(acc, pf, qf, FQ);
+          MOE_SYNC();
+          if (ivalid) MOE_ISSUE_ALL();
+          ++s_done;
+        }
+      } else {
+        MOE_READ_STEP(s_done, 1);
+        for (int kt = 0; kt < nk - 1; ++kt) {
+          MOE_SYNC();
+          MOE_PLAN();
+          MOE_WARM(s_done + 1, 0, true);
+          MOE_ADVANCE();
+          ++s_done;
+          MOE_WARM(s_done, 1, false);
+        }
+        mfma_block<FP, FQ>(acc, pf, qf, FQ);
+        MOE_SYNC();
+        if (ivalid) MOE_ISSUE_ALL();
+        ++s_done;
+      }
+    } else {
+      for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t pf[FP], qf[FQ];
-#pragma unroll
-      for (int i = 0; i < FP; ++i) pf[i] = read_frag<BP, KT::PT_, BK>(sp, prow[i], ks, lane);
-#pragma unroll
-      for (int j = 0; j < FQ; ++j) qf[j] = read_frag<BQ, KT::QT_, BK>(sq, qrow[j], ks, lane);
-#pragma unroll
-      for (int j = 0; j < FQ; ++j) {
-        if (!qlive[j]) continue;   // token rows past the expert's end: zeros
-#pragma unroll
-        for (int i = 0; i < FP; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
+        for (int h = 0; h < KS; ++h) {
+          mfma_block<FP, FQ>(acc, pf, qf, nlive);
+          if (h == KS - 1) {
+            MOE_SYNC();
+            if (ivalid) MOE_ISSUE_ALL();
+            if (kt + 1 < nk) MOE_READ_STEP(s_done + 1, 0);
+            ++s_done;
+          } else {
+            MOE_READ_STEP(s_done, h + 1);
+          }
+        }
       }
     }
-    ++s_done;
-    if (++ckt >= ct.nk) {
-      epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
-      stores_pending = true;
+    // The last barrier published stage s_done: the next tile's first stage.
+    epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
 #pragma unroll
-      for (int i = 0; i < FP; ++i)
+    for (int i = 0; i < FP; ++i)
 #pragma unroll
-        for (int j = 0; j < FQ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      ckt = 0;
+      for (int j = 0; j < FQ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (KT::WG) {
       do {
         cL += per;
         cvalid = cL < cend;
@@ -581,14 +916,29 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
           if (ct.nk == 0) epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
         }
       } while (cvalid && ct.nk == 0);
-#pragma unroll
-      for (int j = 0; j < FQ; ++j) qlive[j] = KT::WG || (ct.q0 + qrow[j] < ct.Me);
+    } else {
+      ++cseq;
+      cL = __builtin_amdgcn_readfirstlane(s_ring[cseq & 15]);
+      cvalid = cL >= 0;
+      if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+    }
+    if (cvalid) {
+      nlive = live_frags<KT::WG, FQ>(ct.q0 + qrow0, ct.Me);
+      MOE_READ_STEP(s_done, 0);
     }
   }
-#undef MOE_ISSUE_NEXT
+#undef MOE_SYNC
+#undef MOE_READ_STEP
+#undef MOE_WARM
+#undef MOE_PLAN
+#undef MOE_DMA
+#undef MOE_ADVANCE
+#undef MOE_ISSUE_ALL
+#undef MOE_FETCH
 }
 
-// tile_start[e] = sum over e' < e of ceil(M_e' / BQ) * PT  (one block)
+// tile_start[e] = sum over e' < e of ceil(M_e' / BQ) * PT, and the 8 tile
+// counters that follow tile_start[E] cleared (one block)
 __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict__ offsets, int E,
                                                       int BQ, int PT,
                                                       int32_t *__restrict__ tile_start) {
@@ -609,6 +959,7 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict_
   }
   if (e < E) tile_start[e + 1] = s[e];
   if (e == 0) tile_start[0] = 0;
+  if (e < 8) tile_start[E + 1 + e] = 0;   // the GEMM's per-XCD tile counters
 }
 
 // d_row_scale[r] = sum of its partials in fixed order
@@ -700,9 +1051,9 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
 // tile configurations
 // 256 x 256 tiles, 8 waves of 128 x 64 (two per SIMD), K in stages of 32
 // through 4 LDS buffers of 32 KB: three stages (96 KB) in flight.
-constexpr int FWD_BP = 256, FWD_BQ = 256, FWD_WP = 2, FWD_WQ = 4, FWD_NS = 4, FWD_BK = 32;  // FWD_GU
-constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 4, DN_BK = 32;  // FWD_DOWN, BWD_DX
-constexpr int DH_BP = 256, DH_BQ = 256, DH_WP = 2, DH_WQ = 4, DH_NS = 4, DH_BK = 32;  // BWD_DH
+constexpr int FWD_BP = 256, FWD_BQ = 256, FWD_WP = 2, FWD_WQ = 4, FWD_NS = 2, FWD_BK = 64;  // FWD_GU
+constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 2, DN_BK = 64;  // FWD_DOWN, BWD_DX
+constexpr int DH_BP = 256, DH_BQ = 256, DH_WP = 2, DH_WQ = 4, DH_NS = 2, DH_BK = 64;  // BWD_DH
 constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK = 32;  // weight grads
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
@@ -749,6 +1100,7 @@ static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start,
   if (R == 0) return MOE_OK;
   a.PT = PT;
   a.tile_start = tile_start;
+  a.counters = tile_start + a.E + 1;
   MOE_LAUNCH("tile_prefix", s,
              k_tile_prefix<<<1, 1024, 0, s>>>(a.offsets, a.E, BQ, PT, tile_start));
   const int64_t bound = ((R + BQ - 1) / BQ + a.E) * (int64_t)PT;
@@ -783,7 +1135,8 @@ static int check_ffn(const char *fn, int E, int64_t R, int d, int f, int dtype) 
   return MOE_OK;
 }
 
-static size_t tile_start_bytes(int E) { return align_up(sizeof(int32_t) * (size_t)(E + 1), 256); }
+// tile_start[E+1] and 8 tile counters
+static size_t tile_start_bytes(int E) { return align_up(sizeof(int32_t) * (size_t)(E + 1 + 8), 256); }
 
 static size_t drs_bytes(int64_t R, int f) {
   const int nparts = (f + DH_BP - 1) / DH_BP * DH_WP;

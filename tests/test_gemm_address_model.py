@@ -15,7 +15,7 @@ import pytest
 
 from mixture_experts_layer_03_amd import inputs as I
 
-BK = 32   # K stage width of the kernels
+BK = 64   # K stage width of the kernels (two 32-wide MFMA k steps)
 TILES = {  # kind: (BP, BQ, P transposed, Q transposed, paired)
     "FWD_GU": (256, 256, False, False, True),
     "FWD_DOWN": (256, 256, False, False, False),
@@ -27,13 +27,24 @@ TILES = {  # kind: (BP, BQ, P transposed, Q transposed, paired)
 
 
 def kc_end(base, ld, rows_valid, rows, kvalid):
-    """Largest readable byte (exclusive) of a K-contiguous tile, in elements*2."""
+    """Largest readable byte (exclusive) of a K-contiguous tile over all its K
+    stages.  Whole stages (k0 + BK <= kvalid) move the resource base to
+    base + k0 and shrink its byte count by k0; the K-tail stage keeps the
+    base and masks chunks past kvalid."""
     rv = min(rows_valid, rows)
     if rv <= 0:
         return base * 2
-    nbytes = rv * ld * 2
-    gen = ((rows - 1) * ld + min(kvalid, ld)) * 2          # largest generated offset + 16
-    return base * 2 + min(nbytes, gen)
+    end = base * 2
+    for k0 in range(0, kvalid, BK):
+        if k0 + BK <= kvalid:
+            nbytes = rv * ld * 2 - 2 * k0
+            gen = ((rows - 1) * ld + BK) * 2                # largest generated offset + 16
+            end = max(end, (base + k0) * 2 + min(nbytes, gen))
+        else:
+            nbytes = rv * ld * 2
+            gen = ((rows - 1) * ld + min(kvalid, ld)) * 2
+            end = max(end, base * 2 + min(nbytes, gen))
+    return end
 
 
 def tr_end(base, ld, cols_valid, rows, kvalid, k0, whole_rows=False):
@@ -124,3 +135,64 @@ def test_in_range_reads_stay_inside_tensors(case):
 def test_whole_row_resources_would_overrun():
     off = _offsets(4096 * 4, 32, 5)
     assert worst_overrun(4096, 2880, 32, 4, 2880, off, whole_rows=True) > 0
+
+
+# --------------------------------------------------------------------------
+# Per-lane load offsets: the kernel keeps the offsets of a wave's first two
+# load instructions per operand and derives instruction i from instruction
+# i % 2 plus (i // 2) * stride.  Restate the full offset formula and check
+# that claim for every wave, lane and instruction of each tile operand.
+
+def kc_swz(row, cpr):
+    return (row >> 1) % cpr
+
+
+def tr_swz(r):
+    return (r & 3) | (((r >> 3) & 1) << 2)
+
+
+def voff_full(rows, trans, paired, nw, bk, ld, wave, lane, i):
+    ni = rows * bk // 512 // nw
+    if not trans:
+        cpr, rpi = bk // 8, 64 // (bk // 8)
+        second = paired and wave * ni >= rows // 2 // rpi
+        shift = rows // 2 if second else 0
+        row = rpi * (wave * ni + i) + lane // cpr
+        ch = (lane % cpr) ^ kc_swz(row, cpr)
+        return ((row - shift) * ld + ch * 8) * 2
+    c16 = rows // 8
+    lin = (wave * ni + i) * 64 + lane
+    kr = lin // c16
+    return (kr * ld + ((lin % c16) ^ (tr_swz(kr) << 1)) * 8) * 2
+
+
+def voff_stride(rows, trans, bk, ld):
+    if not trans:
+        return 2 * (64 // (bk // 8)) * ld * 2
+    return (128 // (rows // 8)) * ld * 2
+
+
+@pytest.mark.parametrize("trans,paired", [(False, False), (False, True), (True, False)])
+def test_load_offsets_follow_two_kept_offsets(trans, paired):
+    rows, nw, bk, ld = 256, 8, BK, 2880
+    ni = rows * bk // 512 // nw
+    stride = voff_stride(rows, trans, bk, ld)
+    for wave in range(nw):
+        for lane in range(64):
+            kept = [voff_full(rows, trans, paired, nw, bk, ld, wave, lane, i) for i in range(min(ni, 2))]
+            for i in range(ni):
+                assert voff_full(rows, trans, paired, nw, bk, ld, wave, lane, i) == \
+                    kept[i % 2] + (i // 2) * stride
+
+
+def test_load_slots_cover_the_stage_once():
+    """Every 16-byte chunk of a stage tile is loaded by exactly one lane."""
+    rows, nw, bk, ld = 256, 8, BK, 2880
+    ni = rows * bk // 512 // nw
+    for trans in (False, True):
+        seen = set()
+        for wave in range(nw):
+            for i in range(ni):
+                for lane in range(64):
+                    seen.add(voff_full(rows, trans, False, nw, bk, ld, wave, lane, i))
+        assert len(seen) == rows * bk // 8
