@@ -522,15 +522,34 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
     const int Pdim = (KIND == BWD_DWDOWN) ? f : d;
     const int Qdim = (KIND == BWD_DWDOWN) ? d : (int)f2;
     float *out = a.o_dw + (int64_t)t.e * Pdim * Qdim;
+    // Fragments i and i+1 (P rows 16 apart) are stored together: lane
+    // (g, c) of fragment i+1, rotated by 8 within its 16-lane row, trades
+    // places so that one store covers Q rows c%8 with P columns 0..31 of the
+    // pair (128 contiguous bytes per row) and the other store Q rows 8 + c%8.
+    static_assert(FP % 2 == 0, "fragment pairs");
+    const bool lo = ec < 8;
+    const int qa = q0 + (ec & 7), pa = p0 + er + (lo ? 0 : 16), pb_ = p0 + er + (lo ? 16 : 0);
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
-      const int q = q0 + qrow[j] + ec;
-      if (q >= Qdim) continue;
+      const int qA = qa + qrow[j], qB = qA + 8;
 #pragma unroll
-      for (int i = 0; i < FP; ++i) {
-        const int p = p0 + prow[i] + er;
-        if (p >= Pdim) continue;
-        *reinterpret_cast<f32x4_t *>(out + (int64_t)q * Pdim + p) = acc[i][j];
+      for (int i = 0; i < FP; i += 2) {
+        f32x4_t r, A, B;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          // row_ror:8 (DPP control 0x128): lane c of each 16-lane row takes
+          // lane (c + 8) % 16.  (The element goes through a scalar: a bit
+          // cast of a vector element expression here read element 0.)
+          const float e = acc[i + 1][j][v];
+          r[v] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(e), 0x128, 0xf, 0xf, false));
+          A[v] = lo ? acc[i][j][v] : r[v];
+          B[v] = lo ? r[v] : acc[i][j][v];
+        }
+        const int pA = pa + prow[i], pB = pb_ + prow[i];
+        if (qA < Qdim && pA < Pdim)
+          *reinterpret_cast<f32x4_t *>(out + (int64_t)qA * Pdim + pA) = A;
+        if (qB < Qdim && pB < Pdim)
+          *reinterpret_cast<f32x4_t *>(out + (int64_t)qB * Pdim + pB) = B;
       }
     }
   }
