@@ -334,7 +334,6 @@ struct Tile {
   int pld, prv, pkv, qld, qrv, qkv;
 };
 
-constexpr int kBandP = 4;   // P-tiles per band in the weight-gradient tile order
 
 // Logical tile L -> Tile.  s_off / s_ts: offsets[E+1] and tile_start[E+1]
 // staged in LDS.
@@ -344,18 +343,15 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, c
   using KT = KindTraits<KIND>;
   Tile t;
   if (KT::WG) {
-    // Weight gradients: an expert's PT x QT tiles are walked in bands of
-    // kBandP P-tiles; inside a band the P-tile index runs fastest, so the
-    // tiles in flight on one XCD share a few P and Q operand slabs in its L2
-    // (each P slab is read once per expert, each Q slab once per band).
+    // Weight gradients: (expert, P-tile, Q-tile) with the Q-tile fastest:
+    // the tiles in flight on one XCD share their P operand slab and walk
+    // the expert's Q slabs together (measured fastest of the P-tile band
+    // widths tried on the gpt-oss-20b-like workload).
     const int per_e = a.PT * a.QT;
     t.e = L / per_e;
     const int rem = L - t.e * per_e;
-    const int band = rem / (kBandP * a.QT);
-    const int in_band = rem - band * kBandP * a.QT;
-    const int bp = min(kBandP, a.PT - band * kBandP);
-    t.q_tile = in_band / bp;
-    t.p_tile = band * kBandP + (in_band - t.q_tile * bp);
+    t.p_tile = rem / a.QT;
+    t.q_tile = rem - t.p_tile * a.QT;
     t.seg0 = s_off[t.e];
     t.Me = s_off[t.e + 1] - t.seg0;
   } else {
