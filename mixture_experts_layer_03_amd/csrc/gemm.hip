@@ -417,6 +417,8 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, c
 }
 
 // ------------------------------------------------------------------ epilogues
+
+constexpr int kDhBatch = 4;   // dSwiGLU epilogue: fragments per batch of saved-activation loads
 //
 // Lane holds D[prow[i] + 4*(lane/16) + v][qrow[j] + lane%16].
 template <int KIND, int FP, int FQ, int WP>
@@ -457,12 +459,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
     }
   } else if (KIND == FWD_DOWN || KIND == BWD_DX) {
     bf16_t *out = (KIND == FWD_DOWN) ? a.o_y : a.o_dx;
+    float wj[FQ];   // combine weights of the wave's token rows, loaded up front
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int q = q0 + qrow[j] + ec;
+      wj[j] = (KIND == FWD_DOWN && a.row_scale) ? a.row_scale[(int64_t)seg0 + (q < Me ? q : 0)] : 1.0f;
+    }
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       const int q = q0 + qrow[j] + ec;
       if (q >= Me) continue;
       const int64_t r = (int64_t)seg0 + q;
-      const float w = (KIND == FWD_DOWN && a.row_scale) ? a.row_scale[r] : 1.0f;
+      const float w = wj[j];
 #pragma unroll
       for (int i = 0; i < FP; ++i) {
         const int n = p0 + prow[i] + er;
@@ -476,37 +484,54 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
     const int nparts = a.PT * WP;
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
+      // token row (rows past the expert's end read row seg0 and store
+      // nothing) and its combine weight
       const int q = q0 + qrow[j] + ec;
       const bool rowok = q < Me;
       const int64_t r = (int64_t)seg0 + (rowok ? q : 0);
-      const float w = (rowok && a.row_scale) ? a.row_scale[r] : 1.0f;
+      const float w = a.row_scale ? a.row_scale[r] : 1.0f;
+      // the saved g, u, h of kDhBatch fragments' columns at a time (one
+      // wait each); columns past f read column 0 and store nothing
       float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < FP; ++i) {
-        const int c = p0 + prow[i] + er;
-        if (!rowok || c >= f) continue;
-        const u32x2_t g2 = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + c);
-        const u32x2_t u2 = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + f + c);
-        const u32x2_t h2 = *reinterpret_cast<const u32x2_t *>(a.h + r * f + c);
-        float dg[4], du[4];
+      for (int hh = 0; hh < FP / kDhBatch; ++hh) {
+        constexpr int FH = kDhBatch;
+        u32x2_t g2[FH], u2[FH], h2[FH];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t gw = g2[v >> 1], uw = u2[v >> 1], hw = h2[v >> 1];
-          const float g = bf16_bits_to_f32((v & 1) ? (gw >> 16) : (gw & 0xffffu));
-          const float u = bf16_bits_to_f32((v & 1) ? (uw >> 16) : (uw & 0xffffu));
-          const float hv = bf16_bits_to_f32((v & 1) ? (hw >> 16) : (hw & 0xffffu));
-          const float sg = 1.0f / (1.0f + __expf(-g));
-          const float silu = g * sg;
-          const float gd = acc[i][j][v];
-          part += hv * gd;
-          const float dh = w * gd;
-          dg[v] = dh * u * sg * (1.0f + g * (1.0f - sg));
-          du[v] = dh * silu;
+        for (int ii = 0; ii < FH; ++ii) {
+          const int c = p0 + prow[hh * FH + ii] + er;
+          const int cc = c < f ? c : 0;
+          g2[ii] = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + cc);
+          u2[ii] = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + f + cc);
+          h2[ii] = *reinterpret_cast<const u32x2_t *>(a.h + r * f + cc);
         }
-        *reinterpret_cast<u32x2_t *>(a.o_dgu + r * f2 + c) =
-            u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-        *reinterpret_cast<u32x2_t *>(a.o_dgu + r * f2 + f + c) =
-            u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+#pragma unroll
+        for (int ii = 0; ii < FH; ++ii) {
+          const int i = hh * FH + ii;
+          const int c = p0 + prow[i] + er;
+          const bool ok = rowok && c < f;
+          float dg[4], du[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t gw = g2[ii][v >> 1], uw = u2[ii][v >> 1], hw = h2[ii][v >> 1];
+            const float g = bf16_bits_to_f32((v & 1) ? (gw >> 16) : (gw & 0xffffu));
+            const float u = bf16_bits_to_f32((v & 1) ? (uw >> 16) : (uw & 0xffffu));
+            const float hv = bf16_bits_to_f32((v & 1) ? (hw >> 16) : (hw & 0xffffu));
+            const float sg = 1.0f / (1.0f + __expf(-g));
+            const float silu = g * sg;
+            const float gd = acc[i][j][v];
+            part += ok ? hv * gd : 0.0f;
+            const float dh = w * gd;
+            dg[v] = dh * u * sg * (1.0f + g * (1.0f - sg));
+            du[v] = dh * silu;
+          }
+          if (ok) {
+            *reinterpret_cast<u32x2_t *>(a.o_dgu + r * f2 + c) =
+                u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+            *reinterpret_cast<u32x2_t *>(a.o_dgu + r * f2 + f + c) =
+                u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          }
+        }
       }
       // sum over the 4 lane groups that share this token (fixed order)
       part += __shfl_xor(part, 16, 64);
@@ -609,7 +634,10 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int FP = BP / WP / 16;
   constexpr int FQ = BQ / WQ / 16;
-  static_assert(FP >= 1 && FQ >= 1 && FQ <= FP, "fragment counts");
+  static_assert(FP >= 1 && FQ >= 1 && (FQ % FP == 0 || FP % FQ == 0), "fragment counts");
+  // interleaved stage: the new Q fragments are read QPR per P row in the
+  // first QROWS rows, the loads go out DPR per P row
+  constexpr int QPR = FQ > FP ? FQ / FP : 1, QROWS = FQ > FP ? FP : FQ;
   static_assert(!KT::PAIRED || (FP % 2 == 0), "paired tiles need an even fragment count");
   static_assert(BP % 128 == 0 && BQ % 128 == 0, "tiles are multiples of 128 rows");
   static_assert(BK == 32 || BK == 64, "stages of one or two 32-wide k steps");
@@ -619,7 +647,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;   // 16-byte slots: P part, stage
   static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
   static_assert(3 * LOADS < 64, "vmcnt range");
-  static_assert(LOADS <= FP, "one load per P-fragment row of the interleaved stage");
+  constexpr int DPR = (LOADS + FP - 1) / FP;
   constexpr int RP = KT::PT_ ? 2 : 1, RQ = KT::QT_ ? 2 : 1;  // LDS reads per fragment
 
   __shared__ u32x4_t smem[NS * SS];
@@ -820,22 +848,25 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   do {                                                                                        \
     const LDS_AS char *nb_ = lds + ((unsigned)(rs) % NS) * (SS * 16);                         \
     bf16x8_t qn_[FQ];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < FQ; ++i) {                                          \
+    _Pragma("unroll") for (int i = 0; i < QROWS; ++i) {                                       \
       _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                          \
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
       pf[i] = frag_at<KT::PT_, KT::PAIRED, BP, BK, FP>(nb_, rdP, i, (rh));                    \
-      qn_[i] = frag_at<KT::QT_, false, BQ, BK, FQ>(nb_, rdQ, i, (rh));                        \
+      _Pragma("unroll") for (int r = 0; r < QPR; ++r)                                         \
+          qn_[i * QPR + r] = frag_at<KT::QT_, false, BQ, BK, FQ>(nb_, rdQ, i * QPR + r, (rh)); \
       __builtin_amdgcn_sched_group_barrier(0x008, FQ, 0);                                     \
-      __builtin_amdgcn_sched_group_barrier(0x100, RP + RQ, 0);                                \
-      if ((LD) && i < LOADS) MOE_DMA(i);                                                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, RP + QPR * RQ, 0);                          \
+      if (LD) { _Pragma("unroll") for (int r = 0; r < DPR; ++r)                               \
+          if (i * DPR + r < LOADS) MOE_DMA(i * DPR + r); }                                    \
     }                                                                                         \
-    _Pragma("unroll") for (int i = FQ; i < FP; ++i) {                                         \
+    _Pragma("unroll") for (int i = QROWS; i < FP; ++i) {                                      \
       _Pragma("unroll") for (int j = 0; j < FQ; ++j)                                          \
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0); \
       pf[i] = frag_at<KT::PT_, KT::PAIRED, BP, BK, FP>(nb_, rdP, i, (rh));                    \
       __builtin_amdgcn_sched_group_barrier(0x008, FQ, 0);                                     \
       __builtin_amdgcn_sched_group_barrier(0x100, RP, 0);                                     \
-      if ((LD) && i < LOADS) MOE_DMA(i);                                                      \
+      if (LD) { _Pragma("unroll") for (int r = 0; r < DPR; ++r)                               \
+          if (i * DPR + r < LOADS) MOE_DMA(i * DPR + r); }                                    \
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < FQ; ++j) qf[j] = qn_[j];                            \
   } while (0)
@@ -1068,7 +1099,7 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
 // through 4 LDS buffers of 32 KB: three stages (96 KB) in flight.
 constexpr int FWD_BP = 256, FWD_BQ = 256, FWD_WP = 2, FWD_WQ = 4, FWD_NS = 2, FWD_BK = 64;  // FWD_GU
 constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 2, DN_BK = 64;  // FWD_DOWN, BWD_DX
-constexpr int DH_BP = 256, DH_BQ = 256, DH_WP = 2, DH_WQ = 4, DH_NS = 2, DH_BK = 64;  // BWD_DH
+constexpr int DH_BP = 256, DH_BQ = 256, DH_WP = 4, DH_WQ = 2, DH_NS = 2, DH_BK = 64;  // BWD_DH
 constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK = 32;  // weight grads
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
