@@ -1098,7 +1098,8 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
 // 256 x 256 tiles, 8 waves of 128 x 64 (two per SIMD), K in stages of 32
 // through 4 LDS buffers of 32 KB: three stages (96 KB) in flight.
 constexpr int FWD_BP = 256, FWD_BQ = 256, FWD_WP = 2, FWD_WQ = 4, FWD_NS = 2, FWD_BK = 64;  // FWD_GU
-constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 2, DN_BK = 64;  // FWD_DOWN, BWD_DX
+constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 2, DN_BK = 64;  // FWD_DOWN
+constexpr int DX_BP = 256, DX_BQ = 256, DX_WP = 2, DX_WQ = 4, DX_NS = 2, DX_BK = 64;  // BWD_DX
 constexpr int DH_BP = 256, DH_BQ = 256, DH_WP = 4, DH_WQ = 2, DH_NS = 2, DH_BK = 64;  // BWD_DH
 constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK = 32;  // weight grads
 
@@ -1304,7 +1305,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
     if (rc) return rc;
   }
   // 2. dX_perm = dGU . W_gu
-  rc = launch_token_gemm<BWD_DX, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK>(a, R, (d + DN_BP - 1) / DN_BP, ts1,
+  rc = launch_token_gemm<BWD_DX, DX_BP, DX_BQ, DX_WP, DX_WQ, DX_NS, DX_BK>(a, R, (d + DX_BP - 1) / DX_BP, ts1,
                                                              "gg_bwd_dx", s);
   if (rc) return rc;
   // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
