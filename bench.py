@@ -64,8 +64,9 @@ def measured_traffic(kernel, workload):
     return None if b is None else round(b["read"] + b["write"])
 
 
-def cpu_baseline(w, a, sample_tokens):
-    """Oracle fwd+bwd on the first `sample_tokens` tokens of the same inputs."""
+def cpu_baseline(w, a, sample_tokens, min_seconds=10.0):
+    """Oracle fwd+bwd on the first `sample_tokens` tokens of the same inputs,
+    repeated until at least `min_seconds` have passed."""
     import numpy as np
     from oracle import moe_oracle as O
     try:
@@ -73,17 +74,23 @@ def cpu_baseline(w, a, sample_tokens):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
+    sample_tokens = min(sample_tokens, w.T)
     s = slice(0, sample_tokens)
     x, dy = a["x"][s], a["dy"][s]
     noise = None if a["noise"] is None else a["noise"][s]
-    t0 = time.perf_counter()
-    o = O.layer_forward(x, a["w_r"], a["w_gu"], a["w_down"], w.k, a["bias"], noise, bf16=True)
-    O.layer_backward(o, x, a["w_r"], a["w_gu"], a["w_down"], dy, w.k, bf16=True)
-    dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores),
+    # whole fwd+bwd passes until at least min_seconds of CPU work
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        o = O.layer_forward(x, a["w_r"], a["w_gu"], a["w_down"], w.k, a["bias"], noise, bf16=True)
+        O.layer_backward(o, x, a["w_r"], a["w_gu"], a["w_down"], dy, w.k, bf16=True)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": passes * sample_tokens / dt, "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": "first %d of %d tokens of the same workload, one fwd+bwd, %.1f s" %
-                      (sample_tokens, w.T, dt)}
+            "sample": "first %d of %d tokens of the same workload, %d fwd+bwd pass(es), %.1f s" %
+                      (sample_tokens, w.T, passes, dt)}
 
 
 def main():
@@ -93,7 +100,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--profile-steps", type=int, default=5,
                     help="extra steps with per-kernel event timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
