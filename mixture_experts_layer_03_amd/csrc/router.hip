@@ -11,89 +11,88 @@ namespace moe {
 
 // ------------------------------------------------------------------ logits
 //
-// Block: 256 threads, tile = 16 tokens x EB experts (EB = 16*EPT).  Thread
-// (tok = tid%16, grp = tid/16) owns experts grp, grp+16, ...: EPT independent
-// chains.  Each (t,e) output is ONE fp32 fma chain over c = 0..d-1 in order,
-// then + bias, then + noise.  x and w_r tiles of 64 columns are staged in LDS
-// as fp32; the next tile's loads are issued before the current tile is used.
-constexpr int kLogitTok = 16;
-constexpr int kLogitCk = 64;
+// Each (t,e) output is ONE fp32 fma chain over c = 0..d-1 in order, then
+// + bias, then + noise, so the work per output cannot be split; there are
+// T*E chains of d dependent fmas.  Block: 256 threads = 8 tokens x 32
+// experts; wave w covers the block's 8 tokens x experts 8w..8w+7, lane l
+// token l/8 and expert l%8, one chain per lane (T=4096, E=32 gives two waves
+// per SIMD).  Operands come from LDS tiles of kLogitCk columns (fp32, rows
+// padded so that the 8 distinct rows one read touches fall on distinct
+// banks; the 8 lanes that share a row read it as a broadcast); the next
+// tile's global loads are in flight while the current one is used (widened
+// to fp32 only when staged).
+constexpr int kLogitTok = 8;     // tokens per block
+constexpr int kLogitExp = 32;    // experts per block
+constexpr int kLogitCk = 64;     // columns per LDS tile
 constexpr int kLogitPad = kLogitCk + 4;
 
-// 8 consecutive elements as fp32
-__device__ __forceinline__ void load8(const bf16_t *p, float *f) {
-  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+// 8 consecutive elements, raw
+struct Raw8 {
+  u32x4_t a, b;
+};
+__device__ __forceinline__ void load8_raw(const bf16_t *p, Raw8 &r) {
+  r.a = *reinterpret_cast<const u32x4_t *>(p);
+}
+__device__ __forceinline__ void load8_raw(const float *p, Raw8 &r) {
+  r.a = *reinterpret_cast<const u32x4_t *>(p);
+  r.b = *reinterpret_cast<const u32x4_t *>(p + 4);
+}
+template <typename T>
+__device__ __forceinline__ void widen8(const Raw8 &r, float *f) {
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_bits_to_f32(v[i] & 0xffffu);
-    f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_bits_to_f32(r.a[i] & 0xffffu);
+      f[2 * i + 1] = bf16_bits_to_f32(r.a[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(r.a[i]);
+      f[4 + i] = __uint_as_float(r.b[i]);
+    }
   }
 }
-__device__ __forceinline__ void load8(const float *p, float *f) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
 
-template <typename T, int EPT>
+template <typename T>
 __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
                                                        const T *__restrict__ wr,
                                                        const float *__restrict__ bias,
                                                        const float *__restrict__ noise,
                                                        int64_t ntok, int d, int E,
                                                        float *__restrict__ logits) {
-  constexpr int EB = 16 * EPT;
-  constexpr int XU = kLogitTok * (kLogitCk / 8);          // 8-element units in the x tile
-  constexpr int WU = EB * (kLogitCk / 8);                 // ... in the w tile
-  constexpr int WPT = (WU + 255) / 256;
+  constexpr int UPR = kLogitCk / 8;                // 8-element units per tile row
+  constexpr int XU = kLogitTok * UPR;              // units of the x tile: 64
+  constexpr int WU = kLogitExp * UPR;              // units of the w tile: 256
+  static_assert(WU == 256 && XU <= 256, "one w unit per thread");
   __shared__ __attribute__((aligned(16))) float xs[kLogitTok][kLogitPad];
-  __shared__ __attribute__((aligned(16))) float ws[EB][kLogitPad];
+  __shared__ __attribute__((aligned(16))) float ws[kLogitExp][kLogitPad];
   const int tid = threadIdx.x;
-  const int tok = tid & 15, grp = tid >> 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int tok = lane >> 3, el = wave * 8 + (lane & 7);
   const int64_t t0 = (int64_t)blockIdx.x * kLogitTok;
-  const int e0 = blockIdx.y * EB;
-  float acc[EPT];
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) acc[i] = 0.0f;
+  const int e0 = blockIdx.y * kLogitExp;
+  float acc = 0.0f;
 
-  float xr[8], wrg[WPT][8];
+  Raw8 xr, wrg;
+  const int row = tid / UPR, col8 = (tid % UPR) * 8;
   auto fetch = [&](int c0) {
-    if (tid < XU) {
-      const int r = tid >> 3, c = c0 + (tid & 7) * 8;
-      const int64_t t = t0 + r;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xr[i] = 0.0f;
-      if (t < ntok && c < d) load8(x + t * d + c, xr);
-    }
-#pragma unroll
-    for (int n = 0; n < WPT; ++n) {
-      const int u = tid + n * 256;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wrg[n][i] = 0.0f;
-      if (u < WU) {
-        const int r = u >> 3, c = c0 + (u & 7) * 8;
-        const int e = e0 + r;
-        if (e < E && c < d) load8(wr + (int64_t)e * d + c, wrg[n]);
-      }
-    }
+    xr.a = xr.b = wrg.a = wrg.b = u32x4_t{0u, 0u, 0u, 0u};
+    if (tid < XU && t0 + row < ntok && c0 + col8 < d) load8_raw(x + (t0 + row) * d + c0 + col8, xr);
+    if (e0 + row < E && c0 + col8 < d) load8_raw(wr + (int64_t)(e0 + row) * d + c0 + col8, wrg);
   };
   auto stage = [&]() {
+    float f[8];
     if (tid < XU) {
-      float *dst = &xs[tid >> 3][(tid & 7) * 8];
-      *reinterpret_cast<float4 *>(dst) = make_float4(xr[0], xr[1], xr[2], xr[3]);
-      *reinterpret_cast<float4 *>(dst + 4) = make_float4(xr[4], xr[5], xr[6], xr[7]);
+      widen8<T>(xr, f);
+      float *dst = &xs[row][col8];
+      *reinterpret_cast<float4 *>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4 *>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
     }
-#pragma unroll
-    for (int n = 0; n < WPT; ++n) {
-      const int u = tid + n * 256;
-      if (u < WU) {
-        float *dst = &ws[u >> 3][(u & 7) * 8];
-        *reinterpret_cast<float4 *>(dst) = make_float4(wrg[n][0], wrg[n][1], wrg[n][2], wrg[n][3]);
-        *reinterpret_cast<float4 *>(dst + 4) =
-            make_float4(wrg[n][4], wrg[n][5], wrg[n][6], wrg[n][7]);
-      }
-    }
+    widen8<T>(wrg, f);
+    float *dst = &ws[row][col8];
+    *reinterpret_cast<float4 *>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4 *>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
   };
 
   fetch(0);
@@ -102,30 +101,30 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
     __syncthreads();
     if (c0 + kLogitCk < d) fetch(c0 + kLogitCk);
     const int cn = min(kLogitCk, d - c0);   // a multiple of 8
-    for (int cc = 0; cc < cn; cc += 4) {
+    auto step = [&](int cc) {
       const float4 xv = *reinterpret_cast<const float4 *>(&xs[tok][cc]);
+      const float4 wv = *reinterpret_cast<const float4 *>(&ws[el][cc]);
+      acc = fmaf(xv.x, wv.x, acc);
+      acc = fmaf(xv.y, wv.y, acc);
+      acc = fmaf(xv.z, wv.z, acc);
+      acc = fmaf(xv.w, wv.w, acc);
+    };
+    if (cn == kLogitCk) {
+      // whole tile: unrolled, so the LDS reads run ahead of the fma chain
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const float4 wv = *reinterpret_cast<const float4 *>(&ws[grp + 16 * i][cc]);
-        acc[i] = fmaf(xv.x, wv.x, acc[i]);
-        acc[i] = fmaf(xv.y, wv.y, acc[i]);
-        acc[i] = fmaf(xv.z, wv.z, acc[i]);
-        acc[i] = fmaf(xv.w, wv.w, acc[i]);
-      }
+      for (int cc = 0; cc < kLogitCk; cc += 4) step(cc);
+    } else {
+      for (int cc = 0; cc < cn; cc += 4) step(cc);
     }
     __syncthreads();
   }
   const int64_t t = t0 + tok;
-  if (t >= ntok) return;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int e = e0 + grp + 16 * i;
-    if (e >= E) continue;
-    float v = acc[i];
-    if (bias) v = v + bias[e];
-    if (noise) v = v + noise[t * E + e];
-    logits[t * E + e] = v;
-  }
+  const int e = e0 + el;
+  if (t >= ntok || e >= E) return;
+  float v = acc;
+  if (bias) v = v + bias[e];
+  if (noise) v = v + noise[t * E + e];
+  logits[t * E + e] = v;
 }
 
 // ------------------------------------------------------------------ top-k
@@ -387,23 +386,15 @@ extern "C" int moe_router_logits(const void *x, const void *w_r, const float *bi
   MOE_REQUIRE(aligned16(x) && aligned16(w_r) && aligned16(logits), MOE_ERR_INVALID_ARG,
               "moe_router_logits: pointers must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  const int ept = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
-  const int eb = 16 * ept;
-  dim3 grid((unsigned)((T + kLogitTok - 1) / kLogitTok), (unsigned)((E + eb - 1) / eb));
-#define LOGITS_CASE(TY, EPTV)                                                                   \
-  MOE_LAUNCH("router_logits", s,                                                                \
-             k_router_logits<TY, EPTV><<<grid, 256, 0, s>>>((const TY *)x, (const TY *)w_r, bias, \
-                                                             logit_add, T, d, E, logits))
-  if (dtype == MOE_BF16) {
-    if (ept == 1) LOGITS_CASE(bf16_t, 1);
-    else if (ept == 2) LOGITS_CASE(bf16_t, 2);
-    else LOGITS_CASE(bf16_t, 4);
-  } else {
-    if (ept == 1) LOGITS_CASE(float, 1);
-    else if (ept == 2) LOGITS_CASE(float, 2);
-    else LOGITS_CASE(float, 4);
-  }
-#undef LOGITS_CASE
+  dim3 grid((unsigned)((T + kLogitTok - 1) / kLogitTok), (unsigned)((E + kLogitExp - 1) / kLogitExp));
+  if (dtype == MOE_BF16)
+    MOE_LAUNCH("router_logits", s,
+               k_router_logits<bf16_t><<<grid, 256, 0, s>>>((const bf16_t *)x, (const bf16_t *)w_r,
+                                                            bias, logit_add, T, d, E, logits));
+  else
+    MOE_LAUNCH("router_logits", s,
+               k_router_logits<float><<<grid, 256, 0, s>>>((const float *)x, (const float *)w_r, bias,
+                                                           logit_add, T, d, E, logits));
   return check_launch("moe_router_logits");
 }
 
