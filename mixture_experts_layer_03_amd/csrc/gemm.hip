@@ -983,17 +983,18 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
 #undef MOE_FETCH
 }
 
-// tile_start[e] = sum over e' < e of ceil(M_e' / BQ) * PT, and the 8 tile
-// counters that follow tile_start[E] cleared (one block)
+// For the two token GEMMs of a pass (P-tile counts PTa, PTb; same BQ):
+// ts[e] = sum over e' < e of ceil(M_e' / BQ) * PT, and the 8 tile counters
+// that follow ts[E] cleared (one block).
 __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict__ offsets, int E,
-                                                      int BQ, int PT,
-                                                      int32_t *__restrict__ tile_start) {
+                                                      int BQ, int PTa, int32_t *__restrict__ tsa,
+                                                      int PTb, int32_t *__restrict__ tsb) {
   __shared__ int s[1024];
   const int e = threadIdx.x;
   int v = 0;
   if (e < E) {
     const int m = offsets[e + 1] - offsets[e];
-    v = (m + BQ - 1) / BQ * PT;
+    v = (m + BQ - 1) / BQ;
   }
   s[e] = v;
   __syncthreads();
@@ -1003,9 +1004,12 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict_
     s[e] += t;
     __syncthreads();
   }
-  if (e < E) tile_start[e + 1] = s[e];
-  if (e == 0) tile_start[0] = 0;
-  if (e < 8) tile_start[E + 1 + e] = 0;   // the GEMM's per-XCD tile counters
+  if (e < E) {
+    tsa[e + 1] = s[e] * PTa;
+    tsb[e + 1] = s[e] * PTb;
+  }
+  if (e == 0) tsa[0] = tsb[0] = 0;
+  if (e < 8) tsa[E + 1 + e] = tsb[E + 1 + e] = 0;   // the GEMMs' per-XCD tile counters
 }
 
 // d_row_scale[r] = sum of its partials in fixed order
@@ -1013,8 +1017,19 @@ __global__ __launch_bounds__(256) void k_drs_reduce(const float *__restrict__ pa
                                                     int64_t R, float *__restrict__ drs) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= R) return;
+  const float *p = part + r * nparts;
   float s = 0.0f;
-  for (int i = 0; i < nparts; ++i) s += part[r * nparts + i];
+  int i = 0;
+  if (nparts % 4 == 0) {   // 16-byte loads (rows then start 16-byte aligned)
+    for (; i < nparts; i += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(p + i);
+      s += v.x;
+      s += v.y;
+      s += v.z;
+      s += v.w;
+    }
+  }
+  for (; i < nparts; ++i) s += p[i];
   drs[r] = s;
 }
 
@@ -1141,15 +1156,21 @@ static int persistent_grid(int64_t tiles) {
   return (int)(t < g ? t : g);
 }
 
+// tile starts and cleared counters of a pass's two token GEMMs (one launch)
+static int launch_tile_prefix(const GemmArgs &a, int BQ, int PTa, int32_t *tsa, int PTb,
+                              int32_t *tsb, hipStream_t s) {
+  MOE_LAUNCH("tile_prefix", s,
+             k_tile_prefix<<<1, 1024, 0, s>>>(a.offsets, a.E, BQ, PTa, tsa, PTb, tsb));
+  return check_launch("tile_prefix");
+}
+
 template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
 static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start, const char *name,
                              hipStream_t s) {
   if (R == 0) return MOE_OK;
   a.PT = PT;
-  a.tile_start = tile_start;
+  a.tile_start = tile_start;   // filled by launch_tile_prefix
   a.counters = tile_start + a.E + 1;
-  MOE_LAUNCH("tile_prefix", s,
-             k_tile_prefix<<<1, 1024, 0, s>>>(a.offsets, a.E, BQ, PT, tile_start));
   const int64_t bound = ((R + BQ - 1) / BQ + a.E) * (int64_t)PT;
   const int grid = persistent_grid(bound);
   MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK><<<grid, WP * WQ * 64, 0, s>>>(a)));
@@ -1243,11 +1264,15 @@ extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, i
   a.E = E;
   a.d = d;
   a.f = f;
+  static_assert(FWD_BQ == DN_BQ, "one tile prefix for both forward GEMMs");
+  const int pt_gu = (f + FWD_BP / 2 - 1) / (FWD_BP / 2), pt_dn = (d + DN_BP - 1) / DN_BP;
+  rc = launch_tile_prefix(a, FWD_BQ, pt_gu, ts0, pt_dn, ts1, s);
+  if (rc) return rc;
   rc = launch_token_gemm<FWD_GU, FWD_BP, FWD_BQ, FWD_WP, FWD_WQ, FWD_NS, FWD_BK>(
-      a, R, (f + FWD_BP / 2 - 1) / (FWD_BP / 2), ts0, "gg_fwd_gate_up_swiglu", s);
+      a, R, pt_gu, ts0, "gg_fwd_gate_up_swiglu", s);
   if (rc) return rc;
   return launch_token_gemm<FWD_DOWN, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK>(
-      a, R, (d + DN_BP - 1) / DN_BP, ts1, "gg_fwd_down_scale", s);
+      a, R, pt_dn, ts1, "gg_fwd_down_scale", s);
 }
 
 extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const void *h,
@@ -1292,7 +1317,12 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   a.E = E;
   a.d = d;
   a.f = f;
-  const int pt_dh = (f + DH_BP - 1) / DH_BP;
+  const int pt_dh = (f + DH_BP - 1) / DH_BP, pt_dx = (d + DX_BP - 1) / DX_BP;
+  static_assert(DH_BQ == DX_BQ, "one tile prefix for both token GEMMs of the backward");
+  if (R > 0) {
+    rc = launch_tile_prefix(a, DH_BQ, pt_dh, ts0, pt_dx, ts1, s);
+    if (rc) return rc;
+  }
   // 1. dGU (and d_row_scale partials) from dY_perm and W_down
   rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ, DH_NS, DH_BK>(a, R, pt_dh, ts0,
                                                              "gg_bwd_dh_dswiglu", s);
@@ -1305,7 +1335,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
     if (rc) return rc;
   }
   // 2. dX_perm = dGU . W_gu
-  rc = launch_token_gemm<BWD_DX, DX_BP, DX_BQ, DX_WP, DX_WQ, DX_NS, DX_BK>(a, R, (d + DX_BP - 1) / DX_BP, ts1,
+  rc = launch_token_gemm<BWD_DX, DX_BP, DX_BQ, DX_WP, DX_WQ, DX_NS, DX_BK>(a, R, pt_dx, ts1,
                                                              "gg_bwd_dx", s);
   if (rc) return rc;
   // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]

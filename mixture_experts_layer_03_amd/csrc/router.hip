@@ -247,44 +247,38 @@ __global__ __launch_bounds__(256) void k_route_bwd(const int32_t *__restrict__ t
 //
 // dx_router[t,:] = sum_e d_logits[t,e] * w_r[e,:] (e ascending, fp32 fma;
 // terms with d_logits == 0 are skipped, they add exact zeros).  One block per
-// token, each thread owns column pairs.
+// token, each thread owns runs of 8 columns (16-byte loads and stores).
 template <typename T>
 __global__ __launch_bounds__(256) void k_router_dx(const float *__restrict__ d_logits,
                                                    const T *__restrict__ wr, int64_t ntok, int d,
                                                    int E, float *__restrict__ dx) {
   const int64_t t = blockIdx.x;
   const float *dl = d_logits + t * E;
-  constexpr int kMaxPairs = 8;   // d <= 256*2*8 = 4096 per pass
-  for (int cbase = 0; cbase < d; cbase += 256 * 2 * kMaxPairs) {
-    float acc[kMaxPairs][2];
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8];
 #pragma unroll
-    for (int i = 0; i < kMaxPairs; ++i) acc[i][0] = acc[i][1] = 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     for (int e = 0; e < E; ++e) {
       const float a = dl[e];
       if (a == 0.0f) continue;
-      const T *row = wr + (int64_t)e * d;
+      Raw8 r;
+      load8_raw(wr + (int64_t)e * d + c, r);
+      float w[8];
+      widen8<T>(r, w);
 #pragma unroll
-      for (int i = 0; i < kMaxPairs; ++i) {
-        const int c = cbase + (i * 256 + threadIdx.x) * 2;
-        if (c < d) {
-          acc[i][0] = fmaf(a, Store<T>::load(row + c), acc[i][0]);
-          acc[i][1] = fmaf(a, Store<T>::load(row + c + 1), acc[i][1]);
-        }
-      }
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(a, w[i], acc[i]);
     }
-#pragma unroll
-    for (int i = 0; i < kMaxPairs; ++i) {
-      const int c = cbase + (i * 256 + threadIdx.x) * 2;
-      if (c < d) *reinterpret_cast<float2 *>(dx + t * d + c) = make_float2(acc[i][0], acc[i][1]);
-    }
+    float4 *out = reinterpret_cast<float4 *>(dx + t * d + c);
+    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
-// dw_r partials: block (e, column tile of 512, token chunk of 1024).  The
+// dw_r partials: block (e, column tile of 2048, token chunk of 256).  The
 // nonzero entries of d_logits[:,e] inside the chunk are found with a ballot
-// and visited in token order.
-constexpr int kDwTokChunk = 1024;
-constexpr int kDwCols = 512;
+// and visited in token order; each thread owns 8 consecutive columns.
+constexpr int kDwTokChunk = 256;
+constexpr int kDwCols = 2048;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_router_dw_partial(const float *__restrict__ d_logits,
@@ -293,26 +287,27 @@ __global__ __launch_bounds__(256) void k_router_dw_partial(const float *__restri
                                                            float *__restrict__ partial) {
   const int e = blockIdx.z;
   const int chunk = blockIdx.y;
-  const int c = blockIdx.x * kDwCols + threadIdx.x * 2;
+  const int c = blockIdx.x * kDwCols + threadIdx.x * 8;
   const int64_t tbeg = (int64_t)chunk * kDwTokChunk;
   __shared__ int s_tok[kDwTokChunk];
   __shared__ float s_val[kDwTokChunk];
   __shared__ int s_cnt[4];
   // compact the nonzero entries of this chunk, keeping token order
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int nz[4];
-  float vals[4];
+  constexpr int NI = kDwTokChunk / 256;   // 64-token groups per wave
+  int nz[NI];
+  float vals[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {   // wave w scans tokens [w*256, w*256+256)
-    const int64_t t = tbeg + wave * 256 + i * 64 + lane;
+  for (int i = 0; i < NI; ++i) {   // wave w scans tokens [w*64*NI, (w+1)*64*NI)
+    const int64_t t = tbeg + wave * 64 * NI + i * 64 + lane;
     const float v = (t < ntok) ? d_logits[t * E + e] : 0.0f;
     vals[i] = v;
     nz[i] = v != 0.0f;
   }
   int wave_tot = 0;
-  int pos[4];
+  int pos[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const uint64_t m = __ballot(nz[i]);
     pos[i] = wave_tot + __popcll(m & ((1ull << lane) - 1ull));
     wave_tot += __popcll(m);
@@ -323,23 +318,30 @@ __global__ __launch_bounds__(256) void k_router_dw_partial(const float *__restri
   for (int w = 0; w < wave; ++w) wbase += s_cnt[w];
   const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     if (nz[i]) {
-      s_tok[wbase + pos[i]] = (int)(wave * 256 + i * 64 + lane);
+      s_tok[wbase + pos[i]] = (int)(wave * 64 * NI + i * 64 + lane);
       s_val[wbase + pos[i]] = vals[i];
     }
   }
   __syncthreads();
-  float a0 = 0.0f, a1 = 0.0f;
   if (c < d) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     for (int n = 0; n < total; ++n) {
       const int64_t t = tbeg + s_tok[n];
       const float a = s_val[n];
-      a0 = fmaf(a, Store<T>::load(x + t * d + c), a0);
-      a1 = fmaf(a, Store<T>::load(x + t * d + c + 1), a1);
+      Raw8 r;
+      load8_raw(x + t * d + c, r);
+      float xv[8];
+      widen8<T>(r, xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(a, xv[i], acc[i]);
     }
-    float *out = partial + ((int64_t)e * gridDim.y + chunk) * d + c;
-    *reinterpret_cast<float2 *>(out) = make_float2(a0, a1);
+    float4 *out = reinterpret_cast<float4 *>(partial + ((int64_t)e * gridDim.y + chunk) * d + c);
+    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
