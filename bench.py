@@ -11,9 +11,10 @@ router backward -> permute backward.  Inputs are resident in HBM before the
 timed region starts.
 
 Prints one JSON line.  Besides throughput it reports the dominant kernel's
-roofline (algorithmic FLOPs per launch / its average launch time, measured with
-HIP events on the stream the kernel runs on) and the CPU oracle's throughput on
-a bounded sample of the same workload.
+roofline (its algorithmic FLOPs or HBM bytes per launch, whichever bounds it
+at peak, over its average launch time measured with HIP events on the stream
+the kernel runs on) and the CPU oracle's throughput on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -42,6 +43,21 @@ def gemm_flops(R, d, f):
         "gg_bwd_dx": 4.0 * R * d * f,
         "gg_bwd_dw_down": 2.0 * R * d * f,
         "gg_bwd_dw_gate_up": 4.0 * R * d * f,
+    }
+
+
+def gemm_bytes(R, d, f, E):
+    """Algorithmic HBM bytes of each grouped GEMM launch: every operand read
+    once and every output written once (bf16 activations and weights, fp32
+    weight gradients and combine weights)."""
+    b = 2.0
+    return {
+        "gg_fwd_gate_up_swiglu": b * (R * d + E * 2 * f * d + R * 2 * f + R * f),
+        "gg_fwd_down_scale": b * (R * f + E * d * f + R * d) + 4.0 * R,
+        "gg_bwd_dh_dswiglu": b * (R * d + E * d * f + R * 2 * f + R * f + R * 2 * f) + 4.0 * R,
+        "gg_bwd_dx": b * (R * 2 * f + E * 2 * f * d + R * d),
+        "gg_bwd_dw_down": b * (R * f + R * d) + 4.0 * E * d * f,
+        "gg_bwd_dw_gate_up": b * (R * d + R * 2 * f) + 4.0 * E * 2 * f * d,
     }
 
 
@@ -189,21 +205,40 @@ def main():
 
     R = w.R
     flops = gemm_flops(R, w.d, w.f)
+    nbytes = gemm_bytes(R, w.d, w.f, w.E)
     gemm_us = {n: kernels[n]["avg_us"] for n in flops if n in kernels}
     roofline = None
     gemm_frac = None
+    gemm_roof_frac = None
     if gemm_us:
+        # a GEMM's roofline time is the larger of its MFMA time and its HBM
+        # time at peak; the bound is whichever that is
+        t_mfma = {n: flops[n] / (PEAK_BF16_TFLOPS * 1e12) for n in gemm_us}
+        t_hbm = {n: nbytes[n] / (PEAK_HBM_GBS * 1e9) for n in gemm_us}
         dom = max(gemm_us, key=gemm_us.get)
-        achieved = flops[dom] / (gemm_us[dom] * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic(dom, w.name),
-                    "avg_launch_us": round(gemm_us[dom], 1),
-                    "algorithmic_flop_per_launch": flops[dom]}
+        t = gemm_us[dom] * 1e-6
+        if t_hbm[dom] > t_mfma[dom]:
+            achieved = nbytes[dom] / t / 1e9
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic(dom, w.name),
+                        "avg_launch_us": round(gemm_us[dom], 1),
+                        "algorithmic_bytes_per_launch": nbytes[dom],
+                        "algorithmic_flop_per_launch": flops[dom]}
+        else:
+            achieved = flops[dom] / t / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": measured_traffic(dom, w.name),
+                        "avg_launch_us": round(gemm_us[dom], 1),
+                        "algorithmic_flop_per_launch": flops[dom],
+                        "algorithmic_bytes_per_launch": nbytes[dom]}
         tot_f = sum(flops[n] for n in gemm_us)
         tot_t = sum(gemm_us[n] for n in gemm_us) * 1e-6
         gemm_frac = tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS
+        gemm_roof_frac = sum(max(t_mfma[n], t_hbm[n]) for n in gemm_us) / tot_t
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,6 +261,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.d, "experts": w.E,
                    "top_k": w.k, "d_ff": w.f, "routed_rows": R, "passes": "fwd+bwd"},
         "grouped_gemm_frac_of_bf16_peak": None if gemm_frac is None else round(gemm_frac, 4),
+        "grouped_gemm_roofline_frac": None if gemm_roof_frac is None else round(gemm_roof_frac, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
