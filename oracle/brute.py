@@ -13,6 +13,11 @@ them shares code with ``moe_oracle``:
     for the backward pass.
   * ``logits_exact``: the router logit fma chain evaluated with exact rational
     arithmetic and one correct rounding to fp32 per step.
+  * ``route_biased_by_scan``: selection on exactly rounded fp32 scores L + b,
+    weights from the full softmax of the unbiased logits, masked to the
+    selection and renormalised.
+  * ``aux_loss_by_loops``: expert load and mean router probability counted
+    token by token in Python, combined into the auxiliary loss.
 """
 from __future__ import annotations
 
@@ -148,3 +153,48 @@ def logits_exact(x, w_r, bias=None, noise=None):
                 acc = _round_fraction_to_f32(Fraction(acc) + Fraction(float(noise[t, e])))
             out[t, e] = acc
     return out
+
+
+def route_biased_by_scan(L, b, k):
+    """Selection by the scores fp32(L + b) (each add exact, then rounded once),
+    weights from the fp64 full softmax of L renormalised over the selection."""
+    L = np.asarray(L, np.float32)
+    T, E = L.shape
+    idx = np.zeros((T, k), np.int64)
+    w = np.zeros((T, k))
+    for t in range(T):
+        score = [_round_fraction_to_f32(Fraction(float(L[t, e])) + Fraction(float(b[e])))
+                 for e in range(E)]
+        sel = topk_by_scan(score, k)
+        m = max(float(v) for v in L[t])
+        p = [math.exp(float(v) - m) for v in L[t]]
+        z = sum(p)
+        p = [v / z for v in p]
+        ps = sum(p[e] for e in sel)
+        idx[t] = sel
+        w[t] = [p[e] / ps for e in sel]
+    return idx, w
+
+
+def aux_loss_by_loops(L, topk_idx, n_valid, k, coeff):
+    """aux = E * sum_e (load_e / (n k)) * (mean_t p[t,e]) over the first n_valid
+    tokens, by explicit loops; returns (aux, coeff * aux, load)."""
+    L = np.asarray(L, np.float64)
+    T, E = L.shape
+    load = [0] * E
+    psum = [0.0] * E
+    for t in range(int(n_valid)):
+        for j in range(k):
+            load[int(topk_idx[t][j])] += 1
+        m = max(L[t])
+        ex = [math.exp(L[t, e] - m) for e in range(E)]
+        z = sum(ex)
+        for e in range(E):
+            psum[e] += ex[e] / z
+    if n_valid == 0:
+        return 0.0, 0.0, load
+    aux = 0.0
+    for e in range(E):
+        aux += (load[e] / (n_valid * k)) * (psum[e] / n_valid)
+    aux *= E
+    return aux, coeff * aux, load

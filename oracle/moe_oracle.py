@@ -317,15 +317,103 @@ def router_logits_bwd(x, w_r, d_logits):
 
 
 # ---------------------------------------------------------------------------
+# router variants: selection-only bias, its balancing update, the
+# load-balancing auxiliary loss, and statistics over a valid token prefix
+# ---------------------------------------------------------------------------
+#
+# The pages name these features without formulas: LFM2's recipe sets
+# ``moe_balancing: bias_update`` because that family has no router auxiliary
+# loss, so balance is kept through a bias on expert *selection* ("Halo:
+# Frontier-Lab Training for Everyone", the LFM2 cookbook config and the
+# paragraph after it); other models train with a router auxiliary loss whose
+# coefficient is set per run, the routers applying its gradient and reporting
+# the unscaled and scaled values (same page, ms-swift DPO integration); and
+# right-padded tails are excluded from MoE statistics, the valid prefix being
+# described by the packed-sequence metadata (same page, sequence-parallel
+# input contract).  The plainest readings, used here:
+#   * selection score s[t,e] = fp32(L[t,e] + b_sel[e]) picks the k experts
+#     (same order and tie rule as ``route``); the weights are the softmax of
+#     the k selected *unbiased* logits, so the bias steers selection only;
+#   * load_e = number of (t, j) with t < n_valid and topk_idx[t,j] = e;
+#   * bias update: b_e += rate * sign(mean_load - load_e), mean_load =
+#     n_valid * k / E (the sign decided exactly in integers);
+#   * aux = E * sum_e f_e * P_e with f_e = load_e / (n_valid * k) and
+#     P_e = mean over t < n_valid of softmax(L[t,:])_e (all E experts);
+#     aux_scaled = coeff * aux; the gradient flows through P only (load is a
+#     count), and padded tokens t >= n_valid get none.  Balanced routing with
+#     uniform probabilities gives aux = 1.
+
+def route_biased(logits, sel_bias, k: int):
+    """Top-k by the fp32 selection score L + b_sel (value descending, ties to the
+    lower expert id); weights = softmax over the k selected unbiased logits.
+    Returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    L = np.asarray(logits, dtype=np.float32)
+    if sel_bias is None:
+        score = L
+    else:
+        score = L + np.asarray(sel_bias, dtype=np.float32)[None, :]   # one fp32 add
+    idx = np.argsort(-score, axis=1, kind="stable")[:, :k].astype(np.int32)
+    sel = _f64(np.take_along_axis(L, idx, axis=1))
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    w = ex / ex.sum(axis=1, keepdims=True)
+    return idx, w.astype(np.float32)
+
+
+def expert_load(topk_idx, E: int, n_valid: Optional[int] = None) -> np.ndarray:
+    """load[e] = selections of expert e by the tokens t < n_valid (int32 [E])."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    n = idx.shape[0] if n_valid is None else int(n_valid)
+    return np.bincount(idx[:n].ravel(), minlength=E).astype(np.int32)
+
+
+def bias_update(sel_bias, load, n_valid: int, k: int, rate: float) -> np.ndarray:
+    """b_e + rate * sign(n_valid*k/E - load_e), in fp32 (one add per expert)."""
+    b = np.asarray(sel_bias, dtype=np.float32)
+    ld = np.asarray(load, dtype=np.int64)
+    E = b.shape[0]
+    sgn = np.sign(int(n_valid) * int(k) - E * ld)          # exact integer comparison
+    step = np.where(sgn > 0, np.float32(rate), np.where(sgn < 0, np.float32(-rate),
+                                                        np.float32(0.0))).astype(np.float32)
+    return (b + step).astype(np.float32)
+
+
+def aux_loss(logits, load, n_valid: int, k: int, coeff: float):
+    """Load-balancing auxiliary loss and its gradient w.r.t. the logits.
+    Returns (aux, aux_scaled, d_logits fp32 [T,E]); d_logits is zero on the
+    padded tail and everywhere when n_valid = 0."""
+    L = _f64(logits)
+    T, E = L.shape
+    n = int(n_valid)
+    dl = np.zeros((T, E), np.float64)
+    if n == 0:
+        return 0.0, 0.0, dl.astype(np.float32)
+    Lv = L[:n]
+    p = np.exp(Lv - Lv.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)                 # softmax over all experts
+    P = p.mean(axis=0)
+    f = _f64(load) / (n * k)
+    aux = E * float(np.sum(f * P))
+    # d(coeff*aux)/dP_e = coeff*E*f_e;  dP_e/dp[t,e] = 1/n;  softmax Jacobian.
+    g = coeff * E * f / n
+    s = np.sum(p * g[None, :], axis=1, keepdims=True)
+    dl[:n] = p * (g[None, :] - s)
+    return aux, coeff * aux, dl.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
 # whole block
 # ---------------------------------------------------------------------------
 
-def layer_forward(x, w_r, w_gu, w_down, k: int, bias=None, noise=None, bf16=True) -> Dict:
+def layer_forward(x, w_r, w_gu, w_down, k: int, bias=None, noise=None, bf16=True,
+                  sel_bias=None) -> Dict:
     T = x.shape[0]
     E = w_r.shape[0]
     o: Dict[str, np.ndarray] = {}
     o["logits"] = router_logits(x, w_r, bias, noise)
-    o["topk_idx"], o["topk_w"] = route(o["logits"], k)
+    if sel_bias is None:
+        o["topk_idx"], o["topk_w"] = route(o["logits"], k)
+    else:
+        o["topk_idx"], o["topk_w"] = route_biased(o["logits"], sel_bias, k)
     o["counts"], o["offsets"], o["slot_to_row"], o["row_to_slot"] = permute_maps(o["topk_idx"], E)
     o["x_perm"], o["w_perm"] = permute_rows(x, o["topk_w"], o["row_to_slot"], k)
     o["gu"], o["h"], o["y_perm"] = expert_ffn_fwd(o["x_perm"], o["offsets"], w_gu, w_down,
@@ -334,7 +422,10 @@ def layer_forward(x, w_r, w_gu, w_down, k: int, bias=None, noise=None, bf16=True
     return o
 
 
-def layer_backward(fwd: Dict, x, w_r, w_gu, w_down, dy, k: int, bf16=True) -> Dict:
+def layer_backward(fwd: Dict, x, w_r, w_gu, w_down, dy, k: int, bf16=True,
+                   aux_coeff: float = 0.0, n_valid: Optional[int] = None) -> Dict:
+    """With aux_coeff != 0 the auxiliary-loss gradient (statistics over the
+    first n_valid tokens, all tokens if None) is added to d_logits."""
     T = x.shape[0]
     E = w_r.shape[0]
     b: Dict[str, np.ndarray] = {}
@@ -343,6 +434,11 @@ def layer_backward(fwd: Dict, x, w_r, w_gu, w_down, dy, k: int, bf16=True) -> Di
                             fwd["w_perm"], b["dy_perm"], bf16))
     b["d_topk_w"], b["d_logits"] = route_bwd(fwd["topk_idx"], fwd["topk_w"], b["d_row_scale"],
                                              fwd["slot_to_row"], E)
+    if aux_coeff != 0.0:
+        n = T if n_valid is None else int(n_valid)
+        b["load"] = expert_load(fwd["topk_idx"], E, n)
+        b["aux"], b["aux_scaled"], g = aux_loss(fwd["logits"], b["load"], n, k, aux_coeff)
+        b["d_logits"] = (_f64(b["d_logits"]) + _f64(g)).astype(np.float32)
     b["dx_router"], b["dw_r"] = router_logits_bwd(x, w_r, b["d_logits"])
     b["dx"] = permute_bwd(b["dx_perm"], fwd["slot_to_row"], T, k, b["dx_router"], bf16)
     return b

@@ -29,8 +29,9 @@ MUTATIONS = [
      'row_to_slot = np.lexsort((-np.arange(flat.size), flat))'),
     ("ties resolved to the higher id", 'idx = np.argsort(-L, axis=1, kind="stable")[:, :k]',
      'idx = (L.shape[1] - 1 - np.argsort(-L[:, ::-1], axis=1, kind="stable"))[:, :k]'),
-    ("softmax over all experts, not renormalised", "w = ex / ex.sum(axis=1, keepdims=True)",
-     "w = ex / np.exp(L.astype(np.float64) - sel[:, :1]).sum(axis=1, keepdims=True)"),
+    ("softmax over all experts, not renormalised",
+     "sel[:, :1])\n    w = ex / ex.sum(axis=1, keepdims=True)",
+     "sel[:, :1])\n    w = ex / np.exp(L.astype(np.float64) - sel[:, :1]).sum(axis=1, keepdims=True)"),
     ("H not rounded to bf16", "h = store(silu(gu[:, :f]) * _f64(gu[:, f:]), bf16)",
      "h = np.asarray(silu(gu[:, :f]) * _f64(gu[:, f:]), np.float32)"),
     ("gate and up halves swapped", "h = store(silu(gu[:, :f]) * _f64(gu[:, f:]), bf16)",
@@ -38,6 +39,16 @@ MUTATIONS = [
     ("router weight gradient scaled", "return (dl @ _f64(w_r)).astype(np.float32), (dl.T @ _f64(x))",
      "return (dl @ _f64(w_r)).astype(np.float32), (dl.T @ _f64(x) * 0.5)"),
     ("router gradient not added to dX", "acc += _f64(dx_add)", "pass"),
+    ("selection bias leaks into the weights", "sel = _f64(np.take_along_axis(L, idx, axis=1))\n    ex = np.exp(sel - sel.max(",
+     "sel = _f64(np.take_along_axis(score, idx, axis=1))\n    ex = np.exp(sel - sel.max("),
+    ("selection bias ignored", "score = L + np.asarray(sel_bias, dtype=np.float32)[None, :]", "score = L"),
+    ("bias update with the sign flipped", "np.sign(int(n_valid) * int(k) - E * ld)",
+     "np.sign(E * ld - int(n_valid) * int(k))"),
+    ("padded tail counted in the load", "np.bincount(idx[:n].ravel(), minlength=E)",
+     "np.bincount(idx.ravel(), minlength=E)"),
+    ("aux load fraction over tokens, not slots", "f = _f64(load) / (n * k)", "f = _f64(load) / n"),
+    ("aux gradient without the softmax centring", "dl[:n] = p * (g[None, :] - s)", "dl[:n] = p * g[None, :]"),
+    ("aux gradient not scaled by the coefficient", "g = coeff * E * f / n", "g = E * f / n"),
 ]
 
 PIN_TESTS = [
@@ -50,6 +61,11 @@ PIN_TESTS = [
     lambda: P.test_backward_matches_torch_autograd_fp32((25, 8, 4, 4, 12)),
     lambda: P.test_backward_matches_torch_autograd_fp32((30, 16, 6, 2, 8)),
     lambda: P.test_backward_invariants(),
+    lambda: P.test_route_biased_closed_forms(),
+    lambda: P.test_route_biased_matches_scan_on_exact_scores(),
+    lambda: P.test_expert_load_by_loops_and_bias_update_closed_forms(),
+    lambda: P.test_aux_loss_closed_forms(),
+    lambda: P.test_aux_loss_matches_loops_and_finite_differences(),
 ]
 
 

@@ -327,3 +327,121 @@ def test_sampled_variants_agree_with_full_oracle():
         np.testing.assert_allclose(dg, b["dw_gu"][e][cols], rtol=1e-4, atol=1e-3)
         np.testing.assert_allclose(du, b["dw_gu"][e][16 + cols], rtol=1e-4, atol=1e-3)
         np.testing.assert_allclose(dd, b["dw_down"][e][:, cols], rtol=1e-4, atol=1e-3)
+
+
+# ---------------------------------------------------------------- router variants
+
+def _variants_golden():
+    with open(os.path.join(GOLDEN, "router_variants_closed_forms.json")) as fh:
+        return json.load(fh)
+
+
+def test_route_biased_closed_forms():
+    for c in _variants_golden()["route_biased"]:
+        L = np.array(c["logits"], np.float32)
+        idx, w = O.route_biased(L, np.array(c["sel_bias"], np.float32), c["k"])
+        assert idx.tolist() == c["topk_idx"], c["name"]
+        np.testing.assert_allclose(w, np.array(c["topk_w"], np.float32), rtol=0, atol=c["atol"],
+                                   err_msg=c["name"])
+
+
+def test_route_biased_matches_scan_on_exact_scores():
+    r = _rng(11)
+    for E, k in [(8, 2), (32, 4), (5, 5), (1, 1), (16, 3)]:
+        L = r.standard_normal((40, E)).astype(np.float32)
+        L[::5] = np.round(L[::5])                         # exact ties in the logits
+        b = (r.standard_normal(E) * 0.7).astype(np.float32)
+        b[::3] = np.round(b[::3])                         # and in the scores
+        idx, w = O.route_biased(L, b, k)
+        bidx, bw = brute.route_biased_by_scan(L, b, k)
+        np.testing.assert_array_equal(idx, bidx)
+        np.testing.assert_allclose(w, bw, rtol=0, atol=2e-7)
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -23)
+        # the zero bias is plain top-k, bit for bit
+        z_idx, z_w = O.route_biased(L, np.zeros(E, np.float32), k)
+        p_idx, p_w = O.route(L, k)
+        np.testing.assert_array_equal(z_idx, p_idx)
+        np.testing.assert_array_equal(z_w, p_w)
+    # a bias far above every logit gap forces its expert into every selection
+    L = r.standard_normal((64, 8)).astype(np.float32)
+    b = np.zeros(8, np.float32)
+    b[5] = 100.0
+    idx, _ = O.route_biased(L, b, 2)
+    assert np.all(idx[:, 0] == 5)
+
+
+def test_expert_load_by_loops_and_bias_update_closed_forms():
+    for c in _variants_golden()["bias_update"]:
+        idx = np.array(c["topk_idx"], np.int32)
+        E = len(c["sel_bias"])
+        load = O.expert_load(idx, E, c["n_valid"])
+        assert load.tolist() == c["load"], c["name"]
+        nb = O.bias_update(np.array(c["sel_bias"], np.float32), load, c["n_valid"], c["k"], c["rate"])
+        assert nb.dtype == np.float32
+        assert nb.tolist() == c["sel_bias_after"], c["name"]
+    r = _rng(12)
+    for E, k, T, n in [(8, 2, 50, 50), (32, 4, 64, 37), (6, 6, 9, 0), (128, 8, 40, 40)]:
+        idx = np.stack([r.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        load = O.expert_load(idx, E, n)
+        by_loop = [0] * E
+        for t in range(n):
+            for j in range(k):
+                by_loop[idx[t, j]] += 1
+        assert load.tolist() == by_loop
+        assert int(load.sum()) == n * k
+        b = (r.standard_normal(E)).astype(np.float32)
+        rate = 0.001
+        nb = O.bias_update(b, load, n, k, rate)
+        from fractions import Fraction
+        mean = Fraction(n * k, E)
+        for e in range(E):
+            want = b[e] + (np.float32(rate) if load[e] < mean else
+                           (-np.float32(rate) if load[e] > mean else np.float32(0.0)))
+            assert nb[e] == np.float32(want)
+
+
+def test_aux_loss_closed_forms():
+    for c in _variants_golden()["aux_loss"]:
+        L = np.array(c["logits"], np.float32)
+        if c["name"].startswith("two experts"):
+            L[0, 0] = np.float32(math.log(3.0))
+        idx = np.array(c["topk_idx"], np.int32)
+        E = L.shape[1]
+        load = O.expert_load(idx, E, c["n_valid"])
+        assert load.tolist() == c["load"], c["name"]
+        aux, scaled, dl = O.aux_loss(L, load, c["n_valid"], c["k"], c["coeff"])
+        tol = max(c["atol"], 1e-7)
+        assert abs(aux - c["aux"]) <= tol, (c["name"], aux)
+        assert abs(scaled - c["aux_scaled"]) <= tol, (c["name"], scaled)
+        np.testing.assert_allclose(dl, np.array(c["d_logits"], np.float64), rtol=0, atol=tol,
+                                   err_msg=c["name"])
+
+
+def test_aux_loss_matches_loops_and_finite_differences():
+    r = _rng(13)
+    for E, k, T, n, coeff in [(8, 2, 30, 30, 0.01), (6, 3, 25, 17, 1.5), (32, 4, 40, 40, 0.1)]:
+        L = (r.standard_normal((T, E)) * 1.5).astype(np.float32)
+        idx, _ = O.route(L, k)
+        load = O.expert_load(idx, E, n)
+        aux, scaled, dl = O.aux_loss(L, load, n, k, coeff)
+        baux, bscaled, bload = brute.aux_loss_by_loops(L, idx, n, k, coeff)
+        assert load.tolist() == bload
+        assert abs(aux - baux) <= 1e-12 * max(1.0, abs(baux))
+        assert abs(scaled - bscaled) <= 1e-12 * max(1.0, abs(bscaled))
+        # the gradient of coeff*aux w.r.t. the logits, with the load held fixed
+        h = 1e-6
+        Ld = L.astype(np.float64)
+        for t in list(range(0, T, 3)):
+            for e in range(E):
+                Lp, Lm = Ld.copy(), Ld.copy()
+                Lp[t, e] += h
+                Lm[t, e] -= h
+                fd = (O.aux_loss(Lp, load, n, k, coeff)[1] - O.aux_loss(Lm, load, n, k, coeff)[1]) / (2 * h)
+                assert abs(fd - dl[t, e]) <= 1e-7 * max(1.0, coeff), (t, e, fd, dl[t, e])
+        # softmax gradients sum to zero per token; the padded tail has none
+        assert np.all(np.abs(dl.astype(np.float64).sum(1)) <= 1e-7)
+        assert np.all(dl[n:] == 0)
+        # statistics over the valid prefix do not see the tail
+        aux2, _, dl2 = O.aux_loss(L[:n], load, n, k, coeff)
+        assert aux2 == aux
+        np.testing.assert_array_equal(dl2, dl[:n])
