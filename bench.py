@@ -194,6 +194,43 @@ def main():
             v["avg_us"] = 1e3 * v["ms_total"] / max(1, v["launches"])
         abi.moe_timing_reset()
 
+    # router variants (selection-only bias, load statistics, its balancing
+    # step, the auxiliary loss with its gradient) on the last step's logits;
+    # timed apart from the block step, which the workload runs without them
+    variants = {}
+    if args.profile_steps > 0:
+        sel_bias = torch.zeros(w.E, dtype=torch.float32, device=dev)
+        vb = {"route_topk_biased": w.T * w.E * 4 + w.E * 4 + w.R * 8,
+              "expert_load": w.R * 4 + w.E * 4, "bias_update": w.E * 12,
+              "aux_loss": w.T * w.E * 12 + w.E * 4}
+        def variant_calls():
+            abi.moe_route_biased(blk.logits, sel_bias, w.k, blk.topk_idx, blk.topk_w)
+            abi.moe_expert_load(blk.topk_idx, w.T, w.E, blk.load, blk.ws)
+            abi.moe_aux_loss(blk.logits, blk.load, w.T, w.k, 1e-3, blk.aux, blk.d_logits, blk.ws)
+            abi.moe_bias_update(blk.load, w.T, w.k, 1e-3, sel_bias)
+
+        for _ in range(2):              # first launches of these kernels: untimed
+            variant_calls()
+        torch.cuda.synchronize()
+        abi.moe_timing_reset()
+        abi.moe_timing_enable(True)
+        for _ in range(max(args.profile_steps, 10)):
+            variant_calls()
+        torch.cuda.synchronize()
+        abi.moe_timing_enable(False)
+        launches = {"route_topk_biased": ["route_topk_biased"],
+                    "expert_load": ["expert_load", "expert_load_reduce"],
+                    "bias_update": ["bias_update"], "aux_loss": ["aux_loss", "aux_loss_final"]}
+        for n in vb:
+            us = 0.0
+            for ln in launches[n]:
+                ms, cnt = abi.moe_timing_query(ln)
+                us += 1e3 * ms / max(1, cnt)
+            if us > 0:
+                variants[n] = {"avg_us_per_call": round(us, 2), "algorithmic_bytes": vb[n],
+                               "hbm_frac": round(vb[n] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        abi.moe_timing_reset()
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -265,6 +302,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
+        "router_variants": variants,
     }
     print(json.dumps(out), flush=True)
 

@@ -214,6 +214,76 @@ int moe_router_logits_bwd(const void *x, const void *w_r, const float *d_logits,
                           int64_t T, int d, int E, float *dx_router, float *dw_r,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- router variants */
+
+/*
+ * The pages name three router features without giving formulas ("Halo:
+ * Frontier-Lab Training for Everyone"): balancing through a bias on expert
+ * selection for a model family without a router auxiliary loss (the LFM2
+ * cookbook config, `moe_balancing: bias_update`, and the paragraph after it);
+ * a router load-balancing auxiliary loss with a per-run coefficient whose
+ * gradient the routers apply and whose unscaled and scaled values they report
+ * (ms-swift DPO integration); and MoE statistics that ignore the right-padded
+ * tail of a batch, the valid prefix being n_valid tokens (sequence-parallel
+ * input contract).  The formulas below are the plainest readings.
+ */
+
+/*
+ * Top-k on the selection score fp32(logits[t,e] + sel_bias[e]) (by value
+ * descending, equal scores to the lower expert id, as moe_route); topk_w[t,j]
+ * is the softmax over the k selected logits WITHOUT the bias, so the bias only
+ * steers which experts are chosen.  sel_bias: [E] fp32, not NULL (moe_route
+ * is the unbiased call).  Other arguments and errors as moe_route; moe_route_bwd
+ * is the adjoint with respect to the logits (the bias gets no gradient).
+ */
+int moe_route_biased(const float *logits, const float *sel_bias, int64_t T, int E, int k,
+                     int32_t *topk_idx, float *topk_w, void *stream);
+
+size_t moe_expert_load_workspace_size(int64_t T, int E, int k);
+
+/*
+ * Expert load over the valid prefix: load[e] = number of slots (t, j) with
+ * t < n_valid and topk_idx[t,j] = e (ids outside [0,E) are not counted).
+ * 0 <= n_valid <= T, else MOE_ERR_INVALID_ARG.  topk_idx: [T,k] int32;
+ * load: [E] int32 (out, fully written; all zero when n_valid = 0).  Exact and
+ * deterministic (per-block integer histograms summed in block order).
+ * ws: moe_expert_load_workspace_size(T,E,k) bytes.
+ */
+int moe_expert_load(const int32_t *topk_idx, int64_t T, int64_t n_valid, int E, int k,
+                    int32_t *load, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Selection-bias balancing step, in place:
+ *   sel_bias[e] += rate * sign(n_valid*k/E - load[e])
+ * (under-loaded experts are raised, over-loaded lowered, an expert exactly at
+ * the mean load is unchanged; the sign is decided exactly in integers; one fp32
+ * add per expert).  load from moe_expert_load with the same n_valid.  rate must
+ * be finite and >= 0.  load: [E] int32; sel_bias: [E] fp32 (in/out).
+ */
+int moe_bias_update(const int32_t *load, int64_t n_valid, int E, int k, float rate,
+                    float *sel_bias, void *stream);
+
+size_t moe_aux_loss_workspace_size(int64_t T, int E);
+
+/*
+ * Load-balancing auxiliary loss over the valid prefix (n = n_valid):
+ *   p[t,:] = softmax(logits[t,:]) over all E experts (fp32),
+ *   P_e = (1/n) sum_{t<n} p[t,e],  f_e = load[e] / (n k),
+ *   aux = E * sum_e f_e P_e  (= 1 for balanced load and uniform p),
+ *   aux_out[0] = aux, aux_out[1] = coeff * aux.
+ * If d_logits is not NULL the gradient of coeff*aux with respect to the logits
+ * is ADDED to it (the load is a count and carries none):
+ *   d_logits[t,e] += p[t,e] (g_e - sum_e' p[t,e'] g_e'),  g_e = coeff E load[e] / (n^2 k),
+ * for t < n; rows t >= n are not touched.  n = 0 writes aux_out = {0, 0} and
+ * touches nothing else.  logits: [T,E] fp32; load: [E] int32 from moe_expert_load
+ * with the same n_valid; aux_out: [2] fp32 (out); d_logits: [T,E] fp32 (in/out)
+ * or NULL; coeff must be finite.  Deterministic: per-block partial sums
+ * combined in a fixed order.  ws: moe_aux_loss_workspace_size(T,E) bytes.
+ */
+int moe_aux_loss(const float *logits, const int32_t *load, int64_t T, int64_t n_valid, int E,
+                 int k, float coeff, float *aux_out, float *d_logits, void *ws, size_t ws_bytes,
+                 void *stream);
+
 /* ---------------------------------------------------------------- timing */
 
 /*
@@ -226,7 +296,9 @@ int moe_router_logits_bwd(const void *x, const void *w_r, const float *d_logits,
  * permute_rows, tile_prefix, gg_fwd_gate_up_swiglu, gg_fwd_down_scale,
  * combine, combine_bwd, gg_bwd_dh_dswiglu, drs_reduce, gg_bwd_dx,
  * gg_bwd_dw_down, gg_bwd_dw_gate_up, route_bwd, router_dx, router_dw_partial,
- * router_dw_reduce, router_dw_zero, permute_bwd, ffn_gu_f32, ffn_down_f32.
+ * router_dw_reduce, router_dw_zero, permute_bwd, ffn_gu_f32, ffn_down_f32,
+ * route_topk_biased, expert_load, expert_load_reduce, bias_update, aux_loss,
+ * aux_loss_final.
  */
 int moe_timing_enable(int on);
 int moe_timing_reset(void);

@@ -51,6 +51,16 @@ _SIGS = {
     "moe_router_logits_bwd_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_router_logits_bwd": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32,
                                      _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_route_biased": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p,
+                                _c_void_p]),
+    "moe_expert_load_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_expert_load": (_i32, [_c_void_p, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p, _sz,
+                               _c_void_p]),
+    "moe_bias_update": (_i32, [_c_void_p, _i64, _i32, _i32, ctypes.c_float, _c_void_p,
+                               _c_void_p]),
+    "moe_aux_loss_workspace_size": (_sz, [_i64, _i32]),
+    "moe_aux_loss": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i32, _i32, ctypes.c_float,
+                            _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "moe_timing_enable": (_i32, [_i32]),
     "moe_timing_reset": (_i32, []),
     "moe_timing_query": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -196,6 +206,40 @@ def moe_router_logits_bwd(x, w_r, d_logits, dx_router, dw_r, ws, stream=None):
     E = w_r.shape[0]
     _check("moe_router_logits_bwd", lib().moe_router_logits_bwd(
         _p(x), _p(w_r), _p(d_logits), _dtype_code(x), T, d, E, _p(dx_router), _p(dw_r), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route_biased(logits, sel_bias, k, topk_idx, topk_w, stream=None):
+    T, E = logits.shape
+    _check("moe_route_biased", lib().moe_route_biased(_p(logits), _p(sel_bias), T, E, k,
+                                                      _p(topk_idx), _p(topk_w), _stream(stream)))
+
+
+def moe_expert_load_workspace_size(T, E, k) -> int:
+    return int(lib().moe_expert_load_workspace_size(T, E, k))
+
+
+def moe_expert_load(topk_idx, n_valid, E, load, ws, stream=None):
+    T, k = topk_idx.shape
+    _check("moe_expert_load", lib().moe_expert_load(
+        _p(topk_idx), T, n_valid, E, k, _p(load), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_bias_update(load, n_valid, k, rate, sel_bias, stream=None):
+    E = load.shape[0]
+    _check("moe_bias_update", lib().moe_bias_update(_p(load), n_valid, E, k, float(rate),
+                                                    _p(sel_bias), _stream(stream)))
+
+
+def moe_aux_loss_workspace_size(T, E) -> int:
+    return int(lib().moe_aux_loss_workspace_size(T, E))
+
+
+def moe_aux_loss(logits, load, n_valid, k, coeff, aux_out, d_logits, ws, stream=None):
+    T, E = logits.shape
+    _check("moe_aux_loss", lib().moe_aux_loss(
+        _p(logits), _p(load), T, n_valid, E, k, float(coeff), _p(aux_out), _p(d_logits), _p(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 

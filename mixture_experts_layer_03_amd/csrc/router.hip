@@ -140,8 +140,11 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// With a selection bias (nullable) the compared value is the fp32 sum
+// logit + sel_bias[e]; the softmax always takes the selected logits alone.
 template <int G>
-__global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int64_t ntok,
+__global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
+                                               const float *__restrict__ sel_bias, int64_t ntok,
                                                int E, int k, int32_t *__restrict__ topk_idx,
                                                float *__restrict__ topk_w) {
   const int lane = threadIdx.x & 63;
@@ -154,10 +157,12 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
 #pragma unroll
   for (int v = 0; v < kMaxPerLane; ++v) {
     const int e = s + v * G;
-    val[v] = (live && v < vpl && e < E) ? logits[t * E + e] : 0.0f;
-    if (!(v < vpl && e < E)) taken |= 1u << v;   // padding never wins
+    const bool ok = v < vpl && e < E;
+    val[v] = (live && ok) ? logits[t * E + e] : 0.0f;
+    if (sel_bias && ok) val[v] += sel_bias[e];
+    if (!ok) taken |= 1u << v;   // padding never wins
   }
-  float my_val = 0.0f, top0 = 0.0f;
+  float my_val = 0.0f;
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
     float bv = 0.0f;
@@ -181,14 +186,18 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
       }
     }
     if (bi % G == s) taken |= 1u << (bi / G);
-    if (j == 0) top0 = bv;
     if (s == j) {
       my_val = bv;
       my_idx = bi;
     }
   }
-  // softmax over the k selected values (max is the first selected)
-  float ex = (s < k) ? __expf(my_val - top0) : 0.0f;
+  // softmax over the k selected logits, shifted by their maximum (without a
+  // selection bias that is the first selected value)
+  if (sel_bias && live && s < k) my_val = logits[t * E + my_idx];
+  float mx = (s < k) ? my_val : -INFINITY;
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  float ex = (s < k) ? __expf(my_val - mx) : 0.0f;
   float sum = ex;
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) sum += __shfl_xor(sum, m, 64);
@@ -400,31 +409,45 @@ extern "C" int moe_router_logits(const void *x, const void *w_r, const float *bi
   return check_launch("moe_router_logits");
 }
 
-extern "C" int moe_route(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
-                         float *topk_w, void *stream) {
+static int route_impl(const float *logits, const float *sel_bias, int64_t T, int E, int k,
+                      int32_t *topk_idx, float *topk_w, void *stream, const char *fn) {
   clear_error();
-  int rc = check_common(T, E, "moe_route");
+  int rc = check_common(T, E, fn);
   if (rc) return rc;
-  MOE_REQUIRE(k >= 1 && k <= E && k <= kMaxTopK, MOE_ERR_UNSUPPORTED, "moe_route: k=%d E=%d", k,
-              E);
+  MOE_REQUIRE(k >= 1 && k <= E && k <= kMaxTopK, MOE_ERR_UNSUPPORTED, "%s: k=%d E=%d", fn, k, E);
   if (T == 0) return MOE_OK;
-  MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
   hipStream_t s = (hipStream_t)stream;
   int G = 1;
   while (G < E && G < 64) G <<= 1;
   const int64_t threads = T * G;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-#define ROUTE_CASE(GV)                                                                   \
-  case GV:                                                                               \
-    MOE_LAUNCH("route_topk", s,                                                          \
-               k_route<GV><<<blocks, 256, 0, s>>>(logits, T, E, k, topk_idx, topk_w)); \
+  const char *name = sel_bias ? "route_topk_biased" : "route_topk";
+#define ROUTE_CASE(GV)                                                                        \
+  case GV:                                                                                    \
+    MOE_LAUNCH(name, s,                                                                       \
+               k_route<GV><<<blocks, 256, 0, s>>>(logits, sel_bias, T, E, k, topk_idx, topk_w)); \
     break
   switch (G) {
     ROUTE_CASE(1); ROUTE_CASE(2); ROUTE_CASE(4); ROUTE_CASE(8);
     ROUTE_CASE(16); ROUTE_CASE(32); ROUTE_CASE(64);
   }
 #undef ROUTE_CASE
-  return check_launch("moe_route");
+  return check_launch(fn);
+}
+
+extern "C" int moe_route(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
+                         float *topk_w, void *stream) {
+  return route_impl(logits, nullptr, T, E, k, topk_idx, topk_w, stream, "moe_route");
+}
+
+extern "C" int moe_route_biased(const float *logits, const float *sel_bias, int64_t T, int E,
+                                int k, int32_t *topk_idx, float *topk_w, void *stream) {
+  if (!sel_bias && T > 0) {
+    clear_error();
+    MOE_REQUIRE(false, MOE_ERR_INVALID_ARG, "moe_route_biased: null sel_bias");
+  }
+  return route_impl(logits, sel_bias, T, E, k, topk_idx, topk_w, stream, "moe_route_biased");
 }
 
 extern "C" int moe_route_bwd(const int32_t *topk_idx, const float *topk_w,

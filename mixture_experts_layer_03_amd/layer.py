@@ -4,10 +4,12 @@
 and issues the library calls of the forward and backward passes in order, all
 on one stream, with no host synchronisation in between:
 
-  forward : moe_router_logits -> moe_route -> moe_permute ->
-            moe_grouped_ffn_fwd -> moe_combine
+  forward : moe_router_logits -> moe_route (moe_route_biased with a
+            selection bias) -> moe_permute -> moe_grouped_ffn_fwd -> moe_combine
   backward: moe_combine_bwd -> moe_grouped_ffn_bwd -> moe_route_bwd ->
-            moe_router_logits_bwd -> moe_permute_bwd
+            [moe_expert_load -> moe_aux_loss, with an auxiliary-loss
+            coefficient] -> moe_router_logits_bwd -> moe_permute_bwd
+  balance : moe_expert_load -> moe_bias_update (selection-bias step)
 
 This mirrors the EP forward path the pages describe (router logits in fp32,
 per-token top-k, tokens sorted by expert, grouped matmul, rows returned and
@@ -53,7 +55,12 @@ class MoEBlock:
         ws_perm = abi.moe_permute_workspace_size(T, E, k)
         ws_ffn = abi.moe_grouped_ffn_workspace_size(R, E, d, f, dc)
         ws_rtr = abi.moe_router_logits_bwd_workspace_size(T, d, E) if backward else 0
-        self.ws = torch.empty(max(ws_perm, ws_ffn, ws_rtr, 256), dtype=torch.uint8, device=device)
+        ws_stat = max(abi.moe_expert_load_workspace_size(T, E, k),
+                      abi.moe_aux_loss_workspace_size(T, E))
+        self.ws = torch.empty(max(ws_perm, ws_ffn, ws_rtr, ws_stat, 256), dtype=torch.uint8,
+                              device=device)
+        self.load = z(E, dt=i32)
+        self.aux = z(2, dt=f32)
         self.has_bwd = backward
         if backward:
             self.dy_perm = z(R, d)
@@ -69,9 +76,14 @@ class MoEBlock:
             self.dx = z(T, d)
 
     # ------------------------------------------------------------ forward
-    def forward(self, x, w_r, w_gu, w_down, bias=None, noise=None, stream=None):
+    def forward(self, x, w_r, w_gu, w_down, bias=None, noise=None, stream=None, sel_bias=None):
+        """bias is added to the logits (it moves selection and weights);
+        sel_bias only shifts the scores the top-k compares."""
         abi.moe_router_logits(x, w_r, bias, noise, self.logits, stream)
-        abi.moe_route(self.logits, self.k, self.topk_idx, self.topk_w, stream)
+        if sel_bias is None:
+            abi.moe_route(self.logits, self.k, self.topk_idx, self.topk_w, stream)
+        else:
+            abi.moe_route_biased(self.logits, sel_bias, self.k, self.topk_idx, self.topk_w, stream)
         self.permute(x, stream)
         self.experts_forward(w_gu, w_down, stream)
         abi.moe_combine(self.y_perm, self.slot_to_row, self.T, self.k, self.y, stream)
@@ -87,17 +99,35 @@ class MoEBlock:
                                 self.gu, self.h, self.y_perm, self.ws, stream)
 
     # ------------------------------------------------------------ backward
-    def backward(self, x, w_r, w_gu, w_down, dy, stream=None):
+    def backward(self, x, w_r, w_gu, w_down, dy, stream=None, aux_coeff: float = 0.0,
+                 n_valid: Optional[int] = None):
+        """aux_coeff != 0 adds the load-balancing auxiliary loss's gradient to
+        the router's; its statistics (and self.aux = [aux, aux_scaled]) cover
+        the first n_valid tokens (all if None)."""
         assert self.has_bwd
         abi.moe_combine_bwd(dy, self.slot_to_row, self.k, self.dy_perm, stream)
         self.experts_backward(w_gu, w_down, stream)
         abi.moe_route_bwd(self.topk_idx, self.topk_w, self.d_row_scale, self.slot_to_row,
                           self.E, self.d_topk_w, self.d_logits, stream)
+        if aux_coeff != 0.0:
+            n = self.T if n_valid is None else n_valid
+            abi.moe_expert_load(self.topk_idx, n, self.E, self.load, self.ws, stream)
+            abi.moe_aux_loss(self.logits, self.load, n, self.k, aux_coeff, self.aux,
+                             self.d_logits, self.ws, stream)
         abi.moe_router_logits_bwd(x, w_r, self.d_logits, self.dx_router, self.dw_r, self.ws,
                                   stream)
         abi.moe_permute_bwd(self.dx_perm, self.slot_to_row, self.dx_router, self.T, self.k,
                             self.dx, stream)
         return self.dx
+
+    def balance_selection_bias(self, sel_bias, rate: float, n_valid: Optional[int] = None,
+                               stream=None):
+        """One selection-bias balancing step from the last forward's routing:
+        self.load = per-expert load of the first n_valid tokens, then sel_bias
+        moves by rate toward the mean load (in place)."""
+        n = self.T if n_valid is None else n_valid
+        abi.moe_expert_load(self.topk_idx, n, self.E, self.load, self.ws, stream)
+        abi.moe_bias_update(self.load, n, self.k, rate, sel_bias, stream)
 
     def experts_backward(self, w_gu, w_down, stream=None):
         abi.moe_grouped_ffn_bwd(self.x_perm, self.gu, self.h, self.offsets, self.E, w_gu,

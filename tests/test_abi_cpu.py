@@ -82,6 +82,37 @@ def test_validation_rejects_before_launch():
     assert "T < 0" in abi.lib().moe_last_error().decode()
 
 
+def test_router_variant_validation_rejects_before_launch():
+    L = abi.lib()
+    F = ctypes.c_float
+    # selection bias is required by the biased call
+    assert L.moe_route_biased(P, None, 10, 4, 2, P, P, None) == -1
+    assert L.moe_route_biased(P, P, 10, 4, 5, P, P, None) == -2
+    assert L.moe_route_biased(None, None, 0, 4, 2, None, None, None) == 0
+    # valid prefix outside [0, T]
+    need = L.moe_expert_load_workspace_size(100, 8, 2)
+    assert need >= 8 * 4
+    rc, msg = _rc_msg(L.moe_expert_load(P, 100, 101, 8, 2, P, P, need, None))
+    assert rc == -1 and "n_valid" in msg, msg
+    assert L.moe_expert_load(P, 100, -1, 8, 2, P, P, need, None) == -1
+    assert L.moe_expert_load(P, 100, 50, 8, 9, P, P, need, None) == -2
+    assert L.moe_expert_load(P, 100, 100, 8, 2, None, P, need, None) == -1
+    assert L.moe_expert_load(P, 100000, 100000, 8, 2, P, P, need, None) == -3
+    # bias rate must be finite and non-negative
+    assert L.moe_bias_update(P, 10, 8, 2, F(-0.5), P, None) == -1
+    assert L.moe_bias_update(P, 10, 8, 2, F(float("nan")), P, None) == -1
+    assert L.moe_bias_update(P, 10, 8, 2, F(float("inf")), P, None) == -1
+    assert L.moe_bias_update(None, 10, 8, 2, F(0.1), P, None) == -1
+    # aux loss
+    wsz = L.moe_aux_loss_workspace_size(4096, 32)
+    assert wsz >= 32 * 4
+    assert L.moe_aux_loss(P, P, 100, 101, 8, 2, F(0.1), P, None, P, wsz, None) == -1
+    assert L.moe_aux_loss(P, P, 100, 100, 8, 2, F(0.1), None, None, P, wsz, None) == -1
+    assert L.moe_aux_loss(P, P, 100, 100, 8, 2, F(float("inf")), P, None, P, wsz, None) == -1
+    assert L.moe_aux_loss(P, P, 1 << 20, 1 << 20, 8, 2, F(0.1), P, None, P, 256, None) == -3
+    assert L.moe_aux_loss(P, P, 100, 100, 2000, 2, F(0.1), P, None, P, wsz, None) == -2
+
+
 def test_empty_inputs_are_ok_without_launch():
     L = abi.lib()
     assert L.moe_router_logits(None, None, None, None, 1, 0, 16, 4, None, None) == 0

@@ -1,0 +1,194 @@
+"""GPU parity of the router variants against the CPU oracle.
+
+Selection-only bias (moe_route_biased), expert load over a valid prefix
+(moe_expert_load), the selection-bias balancing step (moe_bias_update) and the
+load-balancing auxiliary loss with its gradient (moe_aux_loss), each through
+the C ABI, then the whole block with both variants on.
+
+Bit-exact: top-k indices (the scores are one fp32 add on both sides), the
+loads, the updated bias.  topk_w: the block's bound (max-abs 2e-2, rel-L2
+5e-3) and, as a sharper check of the fp32 softmax, max-abs 1e-5.  The
+auxiliary loss is an fp32 sum of fp32 softmax values on the GPU and fp64 in
+the oracle: relative error 1e-5 on aux and aux_scaled; its gradient within
+1e-5 of the largest gradient magnitude.
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_layer_03_amd import inputs as I
+from oracle import moe_oracle as O
+from tests.gpu_util import close, down, need_gpu, up, up_i32
+
+pytestmark = pytest.mark.gpu
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _logits(T, E, seed, ties=True):
+    r = _rng(seed)
+    L = (r.standard_normal((T, E)) * 2.0).astype(np.float32)
+    if ties:
+        L[::9] = np.round(L[::9])
+    return L
+
+
+def _sel_bias(E, seed, big=False):
+    r = _rng(seed + 7)
+    b = (r.standard_normal(E) * 0.5).astype(np.float32)
+    b[::4] = np.round(b[::4] * 2) / 2          # exact halves: score ties with rounded logits
+    if big:
+        b[E // 3] = 50.0                           # always selected
+        b[E // 2] = -50.0                          # never selected
+    return b
+
+
+ROUTE_CASES = [(1000, 8, 2), (777, 32, 4), (4096, 128, 8), (300, 5, 5), (64, 1, 1),
+               (200, 1000, 16), (513, 64, 32)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES, ids=["T%d-E%d-k%d" % c for c in ROUTE_CASES])
+def test_route_biased_matches_oracle(T, E, k):
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    dev = need_gpu()
+    print("GPU case route_biased", T, E, k, flush=True)
+    L = _logits(T, E, 100 + E)
+    b = _sel_bias(E, E, big=E >= 4)
+    gi = torch.empty(T, k, dtype=torch.int32, device=dev)
+    gw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    abi.moe_route_biased(up(L, False, dev), up(b, False, dev), k, gi, gw)
+    torch.cuda.synchronize()
+    idx, w = O.route_biased(L, b, k)
+    assert np.array_equal(down(gi), idx)
+    close("topk_w", down(gw), w)
+    assert np.max(np.abs(down(gw).astype(np.float64) - w)) <= 1e-5
+    # a zero selection bias reproduces the plain top-k bit for bit
+    pi = torch.empty_like(gi)
+    pw = torch.empty_like(gw)
+    abi.moe_route(up(L, False, dev), k, pi, pw)
+    abi.moe_route_biased(up(L, False, dev), torch.zeros(E, device=dev), k, gi, gw)
+    torch.cuda.synchronize()
+    assert torch.equal(pi, gi) and torch.equal(pw.view(torch.int32), gw.view(torch.int32))
+
+
+LOAD_CASES = [(1000, 8, 2, 1000), (1000, 8, 2, 613), (4096, 32, 4, 0), (32768, 128, 8, 32768),
+              (32768, 128, 8, 30001), (300, 1000, 16, 299), (5, 1, 1, 5)]
+
+
+def _topk_for(T, E, k, seed):
+    idx, _ = O.route(_logits(T, E, seed), k)
+    return idx
+
+
+@pytest.mark.parametrize("T,E,k,n", LOAD_CASES, ids=["T%d-E%d-k%d-n%d" % c for c in LOAD_CASES])
+def test_expert_load_and_bias_update_match_oracle(T, E, k, n):
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    dev = need_gpu()
+    print("GPU case expert_load", T, E, k, n, flush=True)
+    idx = _topk_for(T, E, k, 200 + E)
+    ws = torch.empty(abi.moe_expert_load_workspace_size(T, E, k), dtype=torch.uint8, device=dev)
+    load = torch.full((E,), -7, dtype=torch.int32, device=dev)
+    gidx = up_i32(idx, dev)
+    abi.moe_expert_load(gidx, n, E, load, ws)
+    b = _sel_bias(E, 3 * E)
+    gb = up(b, False, dev)
+    rate = 1e-3
+    abi.moe_bias_update(load, n, k, rate, gb)
+    torch.cuda.synchronize()
+    ref = O.expert_load(idx, E, n)
+    assert np.array_equal(down(load), ref)
+    nb = O.bias_update(b, ref, n, k, rate)
+    assert np.array_equal(down(gb).view(np.uint32), nb.view(np.uint32))
+
+
+AUX_CASES = [(1000, 8, 2, 1000, 0.01), (1000, 8, 2, 777, 0.5), (4096, 32, 4, 4096, 1e-3),
+             (4096, 32, 4, 4000, 2.0), (32768, 128, 8, 32768, 1e-2), (300, 1000, 16, 211, 1.0),
+             (257, 5, 5, 256, -0.25), (64, 1, 1, 64, 1.0), (100, 8, 2, 0, 1.0)]
+
+
+@pytest.mark.parametrize("T,E,k,n,coeff", AUX_CASES,
+                         ids=["T%d-E%d-k%d-n%d-c%g" % c for c in AUX_CASES])
+def test_aux_loss_matches_oracle(T, E, k, n, coeff):
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    dev = need_gpu()
+    print("GPU case aux_loss", T, E, k, n, coeff, flush=True)
+    L = _logits(T, E, 300 + E, ties=False)
+    idx = O.route(L, k)[0]
+    ref_load = O.expert_load(idx, E, n)
+    aux, scaled, dl = O.aux_loss(L, ref_load, n, k, coeff)
+    base = _rng(5).standard_normal((T, E)).astype(np.float32)   # gradient is added to this
+    g_dl = up(base, False, dev)
+    g_aux = torch.full((2,), float("nan"), device=dev)
+    ws = torch.empty(max(abi.moe_aux_loss_workspace_size(T, E),
+                         abi.moe_expert_load_workspace_size(T, E, k)), dtype=torch.uint8,
+                     device=dev)
+    load = torch.empty(E, dtype=torch.int32, device=dev)
+    abi.moe_expert_load(up_i32(idx, dev), n, E, load, ws)
+    abi.moe_aux_loss(up(L, False, dev), load, n, k, coeff, g_aux, g_dl, ws)
+    # value only (no gradient) gives the same numbers
+    g_aux2 = torch.full((2,), float("nan"), device=dev)
+    abi.moe_aux_loss(up(L, False, dev), load, n, k, coeff, g_aux2, None, ws)
+    torch.cuda.synchronize()
+    a = down(g_aux).astype(np.float64)
+    assert np.array_equal(down(g_aux), down(g_aux2))
+    if n == 0:
+        assert a[0] == 0.0 and a[1] == 0.0
+        assert np.array_equal(down(g_dl), base)
+        return
+    assert abs(a[0] - aux) <= 1e-5 * abs(aux), (a[0], aux)
+    assert abs(a[1] - scaled) <= 1e-5 * abs(scaled) + 1e-30, (a[1], scaled)
+    got = down(g_dl).astype(np.float64) - base.astype(np.float64)
+    scale = max(np.max(np.abs(dl)), 1e-30)
+    err = np.max(np.abs(got[:n] - dl[:n].astype(np.float64)))
+    print("aux grad max|ref| %.3e  max err %.3e" % (scale, err))
+    # the sum base + grad is rounded to fp32 once on the GPU
+    assert err <= 1e-5 * scale + 4 * np.finfo(np.float32).eps * np.max(np.abs(base))
+    assert np.array_equal(down(g_dl)[n:], base[n:])       # padded tail untouched
+
+
+def _layer_case(T, d, E, k, f, seed):
+    return I.Workload("variants-T%d-d%d-E%d-k%d-f%d" % (T, d, E, k, f), T, d, E, k, f, "bf16",
+                      True, "uniform", seed=seed)
+
+
+LAYER_CASES = [_layer_case(300, 328, 6, 2, 200, 21), _layer_case(512, 256, 16, 4, 384, 22)]
+
+
+@pytest.mark.parametrize("w", LAYER_CASES, ids=[w.name for w in LAYER_CASES])
+def test_block_with_selection_bias_and_aux_loss_matches_oracle(w):
+    import torch
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+    from tests.test_gpu_parity import check_backward, check_forward
+    dev = need_gpu()
+    print("GPU case", w.name, flush=True)
+    a = I.make_inputs(w)
+    b = _sel_bias(w.E, w.E, big=True)
+    n_valid = w.T - w.T // 7            # a right-padded tail
+    coeff = 0.05
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev)
+    x, wr, wgu, wd = (up(a[n], True, dev) for n in ("x", "w_r", "w_gu", "w_down"))
+    gb = up(b, False, dev)
+    blk.forward(x, wr, wgu, wd, sel_bias=gb)
+    blk.backward(x, wr, wgu, wd, up(a["dy"], True, dev), aux_coeff=coeff, n_valid=n_valid)
+    blk.balance_selection_bias(gb, 1e-3, n_valid=n_valid)
+    torch.cuda.synchronize()
+    g = {n: down(getattr(blk, n)) for n in (
+        "logits", "topk_idx", "topk_w", "counts", "offsets", "slot_to_row", "row_to_slot",
+        "x_perm", "w_perm", "gu", "h", "y_perm", "y", "dy_perm", "dgu", "dx_perm", "d_row_scale",
+        "d_topk_w", "d_logits", "dx_router", "dw_r", "dw_gu", "dw_down", "dx", "load", "aux")}
+    o = O.layer_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], w.k, sel_bias=b)
+    bo = O.layer_backward(o, a["x"], a["w_r"], a["w_gu"], a["w_down"], a["dy"], w.k,
+                          aux_coeff=coeff, n_valid=n_valid)
+    check_forward(g, o)
+    check_backward(g, bo)
+    assert np.array_equal(g["load"], bo["load"])
+    assert abs(g["aux"][0] - bo["aux"]) <= 1e-5 * bo["aux"]
+    assert abs(g["aux"][1] - bo["aux_scaled"]) <= 1e-5 * bo["aux_scaled"]
+    nb = O.bias_update(b, bo["load"], n_valid, w.k, 1e-3)
+    assert np.array_equal(down(gb).view(np.uint32), nb.view(np.uint32))
+    # the large bias forces its expert into every token's selection
+    assert np.all(g["topk_idx"][:, 0] == w.E // 3)
