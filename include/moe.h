@@ -217,15 +217,18 @@ int moe_router_logits_bwd(const void *x, const void *w_r, const float *d_logits,
 /* ---------------------------------------------------------------- router variants */
 
 /*
- * The pages name three router features without giving formulas ("Halo:
- * Frontier-Lab Training for Everyone"): balancing through a bias on expert
- * selection for a model family without a router auxiliary loss (the LFM2
- * cookbook config, `moe_balancing: bias_update`, and the paragraph after it);
- * a router load-balancing auxiliary loss with a per-run coefficient whose
- * gradient the routers apply and whose unscaled and scaled values they report
- * (ms-swift DPO integration); and MoE statistics that ignore the right-padded
- * tail of a batch, the valid prefix being n_valid tokens (sequence-parallel
- * input contract).  The formulas below are the plainest readings.
+ * The pages name three router features without giving formulas: balancing
+ * through a bias on expert selection for a model family without a router
+ * auxiliary loss ("Halo's 2.8x over TRL is not a kernel, and its own benchmark
+ * proves it", section "The small-hardware end": the LFM2 config,
+ * `moe_balancing: bias_update`, and the paragraph after it); a router
+ * load-balancing auxiliary loss with a per-run coefficient whose gradient the
+ * routers apply and whose unscaled and scaled values they report (the
+ * TorchTurbo page, "inclusionAI open-sources TorchTurbo, a SuperNode-native
+ * post-training engine", section "Adapter", ms-swift DPO); and MoE statistics
+ * that ignore the right-padded tail of a batch, the valid prefix being n_valid
+ * tokens (same TorchTurbo page, section "Model", sequence-parallel input
+ * contract).  The formulas below are the plainest readings.
  */
 
 /*

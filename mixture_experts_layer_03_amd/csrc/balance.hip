@@ -1,13 +1,16 @@
 // Expert-load statistics over a valid token prefix, the selection-bias
 // balancing update, and the load-balancing auxiliary loss with its gradient.
 //
-// The pages name three router features without formulas ("Halo: Frontier-Lab
-// Training for Everyone"): balancing through an expert-selection bias for a
-// family that has no router auxiliary loss (the LFM2 cookbook config and the
-// paragraph after it), a router auxiliary loss with a per-run coefficient whose
-// gradient the routers apply while reporting the unscaled and scaled values
-// (ms-swift DPO integration), and MoE statistics that skip the right-padded
-// tail of a batch (sequence-parallel input contract).  Readings used here:
+// The pages name three router features without formulas: balancing through an
+// expert-selection bias for a family that has no router auxiliary loss ("Halo's
+// 2.8x over TRL is not a kernel, and its own benchmark proves it", section "The
+// small-hardware end", the LFM2 config and the paragraph after it); a router
+// auxiliary loss with a per-run coefficient whose gradient the routers apply
+// while reporting the unscaled and scaled values (the TorchTurbo page,
+// "inclusionAI open-sources TorchTurbo, a SuperNode-native post-training
+// engine", section "Adapter", ms-swift DPO); and MoE statistics that skip the
+// right-padded tail of a batch (same TorchTurbo page, section "Model",
+// sequence-parallel input contract).  Readings used here:
 //   load_e      = #{(t, j) : t < n_valid, topk_idx[t,j] = e}
 //   bias update : b_e += rate * sign(n_valid * k / E - load_e)
 //   aux         = E * sum_e (load_e / (n_valid k)) * P_e,

@@ -323,14 +323,17 @@ def router_logits_bwd(x, w_r, d_logits):
 #
 # The pages name these features without formulas: LFM2's recipe sets
 # ``moe_balancing: bias_update`` because that family has no router auxiliary
-# loss, so balance is kept through a bias on expert *selection* ("Halo:
-# Frontier-Lab Training for Everyone", the LFM2 cookbook config and the
-# paragraph after it); other models train with a router auxiliary loss whose
-# coefficient is set per run, the routers applying its gradient and reporting
-# the unscaled and scaled values (same page, ms-swift DPO integration); and
-# right-padded tails are excluded from MoE statistics, the valid prefix being
-# described by the packed-sequence metadata (same page, sequence-parallel
-# input contract).  The plainest readings, used here:
+# loss, so balance is kept through a bias on expert *selection* ("Halo's 2.8x
+# over TRL is not a kernel, and its own benchmark proves it", section "The
+# small-hardware end", the LFM2 config and the paragraph after it); other
+# models train with a router auxiliary loss whose coefficient is set per run,
+# the routers applying its gradient and reporting the unscaled and scaled
+# values (the TorchTurbo page, "inclusionAI open-sources TorchTurbo, a
+# SuperNode-native post-training engine", section "Adapter", ms-swift DPO);
+# and right-padded tails are excluded from MoE statistics, the valid prefix
+# being described by the packed-sequence metadata (same TorchTurbo page,
+# section "Model", sequence-parallel input contract).  The plainest readings,
+# used here:
 #   * selection score s[t,e] = fp32(L[t,e] + b_sel[e]) picks the k experts
 #     (same order and tie rule as ``route``); the weights are the softmax of
 #     the k selected *unbiased* logits, so the bias steers selection only;
