@@ -188,6 +188,24 @@ int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int dtype,
 int moe_permute_bwd(const void *dx_perm, const int32_t *slot_to_row, const float *dx_add,
                     int dtype, int64_t T, int d, int k, void *dx, void *stream);
 
+/*
+ * moe_permute_bwd with the router's share of the token gradient formed in the
+ * same pass instead of read from memory:
+ *   dx[t] = store(sum_{j asc} fp32(dx_perm[slot_to_row[t*k+j]]) + r[t]),
+ *   r[t,:] = d_logits[t,:] . w_r  (fp32 fma chain over e ascending from +0,
+ *            entries with d_logits == 0 skipped),
+ * bit for bit what moe_router_logits_bwd's dx_router followed by
+ * moe_permute_bwd gives, without storing dx_router ([T,d] fp32).  Same
+ * pass as B6 of the backward; the router term is B8's dX (the router linear
+ * map's adjoint, "fp32 router logits" in "Halo's 2.8x over TRL is not a
+ * kernel, and its own benchmark proves it", section "Where the gap actually
+ * is").  d_logits: [T,E] fp32; w_r: [E,d] (dtype); 1 <= E <= 1024; other
+ * arguments and errors as moe_permute_bwd.
+ */
+int moe_permute_bwd_router(const void *dx_perm, const int32_t *slot_to_row, const float *d_logits,
+                           const void *w_r, int dtype, int64_t T, int d, int E, int k, void *dx,
+                           void *stream);
+
 /* ---------------------------------------------------------------- router bwd */
 
 /*

@@ -46,6 +46,8 @@ _SIGS = {
     "moe_combine_bwd": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_permute_bwd": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
                                _c_void_p]),
+    "moe_permute_bwd_router": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
+                                      _i32, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_route_bwd": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                              _c_void_p, _c_void_p, _c_void_p]),
     "moe_router_logits_bwd_workspace_size": (_sz, [_i64, _i32, _i32]),
@@ -187,6 +189,14 @@ def moe_permute_bwd(dx_perm, slot_to_row, dx_add, T, k, dx, stream=None):
     _check("moe_permute_bwd", lib().moe_permute_bwd(_p(dx_perm), _p(slot_to_row), _p(dx_add),
                                                     _dtype_code(dx_perm), T, d, k, _p(dx),
                                                     _stream(stream)))
+
+
+def moe_permute_bwd_router(dx_perm, slot_to_row, d_logits, w_r, T, k, dx, stream=None):
+    d = dx_perm.shape[1]
+    E = w_r.shape[0]
+    _check("moe_permute_bwd_router", lib().moe_permute_bwd_router(
+        _p(dx_perm), _p(slot_to_row), _p(d_logits), _p(w_r), _dtype_code(dx_perm), T, d, E, k,
+        _p(dx), _stream(stream)))
 
 
 def moe_route_bwd(topk_idx, topk_w, d_row_scale, slot_to_row, E, d_topk_w, d_logits,

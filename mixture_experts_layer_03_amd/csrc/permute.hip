@@ -234,42 +234,106 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
   }
 }
 
-// dst[t] = store(sum_j src[slot_to_row[t*k+j]] (+ add[t]))
-template <typename T>
+// dst[t] = store(sum_j src[slot_to_row[t*k+j]] (+ add[t])), j ascending in
+// fp32.  With ROUTER the fp32 term added is the router's share of the token
+// gradient, d_logits[t,:] . w_r, formed here as an fma chain over the experts
+// in ascending order that skips zero entries (the same chain, bit for bit, as
+// the router's own dX kernel), so it is never stored.  Each lane covers two
+// 16-byte chunks 64 apart, and the row indices (held one per lane, read out
+// with readlane) are taken four at a time so that four rows' loads are in
+// flight before their adds.
+template <typename T, bool ROUTER>
 __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
                                                     const int32_t *__restrict__ slot_to_row,
-                                                    const float *__restrict__ add, int64_t ntok,
+                                                    const float *__restrict__ add,
+                                                    const float *__restrict__ d_logits,
+                                                    const T *__restrict__ w_r, int E, int64_t ntok,
                                                     int d, int k, T *__restrict__ dst) {
   constexpr int N = Vec16<T>::N;
   const int64_t t = wave_token();
   if (t >= ntok) return;
   const int lane = threadIdx.x & 63;
   const int nvec = d * (int)sizeof(T) / 16;
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[N];
+  const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  for (int c0 = 0; c0 < nvec; c0 += 128) {
+    const int ca = c0 + lane, cb = ca + 64;
+    const bool va = ca < nvec, vb = cb < nvec;
+    float acc_a[N], acc_b[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = slot_to_row[t * k + j];
-      if (r < 0) continue;
-      const u32x4_t v = reinterpret_cast<const u32x4_t *>(src + (int64_t)r * d)[c];
-      float f[N];
-      unpack16(v, f, (const T *)nullptr);
+    for (int i = 0; i < N; ++i) acc_a[i] = acc_b[i] = 0.0f;
+    for (int j = 0; j < k; j += 4) {
+      u32x4_t xa[4], xb[4];
+      int r[4];
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += f[i];
-    }
-    if (add) {
-      const float *a = add + t * d + (int64_t)c * N;
+      for (int u = 0; u < 4; ++u) {
+        r[u] = j + u < k ? __builtin_amdgcn_readlane(myr, j + u) : -1;
+        xa[u] = xb[u] = zero;
+        if (r[u] >= 0) {
+          const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + (int64_t)r[u] * d);
+          if (va) xa[u] = row[ca];
+          if (vb) xb[u] = row[cb];
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < N; i += 4) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(a + i);
-        acc[i] += a4.x;
-        acc[i + 1] += a4.y;
-        acc[i + 2] += a4.z;
-        acc[i + 3] += a4.w;
+      for (int u = 0; u < 4; ++u) {
+        if (r[u] < 0) continue;
+        float f[N];
+        unpack16(xa[u], f, (const T *)nullptr);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc_a[i] += f[i];
+        unpack16(xb[u], f, (const T *)nullptr);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc_b[i] += f[i];
       }
     }
-    reinterpret_cast<u32x4_t *>(dst + t * d)[c] = pack16(acc, (const T *)nullptr);
+    if (add) {
+      const float *ar = add + t * d;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = h ? cb : ca;
+        if (!(h ? vb : va)) continue;
+        float *acc = h ? acc_b : acc_a;
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+          const float4 a4 = *reinterpret_cast<const float4 *>(ar + (int64_t)c * N + i);
+          acc[i] += a4.x;
+          acc[i + 1] += a4.y;
+          acc[i + 2] += a4.z;
+          acc[i + 3] += a4.w;
+        }
+      }
+    }
+    if (ROUTER) {
+      float ra[N], rb[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) ra[i] = rb[i] = 0.0f;
+      for (int e0 = 0; e0 < E; e0 += 64) {
+        const float dl = e0 + lane < E ? d_logits[t * E + e0 + lane] : 0.0f;
+        const int ne = min(64, E - e0);
+        for (int e = 0; e < ne; ++e) {
+          const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), e));
+          if (g == 0.0f) continue;
+          const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(w_r + (int64_t)(e0 + e) * d);
+          float wa[N], wb[N];
+          unpack16(va ? wr[ca] : zero, wa, (const T *)nullptr);
+          unpack16(vb ? wr[cb] : zero, wb, (const T *)nullptr);
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            ra[i] = fmaf(g, wa[i], ra[i]);
+            rb[i] = fmaf(g, wb[i], rb[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        acc_a[i] += ra[i];
+        acc_b[i] += rb[i];
+      }
+    }
+    u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + t * d);
+    if (va) o[ca] = pack16(acc_a, (const T *)nullptr);
+    if (vb) o[cb] = pack16(acc_b, (const T *)nullptr);
   }
 }
 
@@ -368,12 +432,14 @@ extern "C" int moe_combine(const void *y_perm, const int32_t *slot_to_row, int d
   const unsigned blocks = (unsigned)((T + 3) / 4);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("combine", s,
-               k_gather_sum<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)y_perm, slot_to_row,
-                                                           nullptr, T, d, k, (bf16_t *)y));
+               k_gather_sum<bf16_t, false><<<blocks, 256, 0, s>>>(
+                   (const bf16_t *)y_perm, slot_to_row, nullptr, nullptr, nullptr, 0, T, d, k,
+                   (bf16_t *)y));
   else
     MOE_LAUNCH("combine", s,
-               k_gather_sum<float><<<blocks, 256, 0, s>>>((const float *)y_perm, slot_to_row,
-                                                          nullptr, T, d, k, (float *)y));
+               k_gather_sum<float, false><<<blocks, 256, 0, s>>>(
+                   (const float *)y_perm, slot_to_row, nullptr, nullptr, nullptr, 0, T, d, k,
+                   (float *)y));
   return check_launch("moe_combine");
 }
 
@@ -413,11 +479,39 @@ extern "C" int moe_permute_bwd(const void *dx_perm, const int32_t *slot_to_row, 
   const unsigned blocks = (unsigned)((T + 3) / 4);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("permute_bwd", s,
-               k_gather_sum<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)dx_perm, slot_to_row,
-                                                           dx_add, T, d, k, (bf16_t *)dx));
+               k_gather_sum<bf16_t, false><<<blocks, 256, 0, s>>>(
+                   (const bf16_t *)dx_perm, slot_to_row, dx_add, nullptr, nullptr, 0, T, d, k,
+                   (bf16_t *)dx));
   else
     MOE_LAUNCH("permute_bwd", s,
-               k_gather_sum<float><<<blocks, 256, 0, s>>>((const float *)dx_perm, slot_to_row,
-                                                          dx_add, T, d, k, (float *)dx));
+               k_gather_sum<float, false><<<blocks, 256, 0, s>>>(
+                   (const float *)dx_perm, slot_to_row, dx_add, nullptr, nullptr, 0, T, d, k,
+                   (float *)dx));
   return check_launch("moe_permute_bwd");
+}
+
+extern "C" int moe_permute_bwd_router(const void *dx_perm, const int32_t *slot_to_row,
+                                      const float *d_logits, const void *w_r, int dtype, int64_t T,
+                                      int d, int E, int k, void *dx, void *stream) {
+  clear_error();
+  int rc = check_rows("moe_permute_bwd_router", dtype, T, d, k);
+  if (rc) return rc;
+  MOE_REQUIRE(E >= 1 && E <= kMaxExperts, MOE_ERR_UNSUPPORTED, "moe_permute_bwd_router: E=%d", E);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(dx_perm && slot_to_row && d_logits && w_r && dx && aligned16(dx_perm) &&
+                  aligned16(w_r) && aligned16(dx),
+              MOE_ERR_INVALID_ARG, "moe_permute_bwd_router: null or misaligned pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    MOE_LAUNCH("permute_bwd", s,
+               k_gather_sum<bf16_t, true><<<blocks, 256, 0, s>>>(
+                   (const bf16_t *)dx_perm, slot_to_row, nullptr, d_logits, (const bf16_t *)w_r,
+                   E, T, d, k, (bf16_t *)dx));
+  else
+    MOE_LAUNCH("permute_bwd", s,
+               k_gather_sum<float, true><<<blocks, 256, 0, s>>>(
+                   (const float *)dx_perm, slot_to_row, nullptr, d_logits, (const float *)w_r, E,
+                   T, d, k, (float *)dx));
+  return check_launch("moe_permute_bwd_router");
 }

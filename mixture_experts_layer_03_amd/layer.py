@@ -8,7 +8,10 @@ on one stream, with no host synchronisation in between:
             selection bias) -> moe_permute -> moe_grouped_ffn_fwd -> moe_combine
   backward: moe_combine_bwd -> moe_grouped_ffn_bwd -> moe_route_bwd ->
             [moe_expert_load -> moe_aux_loss, with an auxiliary-loss
-            coefficient] -> moe_router_logits_bwd -> moe_permute_bwd
+            coefficient] -> moe_router_logits_bwd (dW_r) ->
+            moe_permute_bwd_router (dX with the router term formed in the
+            same pass; with fuse_router_dx=False, moe_router_logits_bwd also
+            stores dx_router and moe_permute_bwd adds it)
   balance : moe_expert_load -> moe_bias_update (selection-bias step)
 
 This mirrors the EP forward path the pages describe (router logits in fp32,
@@ -28,8 +31,9 @@ from . import abi
 
 class MoEBlock:
     def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype=torch.bfloat16,
-                 device="cuda", backward: bool = True):
+                 device="cuda", backward: bool = True, fuse_router_dx: bool = True):
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
+        self.fuse_router_dx = fuse_router_dx
         self.R = T * k
         self.dtype = dtype
         self.device = device
@@ -69,7 +73,8 @@ class MoEBlock:
             self.d_row_scale = z(R, dt=f32)
             self.d_topk_w = z(T, k, dt=f32)
             self.d_logits = z(T, E, dt=f32)
-            self.dx_router = z(T, d, dt=f32)
+            # the router's fp32 dX is only stored when it is not fused into dX
+            self.dx_router = None if fuse_router_dx else z(T, d, dt=f32)
             self.dw_r = z(E, d, dt=f32)
             self.dw_gu = z(E, 2 * f, d, dt=f32)
             self.dw_down = z(E, d, f, dt=f32)
@@ -114,10 +119,15 @@ class MoEBlock:
             abi.moe_expert_load(self.topk_idx, n, self.E, self.load, self.ws, stream)
             abi.moe_aux_loss(self.logits, self.load, n, self.k, aux_coeff, self.aux,
                              self.d_logits, self.ws, stream)
-        abi.moe_router_logits_bwd(x, w_r, self.d_logits, self.dx_router, self.dw_r, self.ws,
-                                  stream)
-        abi.moe_permute_bwd(self.dx_perm, self.slot_to_row, self.dx_router, self.T, self.k,
-                            self.dx, stream)
+        if self.fuse_router_dx:
+            abi.moe_router_logits_bwd(x, w_r, self.d_logits, None, self.dw_r, self.ws, stream)
+            abi.moe_permute_bwd_router(self.dx_perm, self.slot_to_row, self.d_logits, w_r, self.T,
+                                       self.k, self.dx, stream)
+        else:
+            abi.moe_router_logits_bwd(x, w_r, self.d_logits, self.dx_router, self.dw_r, self.ws,
+                                      stream)
+            abi.moe_permute_bwd(self.dx_perm, self.slot_to_row, self.dx_router, self.T, self.k,
+                                self.dx, stream)
         return self.dx
 
     def balance_selection_bias(self, sel_bias, rate: float, n_valid: Optional[int] = None,

@@ -82,6 +82,16 @@ def test_validation_rejects_before_launch():
     assert "T < 0" in abi.lib().moe_last_error().decode()
 
 
+def test_fused_router_dx_validation():
+    L = abi.lib()
+    assert L.moe_permute_bwd_router(P, P, P, P, 1, 10, 16, 2000, 2, P, None) == -2
+    assert L.moe_permute_bwd_router(P, P, None, P, 1, 10, 16, 8, 2, P, None) == -1
+    assert L.moe_permute_bwd_router(P, P, P, ctypes.c_void_p(0x1004), 1, 10, 16, 8, 2, P,
+                                    None) == -1
+    assert L.moe_permute_bwd_router(P, P, P, P, 1, 10, 12, 8, 2, P, None) == -2
+    assert L.moe_permute_bwd_router(None, None, None, None, 1, 0, 16, 8, 2, None, None) == 0
+
+
 def test_router_variant_validation_rejects_before_launch():
     L = abi.lib()
     F = ctypes.c_float

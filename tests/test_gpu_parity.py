@@ -33,14 +33,15 @@ SMALL = [
 ]
 
 
-def run_gpu(w, a, backward=True):
+def run_gpu(w, a, backward=True, fuse_router_dx=True):
     import torch
     from mixture_experts_layer_03_amd.layer import MoEBlock
     dev = need_gpu()
     bf = w.dtype == "bf16"
     dt = torch.bfloat16 if bf else torch.float32
     print("GPU case", w.name, flush=True)
-    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=dt, device=dev, backward=backward)
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=dt, device=dev, backward=backward,
+                   fuse_router_dx=fuse_router_dx)
     x, wr, wgu, wd = (up(a[n], bf, dev) for n in ("x", "w_r", "w_gu", "w_down"))
     bias = None if a["bias"] is None else up(a["bias"], False, dev)
     noise = None if a["noise"] is None else up(a["noise"], False, dev)
@@ -53,8 +54,10 @@ def run_gpu(w, a, backward=True):
         "x_perm", "w_perm", "gu", "h", "y_perm", "y")}
     if backward:
         for n in ("dy_perm", "dgu", "dx_perm", "d_row_scale", "d_topk_w", "d_logits",
-                  "dx_router", "dw_r", "dw_gu", "dw_down", "dx"):
+                  "dw_r", "dw_gu", "dw_down", "dx"):
             out[n] = down(getattr(blk, n))
+        if not fuse_router_dx:
+            out["dx_router"] = down(blk.dx_router)
     return out
 
 
@@ -95,7 +98,8 @@ def check_backward(g, b):
     assert np.array_equal(g["dy_perm"], b["dy_perm"]), "dy_perm"
     for n in FLIP_BWD:
         close(n, g[n], b[n], flip=True)
-    close("dx_router", g["dx_router"], b["dx_router"])
+    if "dx_router" in g:
+        close("dx_router", g["dx_router"], b["dx_router"])
     close("dx", g["dx"], b["dx"])
 
 
@@ -106,6 +110,20 @@ def test_layer_forward_backward_matches_oracle(w):
     o, b = run_oracle(w, a)
     check_forward(g, o)
     check_backward(g, b)
+
+
+@pytest.mark.parametrize("w", SMALL[:2] + SMALL[4:5], ids=[w.name for w in SMALL[:2] + SMALL[4:5]])
+def test_router_dx_fused_matches_stored_path(w):
+    """dX with the router term formed in the gather pass equals, bit for bit,
+    dX from the stored fp32 router gradient; that stored gradient matches the
+    oracle."""
+    a = I.make_inputs(w)
+    g_f = run_gpu(w, a)
+    g_u = run_gpu(w, a, fuse_router_dx=False)
+    assert np.array_equal(np.asarray(g_f["dx"]).view(np.uint32), np.asarray(g_u["dx"]).view(np.uint32))
+    _, b = run_oracle(w, a)
+    close("dx_router", g_u["dx_router"], b["dx_router"])
+    check_backward(g_u, b)
 
 
 def test_tiny_fp32_forward_matches_oracle():

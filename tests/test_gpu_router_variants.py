@@ -179,7 +179,7 @@ def test_block_with_selection_bias_and_aux_loss_matches_oracle(w):
     g = {n: down(getattr(blk, n)) for n in (
         "logits", "topk_idx", "topk_w", "counts", "offsets", "slot_to_row", "row_to_slot",
         "x_perm", "w_perm", "gu", "h", "y_perm", "y", "dy_perm", "dgu", "dx_perm", "d_row_scale",
-        "d_topk_w", "d_logits", "dx_router", "dw_r", "dw_gu", "dw_down", "dx", "load", "aux")}
+        "d_topk_w", "d_logits", "dw_r", "dw_gu", "dw_down", "dx", "load", "aux")}
     o = O.layer_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], w.k, sel_bias=b)
     bo = O.layer_backward(o, a["x"], a["w_r"], a["w_gu"], a["w_down"], a["dy"], w.k,
                           aux_coeff=coeff, n_valid=n_valid)
