@@ -161,10 +161,13 @@ __global__ __launch_bounds__(256) void k_place(const int32_t *__restrict__ idx, 
 
 // ------------------------------------------------------------------ rows
 //
-// One wave per token; lanes stride over the row in 16-byte chunks.  A token
-// row is read once and written to its k rows (forward permute, combine bwd),
-// or its k rows are gathered and summed in fp32, j ascending (combine,
+// One wave per piece of kRowPiece 16-byte chunks of a token row (a 2880-wide
+// bf16 row is three pieces), so that many waves have loads in flight.  A
+// token row is read once and written to its k rows (forward permute, combine
+// bwd), or its k rows are gathered and summed in fp32, j ascending (combine,
 // permute bwd).
+
+constexpr int kRowPiece = 128;   // 16-byte chunks of a row per wave
 
 template <typename T>
 struct Vec16 {
@@ -195,53 +198,60 @@ __device__ __forceinline__ u32x4_t pack16(const float *f, const float *) {
   return v;
 }
 
-// token served by this wave (wave-uniform, so per-token loads become scalar)
-__device__ __forceinline__ int64_t wave_token() {
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  return (int64_t)blockIdx.x * 4 + w;
-}
 
 // src[t] -> dst[slot_to_row[t*k+j]] for j < k (src may be NULL: no rows);
-// optional w_dst[row] = w_src[t*k+j]
+// optional w_dst[row] = w_src[t*k+j].  One wave per (token, 128-chunk piece
+// of the row), lane l copying chunks l and l + 64 of the piece to the k rows;
+// the piece-0 wave also moves the weights.
 template <typename T>
 __global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
                                                       const int32_t *__restrict__ slot_to_row,
                                                       const float *__restrict__ w_src, int64_t ntok,
                                                       int d, int k, T *__restrict__ dst,
                                                       float *__restrict__ w_dst) {
-  const int64_t t = wave_token();
+  const int nvec = src ? d * (int)sizeof(T) / 16 : 0;
+  const int pieces = nvec > 0 ? (nvec + kRowPiece - 1) / kRowPiece : 1;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t t = wid / pieces;
   if (t >= ntok) return;
+  const int piece = (int)(wid - t * pieces);
   const int lane = threadIdx.x & 63;
-  if (w_dst && lane < k) {
-    const int r = slot_to_row[t * k + lane];
-    if (r >= 0) w_dst[r] = w_src[t * k + lane];
-  }
+  const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
+  if (w_dst && piece == 0 && lane < k && myr >= 0) w_dst[myr] = w_src[t * k + lane];
   if (!src) return;
-  const int nvec = d * (int)sizeof(T) / 16;
+  const int ca = piece * kRowPiece + lane, cb = ca + 64;
+  const bool va = ca < nvec, vb = cb < nvec;
   const u32x4_t *s = reinterpret_cast<const u32x4_t *>(src + t * d);
-  for (int c = lane; c < nvec; c += 64 * 2) {
-    const int c2 = c + 64;
-    const u32x4_t v0 = s[c];
-    u32x4_t v1 = {0, 0, 0, 0};
-    if (c2 < nvec) v1 = s[c2];
-    for (int j = 0; j < k; ++j) {
-      const int r = slot_to_row[t * k + j];
-      if (r < 0) continue;
-      u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + (int64_t)r * d);
-      o[c] = v0;
-      if (c2 < nvec) o[c2] = v1;
-    }
+  u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = v0;
+  if (va) v0 = s[ca];
+  if (vb) v1 = s[cb];
+  for (int j = 0; j < k; ++j) {
+    const int r = __builtin_amdgcn_readlane(myr, j);
+    if (r < 0) continue;
+    u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + (int64_t)r * d);
+    if (va) o[ca] = v0;
+    if (vb) o[cb] = v1;
   }
+}
+
+// blocks (4 waves each) of the row kernels for ntok tokens of d elements
+template <typename V>
+static unsigned row_blocks(int64_t ntok, int d, bool rows = true, int piece = kRowPiece) {
+  const int64_t nvec = rows ? (int64_t)d * (int64_t)sizeof(V) / 16 : 0;
+  const int64_t pieces = nvec > 0 ? (nvec + piece - 1) / piece : 1;
+  return (unsigned)((ntok * pieces + 3) / 4);
 }
 
 // dst[t] = store(sum_j src[slot_to_row[t*k+j]] (+ add[t])), j ascending in
 // fp32.  With ROUTER the fp32 term added is the router's share of the token
 // gradient, d_logits[t,:] . w_r, formed here as an fma chain over the experts
 // in ascending order that skips zero entries (the same chain, bit for bit, as
-// the router's own dX kernel), so it is never stored.  Each lane covers two
-// 16-byte chunks 64 apart, and the row indices (held one per lane, read out
-// with readlane) are taken four at a time so that four rows' loads are in
-// flight before their adds.
+// the router's own dX kernel), so it is never stored.
+// One wave per (token, 128-chunk piece of the row): lane l covers 16-byte
+// chunks l and l + 64 of the piece.  Row indices are held one per lane and
+// read out with readlane; four rows' loads (and four router rows' loads) are
+// issued before their adds.
+
 template <typename T, bool ROUTER>
 __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
                                                     const int32_t *__restrict__ slot_to_row,
@@ -250,92 +260,133 @@ __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
                                                     const T *__restrict__ w_r, int E, int64_t ntok,
                                                     int d, int k, T *__restrict__ dst) {
   constexpr int N = Vec16<T>::N;
-  const int64_t t = wave_token();
-  if (t >= ntok) return;
-  const int lane = threadIdx.x & 63;
   const int nvec = d * (int)sizeof(T) / 16;
+  // the router term needs more registers: one chunk per lane, more waves
+  constexpr int PIECE = ROUTER ? 64 : kRowPiece;
+  const int pieces = (nvec + PIECE - 1) / PIECE;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t t = wid / pieces;
+  if (t >= ntok) return;
+  const int c0 = (int)(wid - t * pieces) * PIECE;
+  const int lane = threadIdx.x & 63;
   const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
+  // router: this lane's entry of the first 64 experts and the nonzero ones
+  const float dl0 = ROUTER && lane < E ? d_logits[t * E + lane] : 0.0f;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  for (int c0 = 0; c0 < nvec; c0 += 128) {
-    const int ca = c0 + lane, cb = ca + 64;
-    const bool va = ca < nvec, vb = cb < nvec;
-    float acc_a[N], acc_b[N];
+  const int ca = c0 + lane, cb = ca + 64;
+  const bool va = ca < nvec, vb = PIECE > 64 && cb < nvec;
+  float acc_a[N], acc_b[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc_a[i] = acc_b[i] = 0.0f;
-    for (int j = 0; j < k; j += 4) {
-      u32x4_t xa[4], xb[4];
-      int r[4];
+  for (int i = 0; i < N; ++i) acc_a[i] = acc_b[i] = 0.0f;
+  // Up to four router rows (the first nonzero experts) are loaded with the
+  // first four gathered rows; their fmas come after the row sums.
+  uint64_t nz = ROUTER ? __ballot(dl0 != 0.0f) : 0;
+  int ev[4];
+  float g[4];
+  u32x4_t wa[4], wb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        r[u] = j + u < k ? __builtin_amdgcn_readlane(myr, j + u) : -1;
-        xa[u] = xb[u] = zero;
-        if (r[u] >= 0) {
-          const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + (int64_t)r[u] * d);
-          if (va) xa[u] = row[ca];
-          if (vb) xb[u] = row[cb];
-        }
-      }
+  for (int u = 0; u < 4; ++u) {
+    ev[u] = -1;
+    g[u] = 0.0f;
+    wa[u] = wb[u] = zero;
+  }
+  auto load_router = [&](int e0, float dl) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (r[u] < 0) continue;
-        float f[N];
-        unpack16(xa[u], f, (const T *)nullptr);
-#pragma unroll
-        for (int i = 0; i < N; ++i) acc_a[i] += f[i];
-        unpack16(xb[u], f, (const T *)nullptr);
-#pragma unroll
-        for (int i = 0; i < N; ++i) acc_b[i] += f[i];
-      }
-    }
-    if (add) {
-      const float *ar = add + t * d;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = h ? cb : ca;
-        if (!(h ? vb : va)) continue;
-        float *acc = h ? acc_b : acc_a;
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-          const float4 a4 = *reinterpret_cast<const float4 *>(ar + (int64_t)c * N + i);
-          acc[i] += a4.x;
-          acc[i + 1] += a4.y;
-          acc[i + 2] += a4.z;
-          acc[i + 3] += a4.w;
-        }
+    for (int u = 0; u < 4; ++u) {
+      ev[u] = -1;
+      if (nz) {
+        const int e = __builtin_ctzll(nz);
+        nz &= nz - 1;
+        ev[u] = e;
+        g[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), e));
+        const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(w_r + (int64_t)(e0 + e) * d);
+        wa[u] = va ? wr[ca] : zero;
+        wb[u] = vb ? wr[cb] : zero;
       }
     }
-    if (ROUTER) {
-      float ra[N], rb[N];
+  };
+  if (ROUTER) load_router(0, dl0);
+  for (int j = 0; j < k; j += 4) {
+    u32x4_t xa[4], xb[4];
+    int r[4];
 #pragma unroll
-      for (int i = 0; i < N; ++i) ra[i] = rb[i] = 0.0f;
-      for (int e0 = 0; e0 < E; e0 += 64) {
-        const float dl = e0 + lane < E ? d_logits[t * E + e0 + lane] : 0.0f;
-        const int ne = min(64, E - e0);
-        for (int e = 0; e < ne; ++e) {
-          const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), e));
-          if (g == 0.0f) continue;
-          const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(w_r + (int64_t)(e0 + e) * d);
-          float wa[N], wb[N];
-          unpack16(va ? wr[ca] : zero, wa, (const T *)nullptr);
-          unpack16(vb ? wr[cb] : zero, wb, (const T *)nullptr);
+    for (int u = 0; u < 4; ++u) {
+      r[u] = j + u < k ? __builtin_amdgcn_readlane(myr, j + u) : -1;
+      xa[u] = xb[u] = zero;
+      if (r[u] >= 0) {
+        const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + (int64_t)r[u] * d);
+        if (va) xa[u] = row[ca];
+        if (vb) xb[u] = row[cb];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (r[u] < 0) continue;
+      float f[N];
+      unpack16(xa[u], f, (const T *)nullptr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc_a[i] += f[i];
+      unpack16(xb[u], f, (const T *)nullptr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc_b[i] += f[i];
+    }
+  }
+  if (add) {
+    const float *ar = add + t * d;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h ? cb : ca;
+      if (!(h ? vb : va)) continue;
+      float *acc = h ? acc_b : acc_a;
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(ar + (int64_t)c * N + i);
+        acc[i] += a4.x;
+        acc[i + 1] += a4.y;
+        acc[i + 2] += a4.z;
+        acc[i + 3] += a4.w;
+      }
+    }
+  }
+  if (ROUTER) {
+    float ra[N], rb[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) ra[i] = rb[i] = 0.0f;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      float dl = dl0;
+      if (e0 > 0) {
+        dl = e0 + lane < E ? d_logits[t * E + e0 + lane] : 0.0f;
+        nz = __ballot(dl != 0.0f);
+        load_router(e0, dl);
+      }
+      while (true) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (ev[u] < 0) continue;
+          float fa[N], fb[N];
+          unpack16(wa[u], fa, (const T *)nullptr);
+          unpack16(wb[u], fb, (const T *)nullptr);
 #pragma unroll
           for (int i = 0; i < N; ++i) {
-            ra[i] = fmaf(g, wa[i], ra[i]);
-            rb[i] = fmaf(g, wb[i], rb[i]);
+            ra[i] = fmaf(g[u], fa[i], ra[i]);
+            rb[i] = fmaf(g[u], fb[i], rb[i]);
           }
         }
-      }
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        acc_a[i] += ra[i];
-        acc_b[i] += rb[i];
+        if (!nz) break;
+        load_router(e0, dl);
       }
     }
-    u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + t * d);
-    if (va) o[ca] = pack16(acc_a, (const T *)nullptr);
-    if (vb) o[cb] = pack16(acc_b, (const T *)nullptr);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      acc_a[i] += ra[i];
+      acc_b[i] += rb[i];
+    }
   }
+  u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + t * d);
+  if (va) o[ca] = pack16(acc_a, (const T *)nullptr);
+  if (vb) o[cb] = pack16(acc_b, (const T *)nullptr);
 }
+
 
 }  // namespace moe
 
@@ -404,7 +455,8 @@ extern "C" int moe_permute(const void *x, const int32_t *topk_idx, const float *
   rc = check_launch("moe_permute(maps)");
   if (rc) return rc;
   if (x || w_perm) {
-    const unsigned blocks = (unsigned)((T + 3) / 4);
+    const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d, x != nullptr)
+                                              : row_blocks<float>(T, d, x != nullptr);
     if (dtype == MOE_BF16)
       MOE_LAUNCH("permute_rows", s,
                  k_scatter_rows<bf16_t><<<blocks, 256, 0, s>>>(
@@ -429,7 +481,7 @@ extern "C" int moe_combine(const void *y_perm, const int32_t *slot_to_row, int d
   MOE_REQUIRE(y_perm && slot_to_row && y && aligned16(y_perm) && aligned16(y), MOE_ERR_INVALID_ARG,
               "moe_combine: null or misaligned pointer");
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d) : row_blocks<float>(T, d);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("combine", s,
                k_gather_sum<bf16_t, false><<<blocks, 256, 0, s>>>(
@@ -452,7 +504,7 @@ extern "C" int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int d
   MOE_REQUIRE(dy && slot_to_row && dy_perm && aligned16(dy) && aligned16(dy_perm),
               MOE_ERR_INVALID_ARG, "moe_combine_bwd: null or misaligned pointer");
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d) : row_blocks<float>(T, d);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("combine_bwd", s,
                k_scatter_rows<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)dy, slot_to_row,
@@ -476,7 +528,7 @@ extern "C" int moe_permute_bwd(const void *dx_perm, const int32_t *slot_to_row, 
                   (!dx_add || aligned16(dx_add)),
               MOE_ERR_INVALID_ARG, "moe_permute_bwd: null or misaligned pointer");
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d) : row_blocks<float>(T, d);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("permute_bwd", s,
                k_gather_sum<bf16_t, false><<<blocks, 256, 0, s>>>(
@@ -502,7 +554,8 @@ extern "C" int moe_permute_bwd_router(const void *dx_perm, const int32_t *slot_t
                   aligned16(w_r) && aligned16(dx),
               MOE_ERR_INVALID_ARG, "moe_permute_bwd_router: null or misaligned pointer");
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d, true, 64)
+                                            : row_blocks<float>(T, d, true, 64);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("permute_bwd", s,
                k_gather_sum<bf16_t, true><<<blocks, 256, 0, s>>>(
