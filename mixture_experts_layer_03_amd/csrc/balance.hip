@@ -176,8 +176,10 @@ __global__ __launch_bounds__(1024) void k_aux_final(const float *__restrict__ ps
   const int tid = threadIdx.x;
   const int e = tid / Q, q = tid % Q;
   float acc = 0.0f;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = q; b < nblk; b += Q) acc += psum[(int64_t)b * E + e];
+  }
   part[tid] = acc;
   __syncthreads();
   float term = 0.0f;
