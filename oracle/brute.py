@@ -198,3 +198,31 @@ def aux_loss_by_loops(L, topk_idx, n_valid, k, coeff):
         aux += (load[e] / (n_valid * k)) * (psum[e] / n_valid)
     aux *= E
     return aux, coeff * aux, load
+
+
+def torch_dense_lora(x, w_gu, w_down, a_gu, b_gu, a_dn, b_dn, scale, gate, dy):
+    """Dense formulation with LoRA-merged expert weights W + s B A, every
+    token through every expert, mixed by the fixed gate matrix [T,E]; torch
+    fp64 autograd for the gradients of sum(Y * dY) with respect to x and the
+    LoRA factors (expert weights frozen).  Returns y and the gradients."""
+    import torch
+    dt = torch.float64
+    X = torch.tensor(np.asarray(x), dtype=dt, requires_grad=True)
+    Ag = torch.tensor(np.asarray(a_gu), dtype=dt, requires_grad=True)
+    Bg = torch.tensor(np.asarray(b_gu), dtype=dt, requires_grad=True)
+    Ad = torch.tensor(np.asarray(a_dn), dtype=dt, requires_grad=True)
+    Bd = torch.tensor(np.asarray(b_dn), dtype=dt, requires_grad=True)
+    Wg = torch.tensor(np.asarray(w_gu), dtype=dt)
+    Wd = torch.tensor(np.asarray(w_down), dtype=dt)
+    G = torch.tensor(np.asarray(gate), dtype=dt)
+    f = Wg.shape[1] // 2
+    Y = 0
+    for e in range(Wg.shape[0]):
+        wg = Wg[e] + scale * Bg[e] @ Ag[e]
+        wd = Wd[e] + scale * Bd[e] @ Ad[e]
+        gu = X @ wg.T
+        h = torch.nn.functional.silu(gu[:, :f]) * gu[:, f:]
+        Y = Y + G[:, e:e + 1] * (h @ wd.T)
+    (Y * torch.tensor(np.asarray(dy), dtype=dt)).sum().backward()
+    return {"y": Y.detach().numpy(), "dx": X.grad.numpy(), "da_gu": Ag.grad.numpy(),
+            "db_gu": Bg.grad.numpy(), "da_dn": Ad.grad.numpy(), "db_dn": Bd.grad.numpy()}

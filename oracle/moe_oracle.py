@@ -285,6 +285,120 @@ def expert_ffn_bwd(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, bf16=T
     return out
 
 
+# ---------------------------------------------------------------------------
+# grouped LoRA on the fused expert weights (experts frozen)
+# ---------------------------------------------------------------------------
+#
+# "Halo: Frontier-Lab Training for Everyone" (section "One trainer
+# architecture, one parallelism stack") applies LoRA directly to the fused 3-D
+# expert weights, with
+# the experts frozen, so that they need no gradient or optimizer state.  The
+# pages give no formulas; the plainest reading, used here, is standard LoRA on
+# each expert matrix: W_gu[e] + s * B_gu[e] @ A_gu[e] and
+# W_down[e] + s * B_dn[e] @ A_dn[e], with A_gu[E,r,d], B_gu[E,2f,r],
+# A_dn[E,r,f], B_dn[E,d,r] (gate rows then up rows in B_gu, like W_gu) and
+# a scale s.  The low-rank products are stored in bf16 like the other
+# activations (storage points of this reading):
+#   z_gu = store(s * X_perm A_gu^T)              [R, r]
+#   GU   = store(X_perm W_gu^T + z_gu B_gu^T)      (one fp32 accumulation)
+#   z_dn = store(s * H A_dn^T)                   [R, r]
+#   Y    = store(w * (H W_down^T + z_dn B_dn^T))
+# backward (no expert weight gradients):
+#   u_dn = store(s * dY_perm B_dn)                [R, r]
+#   Gd   = dY_perm W_down + u_dn A_dn  -> dSwiGLU and d_row_scale as before
+#   u_gu = store(s * dGU B_gu)                    [R, r]
+#   dX_perm = store(dGU W_gu + u_gu A_gu)
+#   dB_gu = dGU^T z_gu, dA_gu = u_gu^T X_perm, dB_dn = S^T z_dn with
+#   S = store(w * dY_perm), dA_dn = (w * u_dn)^T H   (fp32 outputs)
+
+def _ffn_rows_lora(xr, w_gu_e, w_down_e, wr, a_gu_e, b_gu_e, a_dn_e, b_dn_e, scale, bf16):
+    f = w_gu_e.shape[0] // 2
+    z_gu = store(scale * (_f64(xr) @ _f64(a_gu_e).T), bf16)
+    gu = store(_f64(xr) @ _f64(w_gu_e).T + _f64(z_gu) @ _f64(b_gu_e).T, bf16)
+    gate, up = _f64(gu[:, :f]), _f64(gu[:, f:])
+    h = store(silu(gate) * up, bf16)
+    z_dn = store(scale * (_f64(h) @ _f64(a_dn_e).T), bf16)
+    y = _f64(h) @ _f64(w_down_e).T + _f64(z_dn) @ _f64(b_dn_e).T
+    if wr is not None:
+        y = _f64(wr)[:, None] * y
+    return gu, h, store(y, bf16), z_gu, z_dn
+
+
+def expert_ffn_fwd_lora(x_perm, offsets, w_gu, w_down, row_scale, a_gu, b_gu, a_dn, b_dn,
+                        scale: float, bf16=True):
+    """Loop over experts with LoRA on both expert matrices.  Returns GU, H,
+    Y_perm, z_gu[R,r], z_dn[R,r] (stored values)."""
+    R, d = x_perm.shape
+    E, f2, _ = w_gu.shape
+    f = f2 // 2
+    r = a_gu.shape[1]
+    gu = np.zeros((R, 2 * f), np.float32)
+    h = np.zeros((R, f), np.float32)
+    y = np.zeros((R, d), np.float32)
+    z_gu = np.zeros((R, r), np.float32)
+    z_dn = np.zeros((R, r), np.float32)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        wr = None if row_scale is None else row_scale[a:b]
+        gu[a:b], h[a:b], y[a:b], z_gu[a:b], z_dn[a:b] = _ffn_rows_lora(
+            x_perm[a:b], w_gu[e], w_down[e], wr, a_gu[e], b_gu[e], a_dn[e], b_dn[e], scale, bf16)
+    return gu, h, y, z_gu, z_dn
+
+
+def expert_ffn_bwd_lora(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, a_gu, b_gu,
+                        a_dn, b_dn, scale: float, z_gu, z_dn, bf16=True):
+    """Backward with frozen experts.  Returns dict with dGU, dX_perm,
+    d_row_scale, u_gu, u_dn (stored) and dA_gu[E,r,d], dB_gu[E,2f,r],
+    dA_dn[E,r,f], dB_dn[E,d,r] (fp32)."""
+    R, d = x_perm.shape
+    E, f2, _ = w_gu.shape
+    f = f2 // 2
+    r = a_gu.shape[1]
+    out = {
+        "dgu": np.zeros((R, 2 * f), np.float32),
+        "dx_perm": np.zeros((R, d), np.float32),
+        "d_row_scale": np.zeros(R, np.float32),
+        "u_gu": np.zeros((R, r), np.float32),
+        "u_dn": np.zeros((R, r), np.float32),
+        "da_gu": np.zeros((E, r, d), np.float32),
+        "db_gu": np.zeros((E, 2 * f, r), np.float32),
+        "da_dn": np.zeros((E, r, f), np.float32),
+        "db_dn": np.zeros((E, d, r), np.float32),
+    }
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue            # an empty expert's LoRA gradients are zero
+        xr, dyr = x_perm[a:b], dy_perm[a:b]
+        g = _f64(gu[a:b, :f])
+        uu = _f64(gu[a:b, f:])
+        h = store(silu(g) * uu, bf16)
+        w = np.ones(b - a) if row_scale is None else _f64(row_scale[a:b])
+        u_dn = store(scale * (_f64(dyr) @ _f64(b_dn[e])), bf16)
+        gd = _f64(dyr) @ _f64(w_down[e]) + _f64(u_dn) @ _f64(a_dn[e])
+        drs = np.sum(_f64(h) * gd, axis=1)
+        dh = w[:, None] * gd
+        sg = sigmoid(g)
+        dg = dh * uu * sg * (1.0 + g * (1.0 - sg))
+        du = dh * g * sg
+        dgu = store(np.concatenate([dg, du], axis=1), bf16)
+        u_gu = store(scale * (_f64(dgu) @ _f64(b_gu[e])), bf16)
+        dx = store(_f64(dgu) @ _f64(w_gu[e]) + _f64(u_gu) @ _f64(a_gu[e]), bf16)
+        s_ = store(w[:, None] * _f64(dyr), bf16)
+        out["dgu"][a:b] = dgu
+        out["dx_perm"][a:b] = dx
+        out["d_row_scale"][a:b] = drs.astype(np.float32)
+        out["u_gu"][a:b] = u_gu
+        out["u_dn"][a:b] = u_dn
+        out["db_gu"][e] = (_f64(dgu).T @ _f64(z_gu[a:b])).astype(np.float32)
+        out["da_gu"][e] = (_f64(u_gu).T @ _f64(xr)).astype(np.float32)
+        out["db_dn"][e] = (_f64(s_).T @ _f64(z_dn[a:b])).astype(np.float32)
+        out["da_dn"][e] = ((w[:, None] * _f64(u_dn)).T @ _f64(h)).astype(np.float32)
+    return out
+
+
 def permute_bwd(dx_perm, slot_to_row, T: int, k: int, dx_add=None, bf16=True):
     """dX[t] = sum over j of dX_perm[row of slot t*k+j] (+ dx_add[t]); fp64 sum."""
     s2r = np.asarray(slot_to_row, dtype=np.int64).reshape(T, k)

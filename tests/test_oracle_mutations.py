@@ -18,9 +18,10 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 MUTATIONS = [
     ("dropped dSiLU term", "dg = dh * u * sg * (1.0 + g * (1.0 - sg))", "dg = dh * u * sg"),
     ("wrong sign in softmax adjoint", "w * (g - s), axis=1)", "w * (g + s), axis=1)"),
-    ("up gradient uses sigmoid instead of silu", "du = dh * g * sg\n", "du = dh * sg\n"),
+    ("up gradient uses sigmoid instead of silu", "\n    du = dh * g * sg\n", "\n    du = dh * sg\n"),
     ("row weight not applied to the expert output",
-     "y = _f64(wr)[:, None] * y", "y = y"),
+     "y = _f64(wr)[:, None] * y\n    return gu, h, store(y, bf16)\n",
+     "y = y\n    return gu, h, store(y, bf16)\n"),
     ("row weight missing from the down-projection weight gradient",
      "s = store(w[:, None] * _f64(dyr), bf16)\n    return dgu", "s = store(_f64(dyr), bf16)\n    return dgu"),
     ("combine gathers with the wrong map", "s2r = np.asarray(slot_to_row, dtype=np.int64).reshape(T, k)\n    acc = np.zeros((T, y_perm",
@@ -49,6 +50,16 @@ MUTATIONS = [
     ("aux load fraction over tokens, not slots", "f = _f64(load) / (n * k)", "f = _f64(load) / n"),
     ("aux gradient without the softmax centring", "dl[:n] = p * (g[None, :] - s)", "dl[:n] = p * g[None, :]"),
     ("aux gradient not scaled by the coefficient", "g = coeff * E * f / n", "g = E * f / n"),
+    ("LoRA dH gradient without the scale", "u_dn = store(scale * (_f64(dyr) @ _f64(b_dn[e])), bf16)",
+     "u_dn = store((_f64(dyr) @ _f64(b_dn[e])), bf16)"),
+    ("LoRA term missing from dX", "dx = store(_f64(dgu) @ _f64(w_gu[e]) + _f64(u_gu) @ _f64(a_gu[e]), bf16)",
+     "dx = store(_f64(dgu) @ _f64(w_gu[e]), bf16)"),
+    ("LoRA dA_dn without the row weight", "((w[:, None] * _f64(u_dn)).T @ _f64(h))",
+     "(_f64(u_dn).T @ _f64(h))"),
+    ("LoRA dB_dn from dY instead of S", "(_f64(s_).T @ _f64(z_dn[a:b]))", "(_f64(dyr).T @ _f64(z_dn[a:b]))"),
+    ("LoRA down term added after the row weight",
+     "    y = _f64(h) @ _f64(w_down_e).T + _f64(z_dn) @ _f64(b_dn_e).T\n    if wr is not None:\n        y = _f64(wr)[:, None] * y\n    return gu, h, store(y, bf16), z_gu, z_dn",
+     "    y = _f64(h) @ _f64(w_down_e).T\n    if wr is not None:\n        y = _f64(wr)[:, None] * y\n    y = y + _f64(z_dn) @ _f64(b_dn_e).T\n    return gu, h, store(y, bf16), z_gu, z_dn"),
 ]
 
 PIN_TESTS = [
@@ -66,6 +77,9 @@ PIN_TESTS = [
     lambda: P.test_expert_load_by_loops_and_bias_update_closed_forms(),
     lambda: P.test_aux_loss_closed_forms(),
     lambda: P.test_aux_loss_matches_loops_and_finite_differences(),
+    lambda: P.test_lora_with_zero_b_is_the_plain_block(),
+    lambda: P.test_lora_forward_is_the_merged_weight_block(),
+    lambda: P.test_lora_gradients_match_torch_autograd(),
 ]
 
 

@@ -445,3 +445,87 @@ def test_aux_loss_matches_loops_and_finite_differences():
         aux2, _, dl2 = O.aux_loss(L[:n], load, n, k, coeff)
         assert aux2 == aux
         np.testing.assert_array_equal(dl2, dl[:n])
+
+
+# ---------------------------------------------------------------- grouped LoRA
+
+def _lora_case(T=40, d=24, E=5, k=2, f=16, r=8, seed=21, scale=0.5, zero_b=False):
+    rng = _rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    w_r = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    w_gu = (rng.standard_normal((E, 2 * f, d)) / np.sqrt(d)).astype(np.float32)
+    w_down = (rng.standard_normal((E, d, f)) / np.sqrt(f)).astype(np.float32)
+    a_gu = (rng.standard_normal((E, r, d)) / np.sqrt(d)).astype(np.float32)
+    b_gu = (rng.standard_normal((E, 2 * f, r)) * 0.3).astype(np.float32)
+    a_dn = (rng.standard_normal((E, r, f)) / np.sqrt(f)).astype(np.float32)
+    b_dn = (rng.standard_normal((E, d, r)) * 0.3).astype(np.float32)
+    if zero_b:
+        b_gu[:] = 0
+        b_dn[:] = 0
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    L = O.router_logits(x, w_r)
+    idx, tw = O.route(L, k)
+    counts, offsets, s2r, r2s = O.permute_maps(idx, E)
+    x_perm, w_perm = O.permute_rows(x, tw, r2s, k)
+    return dict(x=x, w_gu=w_gu, w_down=w_down, a_gu=a_gu, b_gu=b_gu, a_dn=a_dn, b_dn=b_dn,
+                dy=dy, idx=idx, tw=tw, offsets=offsets, s2r=s2r, r2s=r2s, x_perm=x_perm,
+                w_perm=w_perm, scale=scale, T=T, k=k, E=E)
+
+
+def _lora_run(c, bf16):
+    gu, h, yp, zg, zd = O.expert_ffn_fwd_lora(c["x_perm"], c["offsets"], c["w_gu"], c["w_down"],
+                                              c["w_perm"], c["a_gu"], c["b_gu"], c["a_dn"],
+                                              c["b_dn"], c["scale"], bf16)
+    y = O.combine(yp, c["s2r"], c["T"], c["k"], bf16)
+    dyp = O.combine_bwd(c["dy"], c["s2r"], c["k"])
+    b = O.expert_ffn_bwd_lora(c["x_perm"], gu, c["offsets"], c["w_gu"], c["w_down"], c["w_perm"],
+                              dyp, c["a_gu"], c["b_gu"], c["a_dn"], c["b_dn"], c["scale"], zg, zd,
+                              bf16)
+    dx = O.permute_bwd(b["dx_perm"], c["s2r"], c["T"], c["k"], None, bf16)
+    return dict(gu=gu, h=h, y_perm=yp, y=y, z_gu=zg, z_dn=zd, dx=dx, **b)
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def test_lora_with_zero_b_is_the_plain_block():
+    c = _lora_case(zero_b=True)
+    for bf16 in (False, True):
+        lo = _lora_run(c, bf16)
+        gu, h, yp = O.expert_ffn_fwd(c["x_perm"], c["offsets"], c["w_gu"], c["w_down"],
+                                     c["w_perm"], bf16)
+        np.testing.assert_array_equal(lo["gu"], gu)
+        np.testing.assert_array_equal(lo["y_perm"], yp)
+        dyp = O.combine_bwd(c["dy"], c["s2r"], c["k"])
+        pb = O.expert_ffn_bwd(c["x_perm"], gu, c["offsets"], c["w_gu"], c["w_down"], c["w_perm"],
+                              dyp, bf16)
+        for n in ("dgu", "dx_perm", "d_row_scale"):
+            np.testing.assert_array_equal(lo[n], pb[n])
+        assert not lo["da_gu"].any() and not lo["da_dn"].any()      # no path through B = 0
+        assert lo["db_gu"].any() and lo["db_dn"].any()
+
+
+def test_lora_forward_is_the_merged_weight_block():
+    c = _lora_case()
+    lo = _lora_run(c, False)
+    s = c["scale"]
+    wg = (c["w_gu"].astype(np.float64) + s * c["b_gu"].astype(np.float64) @ c["a_gu"].astype(np.float64))
+    wd = (c["w_down"].astype(np.float64) + s * c["b_dn"].astype(np.float64) @ c["a_dn"].astype(np.float64))
+    gu, h, yp = O.expert_ffn_fwd(c["x_perm"], c["offsets"], wg, wd, c["w_perm"], False)
+    assert _rel(lo["gu"], gu) < 1e-6 and _rel(lo["y_perm"], yp) < 1e-6
+
+
+def test_lora_gradients_match_torch_autograd():
+    c = _lora_case()
+    lo = _lora_run(c, False)
+    T, E, k = c["T"], c["E"], c["k"]
+    gate = np.zeros((T, E))
+    np.put_along_axis(gate, c["idx"].astype(np.int64), c["tw"].astype(np.float64), axis=1)
+    ref = brute.torch_dense_lora(c["x"], c["w_gu"], c["w_down"], c["a_gu"], c["b_gu"], c["a_dn"],
+                                 c["b_dn"], c["scale"], gate, c["dy"])
+    assert _rel(lo["y"], ref["y"]) < 1e-6
+    for n in ("dx", "da_gu", "db_gu", "da_dn", "db_dn"):
+        assert _rel(lo[n], ref[n]) < 1e-5, (n, _rel(lo[n], ref[n]))
