@@ -188,6 +188,48 @@ int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int dtype,
 int moe_permute_bwd(const void *dx_perm, const int32_t *slot_to_row, const float *dx_add,
                     int dtype, int64_t T, int d, int k, void *dx, void *stream);
 
+/* ---------------------------------------------------------------- grouped LoRA */
+
+/*
+ * LoRA on the fused expert weights with the experts frozen ("Halo:
+ * Frontier-Lab Training for Everyone", section "One trainer architecture, one
+ * parallelism stack": a grouped LoRA that adapts the 3-D expert tensors
+ * directly, so the frozen experts need no gradients).  Per expert e, rank r,
+ * scale s: W_gu[e] + s B_gu[e] A_gu[e] and W_down[e] + s B_dn[e] A_dn[e] with
+ * a_gu [E,r,d], b_gu [E,2f,r] (gate rows then up rows), a_dn [E,r,f],
+ * b_dn [E,d,r], all bf16, caller-owned device memory.  r is a multiple of 16,
+ * 16 <= r <= 64; dtype must be MOE_BF16; other shapes, errors and conventions
+ * as moe_grouped_ffn_fwd / _bwd.  Stored intermediates (bf16, [R,r]):
+ *   z_gu = store(s X_perm A_gu^T),  z_dn = store(s H A_dn^T)      (forward outputs)
+ * forward:  GU = store(X_perm W_gu^T + z_gu B_gu^T) (one fp32 accumulation:
+ *           the rank-r product is one more K stage of the grouped GEMM),
+ *           H = store(silu(g) u),  Y_perm = store(w (H W_down^T + z_dn B_dn^T)).
+ * backward: u_dn = store(s dY_perm B_dn);  Gd = dY_perm W_down + u_dn A_dn
+ *           feeds the dSwiGLU epilogue and d_row_scale as in moe_grouped_ffn_bwd;
+ *           u_gu = store(s dGU B_gu);  dX_perm = store(dGU W_gu + u_gu A_gu);
+ *           dB_gu = dGU^T z_gu [E,2f,r], dA_gu = u_gu^T X_perm [E,r,d],
+ *           dB_dn = S^T z_dn [E,d,r] (S = store(w dY_perm)),
+ *           dA_dn = store(w u_dn)^T H [E,r,f]; fp32, fully written (zeros for
+ *           empty experts).  No expert weight gradients are formed.
+ * ws: moe_grouped_ffn_lora_workspace_size(R,E,d,f,r) bytes for either call.
+ */
+size_t moe_grouped_ffn_lora_workspace_size(int64_t R, int E, int d, int f, int r);
+int moe_grouped_ffn_fwd_lora(const void *x_perm, const int32_t *offsets, int E, int64_t R, int d,
+                             int f, const void *w_gu, const void *w_down, const float *row_scale,
+                             const void *a_gu, const void *b_gu, const void *a_dn,
+                             const void *b_dn, int r, float scale, int dtype, void *z_gu,
+                             void *z_dn, void *gu, void *h, void *y_perm, void *ws,
+                             size_t ws_bytes, void *stream);
+int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, const void *h,
+                             const int32_t *offsets, int E, int64_t R, int d, int f,
+                             const void *w_gu, const void *w_down, const float *row_scale,
+                             const void *dy_perm, const void *a_gu, const void *b_gu,
+                             const void *a_dn, const void *b_dn, int r, float scale,
+                             const void *z_gu, const void *z_dn, int dtype, void *dgu,
+                             void *dx_perm, float *d_row_scale, float *da_gu, float *db_gu,
+                             float *da_dn, float *db_dn, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /*
  * moe_permute_bwd with the router's share of the token gradient formed in the
  * same pass instead of read from memory:
@@ -319,7 +361,7 @@ int moe_aux_loss(const float *logits, const int32_t *load, int64_t T, int64_t n_
  * gg_bwd_dw_down, gg_bwd_dw_gate_up, route_bwd, router_dx, router_dw_partial,
  * router_dw_reduce, router_dw_zero, permute_bwd, ffn_gu_f32, ffn_down_f32,
  * route_topk_biased, expert_load, expert_load_reduce, bias_update, aux_loss,
- * aux_loss_final.
+ * aux_loss_final, lora_proj, lora_transpose, lora_grad.
  */
 int moe_timing_enable(int on);
 int moe_timing_reset(void);

@@ -63,6 +63,18 @@ _SIGS = {
     "moe_aux_loss_workspace_size": (_sz, [_i64, _i32]),
     "moe_aux_loss": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i32, _i32, ctypes.c_float,
                             _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_lora_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "moe_grouped_ffn_fwd_lora": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _c_void_p, _i32, ctypes.c_float, _i32, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _sz, _c_void_p]),
+    "moe_grouped_ffn_bwd_lora": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
+                                        _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                        ctypes.c_float, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_void_p, _sz, _c_void_p]),
     "moe_timing_enable": (_i32, [_i32]),
     "moe_timing_reset": (_i32, []),
     "moe_timing_query": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -251,6 +263,34 @@ def moe_aux_loss(logits, load, n_valid, k, coeff, aux_out, d_logits, ws, stream=
     _check("moe_aux_loss", lib().moe_aux_loss(
         _p(logits), _p(load), T, n_valid, E, k, float(coeff), _p(aux_out), _p(d_logits), _p(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn_lora_workspace_size(R, E, d, f, r) -> int:
+    return int(lib().moe_grouped_ffn_lora_workspace_size(R, E, d, f, r))
+
+
+def moe_grouped_ffn_fwd_lora(x_perm, offsets, E, w_gu, w_down, row_scale, a_gu, b_gu, a_dn, b_dn,
+                             scale, z_gu, z_dn, gu, h, y_perm, ws, stream=None):
+    R, d = x_perm.shape
+    f = w_down.shape[2]
+    r = a_gu.shape[1]
+    _check("moe_grouped_ffn_fwd_lora", lib().moe_grouped_ffn_fwd_lora(
+        _p(x_perm), _p(offsets), E, R, d, f, _p(w_gu), _p(w_down), _p(row_scale), _p(a_gu),
+        _p(b_gu), _p(a_dn), _p(b_dn), r, float(scale), _dtype_code(x_perm), _p(z_gu), _p(z_dn),
+        _p(gu), _p(h), _p(y_perm), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn_bwd_lora(x_perm, gu, h, offsets, E, w_gu, w_down, row_scale, dy_perm, a_gu,
+                             b_gu, a_dn, b_dn, scale, z_gu, z_dn, dgu, dx_perm, d_row_scale,
+                             da_gu, db_gu, da_dn, db_dn, ws, stream=None):
+    R, d = x_perm.shape
+    f = w_down.shape[2]
+    r = a_gu.shape[1]
+    _check("moe_grouped_ffn_bwd_lora", lib().moe_grouped_ffn_bwd_lora(
+        _p(x_perm), _p(gu), _p(h), _p(offsets), E, R, d, f, _p(w_gu), _p(w_down), _p(row_scale),
+        _p(dy_perm), _p(a_gu), _p(b_gu), _p(a_dn), _p(b_dn), r, float(scale), _p(z_gu), _p(z_dn),
+        _dtype_code(w_gu), _p(dgu), _p(dx_perm), _p(d_row_scale), _p(da_gu), _p(db_gu),
+        _p(da_dn), _p(db_dn), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_timing_enable(on: bool):

@@ -45,6 +45,13 @@ struct GemmArgs {
   // outputs
   bf16_t *o_gu, *o_h, *o_y, *o_dgu, *o_dx;
   float *o_dw, *o_drs;         // dw: [E, Qdim, Pdim]; drs partials [R, PT*WP]
+  // grouped LoRA (token GEMMs with one extra K stage of width lora_r):
+  //   FWD_GU   P: B_gu [E,2f,r] rows   Q: z_gu [R,r] rows
+  //   FWD_DOWN P: B_dn [E,d,r] rows    Q: z_dn [R,r] rows
+  //   BWD_DH   P: A_dn [E,r,f] (transposed, like W_down)   Q: u_dn [R,r] rows
+  //   BWD_DX   P: A_gu [E,r,d] (transposed, like W_gu)     Q: u_gu [R,r] rows
+  const bf16_t *lora_p, *lora_q;
+  int lora_r;
   int E, d, f;
   int PT;                      // tiles along P
   int QT;                      // tiles along Q (weight-gradient kinds)
@@ -332,12 +339,14 @@ struct Tile {
   int e, seg0, Me, p_tile, q_tile, p0, q0, nk;
   const bf16_t *pb, *pb2, *qb;
   int pld, prv, pkv, qld, qrv, qkv;
+  const bf16_t *lpb, *lpb2, *lqb;   // LoRA stage operands (last stage of the tile)
+  int lpld;
 };
 
 
 // Logical tile L -> Tile.  s_off / s_ts: offsets[E+1] and tile_start[E+1]
 // staged in LDS.
-template <int KIND, int BP, int BQ, int BK>
+template <int KIND, int BP, int BQ, int BK, bool LORA = false>
 __device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, const int *s_ts,
                                           int L) {
   using KT = KindTraits<KIND>;
@@ -413,6 +422,22 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, c
   }
   if (!t.pb2) t.pb2 = t.pb;
   t.nk = (K + BK - 1) / BK;
+  if constexpr (LORA) {
+    // one more K stage: the rank-r product with the LoRA factors
+    const int r = a.lora_r;
+    t.lqb = a.lora_q + ((int64_t)seg0 + q0) * r;
+    if (KIND == FWD_GU) {
+      const bf16_t *B = a.lora_p + (int64_t)e * f2 * r;
+      t.lpb = B + (int64_t)p0 * r; t.lpb2 = B + ((int64_t)f + p0) * r; t.lpld = r;
+    } else if (KIND == FWD_DOWN) {
+      t.lpb = a.lora_p + ((int64_t)e * d + p0) * r; t.lpb2 = t.lpb; t.lpld = r;
+    } else if (KIND == BWD_DH) {
+      t.lpb = a.lora_p + (int64_t)e * r * f + p0; t.lpb2 = t.lpb; t.lpld = f;
+    } else {   // BWD_DX
+      t.lpb = a.lora_p + (int64_t)e * r * d + p0; t.lpb2 = t.lpb; t.lpld = d;
+    }
+    t.nk += 1;
+  }
   return t;
 }
 
@@ -627,7 +652,7 @@ __device__ __forceinline__ void mfma_block(f32x4_t (&acc)[FP][FQ], const bf16x8_
 // the loads of stage n+NS), the wave reads stage n+1's fragments between the
 // MFMAs of stage n.  After a tile's epilogue, the next tile's first MFMAs are
 // issued before the wait, so the epilogue's stores drain under them.
-template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false>
 __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   using KT = KindTraits<KIND>;
   constexpr int NW = WP * WQ;
@@ -739,11 +764,11 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   int iL = first, ikt = 0, iseq = 0;
   bool ivalid = iL < cend;
   Tile it{};
-  if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);
+  if (ivalid) it = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, iL);
   while (ivalid && it.nk == 0) {
     iL += per;
     ivalid = iL < cend;
-    if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);
+    if (ivalid) it = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, iL);
   }
   int s_issued = 0, s_done = 0;
 
@@ -756,7 +781,18 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   uint32_t mP = dummy, mQ = dummy, stepP = 0, stepQ = 0;
 #define MOE_PLAN()                                                                            \
   do {                                                                                        \
-    if (ivalid) {                                                                             \
+    if (ivalid && LORA && ikt == it.nk - 1) {                                                 \
+      /* the LoRA stage: both operands through the general path, K = lora_r */                \
+      u32x4_t *st_ = smem + ((unsigned)s_issued % NS) * SS;                                   \
+      issue_stage<BP, KT::PT_, KT::PAIRED, NW, BK>(it.lpb, it.lpb2, it.lpld, it.prv,          \
+                                                   a.lora_r, 0, st_, wave, lane);             \
+      issue_stage<BQ, KT::QT_, false, NW, BK>(it.lqb, it.lqb, a.lora_r, it.qrv, a.lora_r, 0,  \
+                                              st_ + SP, wave, lane);                          \
+      rsP = make_rsrc(a.offsets, 0);                                                          \
+      rsQ = rsP;                                                                              \
+      mP = mQ = dummy;                                                                        \
+      stepP = stepQ = 0;                                                                      \
+    } else if (ivalid) {                                                                      \
       u32x4_t *st_ = smem + ((unsigned)s_issued % NS) * SS;                                   \
       plan_operand<BP, KT::PT_, KT::PAIRED, NW, BK>(it.pb, it.pb2, pld, it.prv, it.pkv,       \
                                                     ikt * BK, st_, wave, lane, dummy, rsP,    \
@@ -788,14 +824,14 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
           do {                                                                                \
             iL += per;                                                                        \
             ivalid = iL < cend;                                                               \
-            if (ivalid) it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);                 \
+            if (ivalid) it = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, iL);                 \
           } while (ivalid && it.nk == 0);                                                     \
         } else {                                                                              \
           ++iseq;                                                                             \
           iL = __builtin_amdgcn_readfirstlane(s_ring[iseq & 15]);                             \
           ivalid = iL >= 0;                                                                   \
           if (ivalid) {                                                                       \
-            it = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, iL);                             \
+            it = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, iL);                             \
             if (tid == 0) s_ring[(iseq + NS) & 15] = MOE_FETCH();                             \
           }                                                                                   \
         }                                                                                     \
@@ -818,12 +854,12 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   int cL = first, cseq = 0;
   bool cvalid = cL < cend;
   Tile ct{};
-  if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+  if (cvalid) ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
   while (cvalid && ct.nk == 0) {   // experts with no rows: zero weight gradients
     epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
     cL += per;
     cvalid = cL < cend;
-    if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+    if (cvalid) ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
   }
   // live Q fragments of this wave in the current tile (a prefix)
   int nlive = cvalid ? live_frags<KT::WG, FQ>(ct.q0 + qrow0, ct.Me) : 0;
@@ -958,7 +994,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
         cL += per;
         cvalid = cL < cend;
         if (cvalid) {
-          ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+          ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
           if (ct.nk == 0) epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
         }
       } while (cvalid && ct.nk == 0);
@@ -966,7 +1002,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       ++cseq;
       cL = __builtin_amdgcn_readfirstlane(s_ring[cseq & 15]);
       cvalid = cL >= 0;
-      if (cvalid) ct = make_tile<KIND, BP, BQ, BK>(a, s_off, s_ts, cL);
+      if (cvalid) ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
     }
     if (cvalid) {
       nlive = live_frags<KT::WG, FQ>(ct.q0 + qrow0, ct.Me);
@@ -1107,6 +1143,196 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ 
   for (int v = 0; v < 4; ++v) y[r * d + n + v] = w * acc[v];
 }
 
+// ------------------------------------------------------------------ grouped LoRA
+//
+// Rank-r products of the LoRA factors over the rows of each expert (r a
+// multiple of 16, at most 64).  The K-wide contractions of the block itself
+// run in the grouped GEMMs above as one more K stage; these kernels form the
+// r-wide operands and the factor gradients.
+
+constexpr int kLoraMaxRank = 64;
+
+// out[row, i] = store(s * sum_c in[row, c] * F[e][i][c]) for the rows of each
+// expert e (F: [E, r, K], K contiguous); with w_out also
+// out_w[row, i] = store(w[row] * out[row, i]).  One block (4 waves) per tile
+// of 16 rows of one expert; wave w takes the 32-wide k steps w, w+4, ...;
+// MFMA operands straight from global memory (16 bytes per lane); the four
+// partial 16 x r tiles are summed in wave order through LDS.
+template <int R>
+__global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in,
+                                                   const bf16_t *__restrict__ F,
+                                                   const int32_t *__restrict__ offsets,
+                                                   const int32_t *__restrict__ ts, int E, int K,
+                                                   float scale, const float *__restrict__ w,
+                                                   bf16_t *__restrict__ out,
+                                                   bf16_t *__restrict__ out_w) {
+  constexpr int NR = R / 16;
+  __shared__ float red[4][16][R];
+  const int tile = blockIdx.x;
+  if (tile >= ts[E]) return;
+  int lo = 0, hi = E;   // largest e with ts[e] <= tile
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ts[mid] <= tile) lo = mid; else hi = mid;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(lo);
+  const int seg0 = offsets[e], Me = offsets[e + 1] - seg0;
+  const int r0 = __builtin_amdgcn_readfirstlane((tile - ts[e]) * 16);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane & 15, ch = lane >> 4;
+  const bool rvalid = r0 + rr < Me;
+  const bf16_t *arow = in + ((int64_t)seg0 + r0 + (rvalid ? rr : 0)) * K + ch * 8;
+  const bf16_t *Fe = F + (int64_t)e * R * K + (int64_t)rr * K + ch * 8;
+  f32x4_t acc[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const int nsteps = (K + 31) / 32;
+  int st = wave;
+  for (; st + 12 < nsteps; st += 16) {   // four steps in flight
+    u32x4_t av[4], bv[4][NR];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = (st + 4 * u) * 32 + ch * 8;
+      const bool kv = k < K;
+      av[u] = (rvalid && kv) ? *reinterpret_cast<const u32x4_t *>(arow + (st + 4 * u) * 32) : zero;
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        bv[u][j] = kv ? *reinterpret_cast<const u32x4_t *>(Fe + (int64_t)j * 16 * K + (st + 4 * u) * 32)
+                      : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][j]),
+                                                         acc[j], 0, 0, 0);
+  }
+  for (; st < nsteps; st += 4) {
+    const int k = st * 32 + ch * 8;
+    const bool kv = k < K;
+    const u32x4_t av = (rvalid && kv) ? *reinterpret_cast<const u32x4_t *>(arow + st * 32) : zero;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const u32x4_t bv = kv ? *reinterpret_cast<const u32x4_t *>(Fe + (int64_t)j * 16 * K + st * 32)
+                            : zero;
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[j], 0, 0,
+                                                       0);
+    }
+  }
+  // lane holds rows 4*(lane/16) + v, rank 16*j + lane%16
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][4 * ch + v][16 * j + rr] = acc[j][v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * R; i += 256) {
+    const int row = i / R, rank = i % R;
+    if (r0 + row >= Me) continue;
+    const float v = ((red[0][row][rank] + red[1][row][rank]) + red[2][row][rank]) + red[3][row][rank];
+    const int64_t o = ((int64_t)seg0 + r0 + row) * R + rank;
+    const float z = round_bf16(scale * v);
+    out[o] = (bf16_t)f32_to_bf16_bits(z);
+    if (out_w) out_w[o] = (bf16_t)f32_to_bf16_bits(w[seg0 + r0 + row] * z);
+  }
+}
+
+// Ft[e][i][c] = F[e][c][i]  (F: [E, K, r] -> Ft: [E, r, K])
+__global__ __launch_bounds__(256) void k_lora_transpose(const bf16_t *__restrict__ F, int E, int K,
+                                                        int r, bf16_t *__restrict__ Ft) {
+  const int64_t n = (int64_t)E * K * r;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t e = i / ((int64_t)K * r);
+  const int64_t rem = i - e * K * r;
+  const int rank = (int)(rem / K), c = (int)(rem - (int64_t)rank * K);
+  Ft[i] = F[(e * K + c) * r + rank];
+}
+
+// LoRA factor gradient of expert e over its rows:
+//   G[c][i] = sum_{rows of e} M[row][c] * Z[row][i]     (M: [R, K], Z: [R, r])
+// stored as out[e][c][i] (KR) or out[e][i][c] (RK), fp32.  One block (4
+// waves) per (expert, 256-column slab of M); the rows of the expert are the
+// reduction, 32 per stage, both operands staged transposed into LDS by the
+// same direct loads as the weight-gradient GEMMs (Z padded to 128 columns,
+// the narrowest width whose transposed layout keeps the block swizzle inside
+// a k-row; columns past r are loaded but never used), double-buffered.  Wave w owns columns
+// 64w .. 64w+63 of the slab: 4 x (r/16) MFMA tiles.  Empty experts store zeros.
+template <int R, bool KR>
+__global__ __launch_bounds__(256) void k_lora_grad(const bf16_t *__restrict__ M,
+                                                   const bf16_t *__restrict__ Z,
+                                                   const int32_t *__restrict__ offsets, int E,
+                                                   int K, float *__restrict__ out) {
+  constexpr int BP = 256, BQ = 128, BK = 32, NW = 4, NS = 2;
+  constexpr int NR = R / 16;
+  constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;
+  constexpr int LOADS = BP * BK / 512 / NW + BQ * BK / 512 / NW;
+  __shared__ u32x4_t smem[NS * SS];
+  const LDS_AS char *lds = (const LDS_AS char *)smem;
+  const int nslab = (K + BP - 1) / BP;
+  const int e = blockIdx.x / nslab;
+  const int c0 = (blockIdx.x - e * nslab) * BP;
+  const int seg0 = offsets[e], Me = offsets[e + 1] - seg0;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  uint32_t rdP[4], rdQ[NR];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rdP[i] = tr_frag_off<BP>(wave * 64 + 16 * i, lane);
+#pragma unroll
+  for (int j = 0; j < NR; ++j) rdQ[j] = (uint32_t)(SP * 16) + tr_frag_off<BQ>(16 * j, lane);
+  f32x4_t acc[4][NR];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16_t *mb = M + (int64_t)seg0 * K + c0;
+  const bf16_t *zb = Z + (int64_t)seg0 * R;
+  const int nk = (Me + BK - 1) / BK;
+  auto issue = [&](int kt) {
+    u32x4_t *st = smem + (kt % NS) * SS;
+    issue_stage<BP, true, false, NW, BK>(mb, mb, K, K - c0, Me, kt * BK, st, wave, lane);
+    issue_stage<BQ, true, false, NW, BK>(zb, zb, R, R, Me, kt * BK, st + SP, wave, lane);
+  };
+  if (nk > 0) issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) {
+      issue(kt + 1);
+      wait_vm_lgkm0<LOADS>();
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    __builtin_amdgcn_s_barrier();   // stage kt landed for every wave
+    const LDS_AS char *sb = lds + (kt % NS) * (SS * 16);
+    bf16x8_t pf[4], qf[NR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = frag_at<true, false, BP, BK, 4>(sb, rdP, i, 0);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) qf[j] = frag_at<true, false, BQ, BK, NR>(sb, rdQ, j, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
+    wait_vm_lgkm0<63>();            // this wave's reads of stage kt are done
+    __builtin_amdgcn_s_barrier();   // before its buffer takes stage kt + 2
+  }
+  // lane holds column c0 + 64*wave + 16*i + 4*(lane/16) + v, rank 16*j + lane%16
+  float *oe = out + (int64_t)e * K * R;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = c0 + wave * 64 + 16 * i + 4 * (lane >> 4) + v;
+        const int rank = 16 * j + (lane & 15);
+        if (c < K) {
+          if (KR) oe[(int64_t)c * R + rank] = acc[i][j][v];
+          else oe[(int64_t)rank * K + c] = acc[i][j][v];
+        }
+      }
+}
+
 // ------------------------------------------------------------------ launch
 
 // tile configurations
@@ -1164,7 +1390,7 @@ static int launch_tile_prefix(const GemmArgs &a, int BQ, int PTa, int32_t *tsa, 
   return check_launch("tile_prefix");
 }
 
-template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false>
 static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start, const char *name,
                              hipStream_t s) {
   if (R == 0) return MOE_OK;
@@ -1173,7 +1399,8 @@ static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start,
   a.counters = tile_start + a.E + 1;
   const int64_t bound = ((R + BQ - 1) / BQ + a.E) * (int64_t)PT;
   const int grid = persistent_grid(bound);
-  MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK><<<grid, WP * WQ * 64, 0, s>>>(a)));
+  MOE_LAUNCH(name, s,
+             (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK, LORA><<<grid, WP * WQ * 64, 0, s>>>(a)));
   return check_launch(name);
 }
 
@@ -1355,4 +1582,266 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   a.o_dw = dw_gu;
   return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, d, 2 * f, "gg_bwd_dw_gate_up",
                                                                 s);
+}
+
+// ====================================================================== grouped LoRA
+
+static int check_lora(const char *fn, int r, float scale) {
+  MOE_REQUIRE(r >= 16 && r <= kLoraMaxRank && r % 16 == 0, MOE_ERR_UNSUPPORTED,
+              "%s: rank %d (a multiple of 16 up to %d)", fn, r, kLoraMaxRank);
+  MOE_REQUIRE(scale == scale && scale > -INFINITY && scale < INFINITY, MOE_ERR_INVALID_ARG,
+              "%s: scale must be finite", fn);
+  return MOE_OK;
+}
+
+// 16-row tile prefix, transposed B factors, u_dn, w*u_dn, u_gu after the
+// plain grouped-FFN workspace
+static size_t lora_extra_bytes(int64_t R, int E, int d, int f, int r) {
+  return tile_start_bytes(E) + align_up(2 * (size_t)E * r * d, 256) +
+         align_up(2 * (size_t)E * r * 2 * f, 256) + 3 * align_up(2 * (size_t)R * r, 256);
+}
+
+extern "C" size_t moe_grouped_ffn_lora_workspace_size(int64_t R, int E, int d, int f, int r) {
+  if (R < 0 || E < 1 || f < 1 || d < 1 || r < 1) return 0;
+  return moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16) + lora_extra_bytes(R, E, d, f, r);
+}
+
+template <int RK>
+static int launch_lora_proj(const bf16_t *in, const bf16_t *F, const int32_t *offsets,
+                            const int32_t *ts, int E, int64_t R, int K, float scale, const float *w,
+                            bf16_t *out, bf16_t *out_w, const char *name, hipStream_t s) {
+  const unsigned blocks = (unsigned)((R + 15) / 16 + E);   // bound on 16-row tiles
+  MOE_LAUNCH(name, s,
+             k_lora_proj<RK><<<blocks, 256, 0, s>>>(in, F, offsets, ts, E, K, scale, w, out, out_w));
+  return check_launch(name);
+}
+
+static int lora_proj(int r, const bf16_t *in, const bf16_t *F, const int32_t *offsets,
+                     const int32_t *ts, int E, int64_t R, int K, float scale, const float *w,
+                     bf16_t *out, bf16_t *out_w, const char *name, hipStream_t s) {
+  switch (r) {
+    case 16: return launch_lora_proj<16>(in, F, offsets, ts, E, R, K, scale, w, out, out_w, name, s);
+    case 32: return launch_lora_proj<32>(in, F, offsets, ts, E, R, K, scale, w, out, out_w, name, s);
+    case 48: return launch_lora_proj<48>(in, F, offsets, ts, E, R, K, scale, w, out, out_w, name, s);
+    default: return launch_lora_proj<64>(in, F, offsets, ts, E, R, K, scale, w, out, out_w, name, s);
+  }
+}
+
+template <int RK, bool KR>
+static int launch_lora_grad_t(const bf16_t *M, const bf16_t *Z, const int32_t *offsets, int E,
+                              int K, float *out, const char *name, hipStream_t s) {
+  const unsigned blocks = (unsigned)(E * ((K + 255) / 256));
+  MOE_LAUNCH(name, s, (k_lora_grad<RK, KR><<<blocks, 256, 0, s>>>(M, Z, offsets, E, K, out)));
+  return check_launch(name);
+}
+
+template <bool KR>
+static int lora_grad(int r, const bf16_t *M, const bf16_t *Z, const int32_t *offsets, int E, int K,
+                     float *out, const char *name, hipStream_t s) {
+  switch (r) {
+    case 16: return launch_lora_grad_t<16, KR>(M, Z, offsets, E, K, out, name, s);
+    case 32: return launch_lora_grad_t<32, KR>(M, Z, offsets, E, K, out, name, s);
+    case 48: return launch_lora_grad_t<48, KR>(M, Z, offsets, E, K, out, name, s);
+    default: return launch_lora_grad_t<64, KR>(M, Z, offsets, E, K, out, name, s);
+  }
+}
+
+extern "C" int moe_grouped_ffn_fwd_lora(const void *x_perm, const int32_t *offsets, int E,
+                                        int64_t R, int d, int f, const void *w_gu,
+                                        const void *w_down, const float *row_scale,
+                                        const void *a_gu, const void *b_gu, const void *a_dn,
+                                        const void *b_dn, int r, float scale, int dtype,
+                                        void *z_gu, void *z_dn, void *gu, void *h, void *y_perm,
+                                        void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_ffn("moe_grouped_ffn_fwd_lora", E, R, d, f, dtype);
+  if (rc) return rc;
+  rc = check_lora("moe_grouped_ffn_fwd_lora", r, scale);
+  if (rc) return rc;
+  MOE_REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_fwd_lora: needs MOE_BF16");
+  if (R == 0) return MOE_OK;
+  MOE_REQUIRE(x_perm && offsets && w_gu && w_down && a_gu && b_gu && a_dn && b_dn && z_gu &&
+                  z_dn && h && y_perm,
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_fwd_lora: null pointer");
+  MOE_REQUIRE(aligned16(x_perm) && aligned16(w_gu) && aligned16(w_down) && aligned16(a_gu) &&
+                  aligned16(b_gu) && aligned16(a_dn) && aligned16(b_dn) && aligned16(z_gu) &&
+                  aligned16(z_dn) && aligned16(h) && aligned16(y_perm) && (!gu || aligned16(gu)),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_fwd_lora: pointers must be 16-byte aligned");
+  const size_t need = moe_grouped_ffn_lora_workspace_size(R, E, d, f, r);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_grouped_ffn_fwd_lora: workspace %zu < %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *ts0 = (int32_t *)ws;
+  int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
+  int32_t *ts16 = (int32_t *)((char *)ws + moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16));
+  GemmArgs a{};
+  a.x_perm = (const bf16_t *)x_perm;
+  a.w_gu = (const bf16_t *)w_gu;
+  a.w_down = (const bf16_t *)w_down;
+  a.h = (const bf16_t *)h;
+  a.row_scale = row_scale;
+  a.offsets = offsets;
+  a.o_gu = (bf16_t *)gu;
+  a.o_h = (bf16_t *)h;
+  a.o_y = (bf16_t *)y_perm;
+  a.lora_r = r;
+  a.E = E;
+  a.d = d;
+  a.f = f;
+  const int pt_gu = (f + FWD_BP / 2 - 1) / (FWD_BP / 2), pt_dn = (d + DN_BP - 1) / DN_BP;
+  rc = launch_tile_prefix(a, FWD_BQ, pt_gu, ts0, pt_dn, ts1, s);
+  if (rc) return rc;
+  rc = launch_tile_prefix(a, 16, 1, ts16, 1, ts16, s);   // 16-row tiles of the projections
+  if (rc) return rc;
+  // z_gu = store(s X_perm A_gu^T); GU and H with the extra K stage z_gu . B_gu^T
+  rc = lora_proj(r, (const bf16_t *)x_perm, (const bf16_t *)a_gu, offsets, ts16, E, R, d, scale,
+                 nullptr, (bf16_t *)z_gu, nullptr, "lora_proj", s);
+  if (rc) return rc;
+  a.lora_p = (const bf16_t *)b_gu;
+  a.lora_q = (const bf16_t *)z_gu;
+  rc = launch_token_gemm<FWD_GU, FWD_BP, FWD_BQ, FWD_WP, FWD_WQ, FWD_NS, FWD_BK, true>(
+      a, R, pt_gu, ts0, "gg_fwd_gate_up_swiglu", s);
+  if (rc) return rc;
+  // z_dn = store(s H A_dn^T); Y_perm with the extra K stage z_dn . B_dn^T
+  rc = lora_proj(r, (const bf16_t *)h, (const bf16_t *)a_dn, offsets, ts16, E, R, f, scale,
+                 nullptr, (bf16_t *)z_dn, nullptr, "lora_proj", s);
+  if (rc) return rc;
+  a.lora_p = (const bf16_t *)b_dn;
+  a.lora_q = (const bf16_t *)z_dn;
+  return launch_token_gemm<FWD_DOWN, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK, true>(
+      a, R, pt_dn, ts1, "gg_fwd_down_scale", s);
+}
+
+extern "C" int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, const void *h,
+                                        const int32_t *offsets, int E, int64_t R, int d, int f,
+                                        const void *w_gu, const void *w_down,
+                                        const float *row_scale, const void *dy_perm,
+                                        const void *a_gu, const void *b_gu, const void *a_dn,
+                                        const void *b_dn, int r, float scale, const void *z_gu,
+                                        const void *z_dn, int dtype, void *dgu, void *dx_perm,
+                                        float *d_row_scale, float *da_gu, float *db_gu,
+                                        float *da_dn, float *db_dn, void *ws, size_t ws_bytes,
+                                        void *stream) {
+  clear_error();
+  int rc = check_ffn("moe_grouped_ffn_bwd_lora", E, R, d, f, dtype);
+  if (rc) return rc;
+  rc = check_lora("moe_grouped_ffn_bwd_lora", r, scale);
+  if (rc) return rc;
+  MOE_REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_bwd_lora: needs MOE_BF16");
+  MOE_REQUIRE(offsets && w_gu && w_down && a_gu && b_gu && a_dn && b_dn && da_gu && db_gu &&
+                  da_dn && db_dn,
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd_lora: null pointer");
+  MOE_REQUIRE(R == 0 || (x_perm && gu && h && dy_perm && z_gu && z_dn && dgu && dx_perm),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd_lora: null activation pointer");
+  MOE_REQUIRE(aligned16(w_gu) && aligned16(w_down) && aligned16(a_gu) && aligned16(b_gu) &&
+                  aligned16(a_dn) && aligned16(b_dn) &&
+                  (R == 0 || (aligned16(x_perm) && aligned16(gu) && aligned16(h) &&
+                              aligned16(dy_perm) && aligned16(z_gu) && aligned16(z_dn) &&
+                              aligned16(dgu) && aligned16(dx_perm))),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd_lora: pointers must be 16-byte aligned");
+  const size_t need = moe_grouped_ffn_lora_workspace_size(R, E, d, f, r);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_grouped_ffn_bwd_lora: workspace %zu < %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  char *wb = (char *)ws;
+  int32_t *ts0 = (int32_t *)wb;
+  int32_t *ts1 = (int32_t *)(wb + tile_start_bytes(E));
+  float *drs_part = (float *)(wb + 2 * tile_start_bytes(E));
+  bf16_t *s_perm = (bf16_t *)(wb + 2 * tile_start_bytes(E) + drs_bytes(R, f));
+  char *lw = wb + moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16);
+  int32_t *ts16 = (int32_t *)lw;
+  lw += tile_start_bytes(E);
+  bf16_t *b_dn_t = (bf16_t *)lw;   // [E, r, d]
+  lw += align_up(2 * (size_t)E * r * d, 256);
+  bf16_t *b_gu_t = (bf16_t *)lw;   // [E, r, 2f]
+  lw += align_up(2 * (size_t)E * r * 2 * f, 256);
+  bf16_t *u_dn = (bf16_t *)lw;
+  lw += align_up(2 * (size_t)R * r, 256);
+  bf16_t *uw_dn = (bf16_t *)lw;
+  lw += align_up(2 * (size_t)R * r, 256);
+  bf16_t *u_gu = (bf16_t *)lw;
+  GemmArgs a{};
+  a.x_perm = (const bf16_t *)x_perm;
+  a.w_gu = (const bf16_t *)w_gu;
+  a.w_down = (const bf16_t *)w_down;
+  a.h = (const bf16_t *)h;
+  a.gu = (const bf16_t *)gu;
+  a.dy_perm = (const bf16_t *)dy_perm;
+  a.dgu = (const bf16_t *)dgu;
+  a.row_scale = row_scale;
+  a.offsets = offsets;
+  a.o_dgu = (bf16_t *)dgu;
+  a.o_dx = (bf16_t *)dx_perm;
+  a.o_drs = drs_part;
+  a.lora_r = r;
+  a.E = E;
+  a.d = d;
+  a.f = f;
+  // B factors with K contiguous for the projections
+  {
+    const int64_t n1 = (int64_t)E * d * r, n2 = (int64_t)E * 2 * f * r;
+    MOE_LAUNCH("lora_transpose", s,
+               k_lora_transpose<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
+                   (const bf16_t *)b_dn, E, d, r, b_dn_t));
+    MOE_LAUNCH("lora_transpose", s,
+               k_lora_transpose<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
+                   (const bf16_t *)b_gu, E, 2 * f, r, b_gu_t));
+    rc = check_launch("moe_grouped_ffn_bwd_lora(transpose)");
+    if (rc) return rc;
+  }
+  const int pt_dh = (f + DH_BP - 1) / DH_BP, pt_dx = (d + DX_BP - 1) / DX_BP;
+  if (R > 0) {
+    rc = launch_tile_prefix(a, DH_BQ, pt_dh, ts0, pt_dx, ts1, s);
+    if (rc) return rc;
+    rc = launch_tile_prefix(a, 16, 1, ts16, 1, ts16, s);
+    if (rc) return rc;
+    // u_dn = store(s dY_perm B_dn), w * u_dn stored too
+    rc = lora_proj(r, (const bf16_t *)dy_perm, b_dn_t, offsets, ts16, E, R, d, scale, row_scale
+                   ? row_scale : nullptr, u_dn, row_scale ? uw_dn : nullptr, "lora_proj", s);
+    if (rc) return rc;
+    if (!row_scale) uw_dn = u_dn;
+  }
+  // 1. dGU (and d_row_scale partials): dY_perm W_down + u_dn A_dn
+  a.lora_p = (const bf16_t *)a_dn;
+  a.lora_q = u_dn;
+  rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ, DH_NS, DH_BK, true>(
+      a, R, pt_dh, ts0, "gg_bwd_dh_dswiglu", s);
+  if (rc) return rc;
+  if (d_row_scale && R > 0) {
+    MOE_LAUNCH("drs_reduce", s,
+               k_drs_reduce<<<(unsigned)((R + 255) / 256), 256, 0, s>>>(drs_part, pt_dh * DH_WP, R,
+                                                                       d_row_scale));
+    rc = check_launch("moe_grouped_ffn_bwd_lora(drs)");
+    if (rc) return rc;
+  }
+  // 2. u_gu = store(s dGU B_gu); dX_perm = dGU W_gu + u_gu A_gu
+  if (R > 0) {
+    rc = lora_proj(r, (const bf16_t *)dgu, b_gu_t, offsets, ts16, E, R, 2 * f, scale, nullptr,
+                   u_gu, nullptr, "lora_proj", s);
+    if (rc) return rc;
+  }
+  a.lora_p = (const bf16_t *)a_gu;
+  a.lora_q = u_gu;
+  rc = launch_token_gemm<BWD_DX, DX_BP, DX_BQ, DX_WP, DX_WQ, DX_NS, DX_BK, true>(
+      a, R, pt_dx, ts1, "gg_bwd_dx", s);
+  if (rc) return rc;
+  // 3. S = store(w dY_perm) for dB_dn
+  if (R > 0) {
+    const int64_t n = R * (d / 8);
+    MOE_LAUNCH("row_scale", s,
+               k_row_scale<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+                   (const bf16_t *)dy_perm, row_scale, R, d, s_perm));
+    rc = check_launch("moe_grouped_ffn_bwd_lora(row scale)");
+    if (rc) return rc;
+  }
+  // 4. factor gradients (fp32): dB_gu = dGU^T z_gu, dA_gu = u_gu^T X_perm,
+  //    dB_dn = S^T z_dn, dA_dn = store(w u_dn)^T H
+  rc = lora_grad<true>(r, (const bf16_t *)dgu, (const bf16_t *)z_gu, offsets, E, 2 * f, db_gu,
+                       "lora_grad", s);
+  if (rc) return rc;
+  rc = lora_grad<false>(r, (const bf16_t *)x_perm, u_gu, offsets, E, d, da_gu, "lora_grad", s);
+  if (rc) return rc;
+  rc = lora_grad<true>(r, s_perm, (const bf16_t *)z_dn, offsets, E, d, db_dn, "lora_grad", s);
+  if (rc) return rc;
+  return lora_grad<false>(r, (const bf16_t *)h, uw_dn, offsets, E, f, da_dn, "lora_grad", s);
 }

@@ -309,7 +309,8 @@ def expert_ffn_bwd(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, bf16=T
 #   u_gu = store(s * dGU B_gu)                    [R, r]
 #   dX_perm = store(dGU W_gu + u_gu A_gu)
 #   dB_gu = dGU^T z_gu, dA_gu = u_gu^T X_perm, dB_dn = S^T z_dn with
-#   S = store(w * dY_perm), dA_dn = (w * u_dn)^T H   (fp32 outputs)
+#   S = store(w * dY_perm), dA_dn = store(w * u_dn)^T H   (fp32 outputs;
+#   the row-weighted u_dn is stored like S, the row-weighted dY)
 
 def _ffn_rows_lora(xr, w_gu_e, w_down_e, wr, a_gu_e, b_gu_e, a_dn_e, b_dn_e, scale, bf16):
     f = w_gu_e.shape[0] // 2
@@ -395,7 +396,7 @@ def expert_ffn_bwd_lora(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, a
         out["db_gu"][e] = (_f64(dgu).T @ _f64(z_gu[a:b])).astype(np.float32)
         out["da_gu"][e] = (_f64(u_gu).T @ _f64(xr)).astype(np.float32)
         out["db_dn"][e] = (_f64(s_).T @ _f64(z_dn[a:b])).astype(np.float32)
-        out["da_dn"][e] = ((w[:, None] * _f64(u_dn)).T @ _f64(h)).astype(np.float32)
+        out["da_dn"][e] = (_f64(store(w[:, None] * _f64(u_dn), bf16)).T @ _f64(h)).astype(np.float32)
     return out
 
 

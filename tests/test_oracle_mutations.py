@@ -54,7 +54,7 @@ MUTATIONS = [
      "u_dn = store((_f64(dyr) @ _f64(b_dn[e])), bf16)"),
     ("LoRA term missing from dX", "dx = store(_f64(dgu) @ _f64(w_gu[e]) + _f64(u_gu) @ _f64(a_gu[e]), bf16)",
      "dx = store(_f64(dgu) @ _f64(w_gu[e]), bf16)"),
-    ("LoRA dA_dn without the row weight", "((w[:, None] * _f64(u_dn)).T @ _f64(h))",
+    ("LoRA dA_dn without the row weight", "(_f64(store(w[:, None] * _f64(u_dn), bf16)).T @ _f64(h))",
      "(_f64(u_dn).T @ _f64(h))"),
     ("LoRA dB_dn from dY instead of S", "(_f64(s_).T @ _f64(z_dn[a:b]))", "(_f64(dyr).T @ _f64(z_dn[a:b]))"),
     ("LoRA down term added after the row weight",
