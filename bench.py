@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--profile-steps", type=int, default=5,
                     help="extra steps with per-kernel event timing")
+    ap.add_argument("--lora-rank", type=int, default=16,
+                    help="also time the step with frozen experts and rank-r LoRA (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (reference for HBM "
                          "byte counters)")
@@ -231,6 +233,48 @@ def main():
                                "hbm_frac": round(vb[n] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         abi.moe_timing_reset()
 
+    # the same step with the experts frozen and rank-r LoRA factors on both
+    # expert matrices (grouped LoRA): the expert weight gradients are replaced
+    # by the LoRA factor gradients
+    lora_out = None
+    if args.lora_rank > 0:
+        lf = I.make_lora_factors(w, args.lora_rank)
+        lora = tuple(up(lf[n]) for n in ("a_gu", "b_gu", "a_dn", "b_dn"))
+        lblk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev,
+                        lora_rank=args.lora_rank, lora_scale=1.0)
+
+        def lstep():
+            lblk.forward(x, wr, wgu, wd, bias, noise, lora=lora)
+            lblk.backward(x, wr, wgu, wd, dy, lora=lora)
+
+        for _ in range(max(2, args.warmup)):
+            lstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            lstep()
+        torch.cuda.synchronize()
+        lel = time.perf_counter() - t0
+        lk = {}
+        if args.profile_steps > 0:
+            abi.moe_timing_reset()
+            abi.moe_timing_enable(True)
+            for _ in range(args.profile_steps):
+                lstep()
+            torch.cuda.synchronize()
+            abi.moe_timing_enable(False)
+            for n in ("lora_proj", "lora_transpose", "lora_grad", "gg_fwd_gate_up_swiglu",
+                      "gg_fwd_down_scale", "gg_bwd_dh_dswiglu", "gg_bwd_dx"):
+                ms, cnt = abi.moe_timing_query(n)
+                if cnt:
+                    lk[n] = round(1e3 * ms / args.profile_steps, 1)
+            abi.moe_timing_reset()
+        lora_out = {"rank": args.lora_rank, "ms_per_step": round(lel * 1e3 / args.steps, 4),
+                    "tokens_per_s": round(w.T * args.steps / lel, 1),
+                    "speedup_vs_full_step": round(elapsed / lel, 3),
+                    "kernels_us_per_step": lk}
+        del lblk
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -303,6 +347,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
         "router_variants": variants,
+        "lora": lora_out,
     }
     print(json.dumps(out), flush=True)
 

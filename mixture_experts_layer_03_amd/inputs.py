@@ -147,8 +147,10 @@ def make_lora_factors(w: Workload, r: int, seed: Optional[int] = None) -> Dict[s
     """LoRA factors for the fused expert weights of workload ``w`` (rank r),
     drawn from their own stream (seed + 7919) in the order A_gu, B_gu, A_dn,
     B_dn: A ~ N(0,1)/sqrt(fan_in) (d for the gate/up factor, f for the down
-    one), B ~ N(0,1)/sqrt(r) (nonzero, so that every LoRA path carries
-    signal; training would start B at zero).  Shapes: a_gu[E,r,d],
+    one), B ~ N(0,1)/(4 sqrt(r)): nonzero, so that every LoRA path carries
+    signal (training would start B at zero), and a quarter of the base
+    weights' scale, so that the adapted layer keeps the base layer's
+    magnitudes, as a trained adapter does.  Shapes: a_gu[E,r,d],
     b_gu[E,2f,r], a_dn[E,r,f], b_dn[E,d,r]; bf16-exact for bf16 workloads."""
     seed = (w.seed if seed is None else seed) + 7919
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -156,7 +158,7 @@ def make_lora_factors(w: Workload, r: int, seed: Optional[int] = None) -> Dict[s
     E, d, f = w.E, w.d, w.f
     return {
         "a_gu": _normal(rng, (E, r, d), 1.0 / math.sqrt(d), bf16),
-        "b_gu": _normal(rng, (E, 2 * f, r), 1.0 / math.sqrt(r), bf16),
+        "b_gu": _normal(rng, (E, 2 * f, r), 0.25 / math.sqrt(r), bf16),
         "a_dn": _normal(rng, (E, r, f), 1.0 / math.sqrt(f), bf16),
-        "b_dn": _normal(rng, (E, d, r), 1.0 / math.sqrt(r), bf16),
+        "b_dn": _normal(rng, (E, d, r), 0.25 / math.sqrt(r), bf16),
     }

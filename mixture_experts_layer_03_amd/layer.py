@@ -14,6 +14,11 @@ on one stream, with no host synchronisation in between:
             stores dx_router and moe_permute_bwd adds it)
   balance : moe_expert_load -> moe_bias_update (selection-bias step)
 
+With ``lora_rank`` set the experts are frozen and carry LoRA factors:
+moe_grouped_ffn_fwd_lora / moe_grouped_ffn_bwd_lora replace the grouped-FFN
+calls, and the backward forms the LoRA factor gradients instead of the expert
+weight gradients.
+
 This mirrors the EP forward path the pages describe (router logits in fp32,
 per-token top-k, tokens sorted by expert, grouped matmul, rows returned and
 weighted by the top-k probabilities: "Halo's 2.8x over TRL is not a kernel,
@@ -31,9 +36,11 @@ from . import abi
 
 class MoEBlock:
     def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype=torch.bfloat16,
-                 device="cuda", backward: bool = True, fuse_router_dx: bool = True):
+                 device="cuda", backward: bool = True, fuse_router_dx: bool = True,
+                 lora_rank: int = 0, lora_scale: float = 1.0):
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.fuse_router_dx = fuse_router_dx
+        self.lora_rank, self.lora_scale = lora_rank, lora_scale
         self.R = T * k
         self.dtype = dtype
         self.device = device
@@ -61,6 +68,10 @@ class MoEBlock:
         ws_rtr = abi.moe_router_logits_bwd_workspace_size(T, d, E) if backward else 0
         ws_stat = max(abi.moe_expert_load_workspace_size(T, E, k),
                       abi.moe_aux_loss_workspace_size(T, E))
+        if lora_rank:
+            ws_ffn = abi.moe_grouped_ffn_lora_workspace_size(R, E, d, f, lora_rank)
+            self.z_gu = z(R, lora_rank)
+            self.z_dn = z(R, lora_rank)
         self.ws = torch.empty(max(ws_perm, ws_ffn, ws_rtr, ws_stat, 256), dtype=torch.uint8,
                               device=device)
         self.load = z(E, dt=i32)
@@ -76,12 +87,18 @@ class MoEBlock:
             # the router's fp32 dX is only stored when it is not fused into dX
             self.dx_router = None if fuse_router_dx else z(T, d, dt=f32)
             self.dw_r = z(E, d, dt=f32)
-            self.dw_gu = z(E, 2 * f, d, dt=f32)
-            self.dw_down = z(E, d, f, dt=f32)
+            if lora_rank:   # frozen experts: LoRA factor gradients only
+                r = lora_rank
+                self.da_gu, self.db_gu = z(E, r, d, dt=f32), z(E, 2 * f, r, dt=f32)
+                self.da_dn, self.db_dn = z(E, r, f, dt=f32), z(E, d, r, dt=f32)
+            else:
+                self.dw_gu = z(E, 2 * f, d, dt=f32)
+                self.dw_down = z(E, d, f, dt=f32)
             self.dx = z(T, d)
 
     # ------------------------------------------------------------ forward
-    def forward(self, x, w_r, w_gu, w_down, bias=None, noise=None, stream=None, sel_bias=None):
+    def forward(self, x, w_r, w_gu, w_down, bias=None, noise=None, stream=None, sel_bias=None,
+                lora=None):
         """bias is added to the logits (it moves selection and weights);
         sel_bias only shifts the scores the top-k compares."""
         abi.moe_router_logits(x, w_r, bias, noise, self.logits, stream)
@@ -90,7 +107,7 @@ class MoEBlock:
         else:
             abi.moe_route_biased(self.logits, sel_bias, self.k, self.topk_idx, self.topk_w, stream)
         self.permute(x, stream)
-        self.experts_forward(w_gu, w_down, stream)
+        self.experts_forward(w_gu, w_down, stream, lora)
         abi.moe_combine(self.y_perm, self.slot_to_row, self.T, self.k, self.y, stream)
         return self.y
 
@@ -99,19 +116,27 @@ class MoEBlock:
                         self.counts, self.offsets, self.slot_to_row, self.row_to_slot,
                         self.x_perm, self.w_perm, self.ws, dtype=self.dcode, stream=stream)
 
-    def experts_forward(self, w_gu, w_down, stream=None):
+    def experts_forward(self, w_gu, w_down, stream=None, lora=None):
+        """lora: (a_gu, b_gu, a_dn, b_dn) device tensors when lora_rank is set."""
+        if self.lora_rank:
+            a_gu, b_gu, a_dn, b_dn = lora
+            abi.moe_grouped_ffn_fwd_lora(self.x_perm, self.offsets, self.E, w_gu, w_down,
+                                         self.w_perm, a_gu, b_gu, a_dn, b_dn, self.lora_scale,
+                                         self.z_gu, self.z_dn, self.gu, self.h, self.y_perm,
+                                         self.ws, stream)
+            return
         abi.moe_grouped_ffn_fwd(self.x_perm, self.offsets, self.E, w_gu, w_down, self.w_perm,
                                 self.gu, self.h, self.y_perm, self.ws, stream)
 
     # ------------------------------------------------------------ backward
     def backward(self, x, w_r, w_gu, w_down, dy, stream=None, aux_coeff: float = 0.0,
-                 n_valid: Optional[int] = None):
+                 n_valid: Optional[int] = None, lora=None):
         """aux_coeff != 0 adds the load-balancing auxiliary loss's gradient to
         the router's; its statistics (and self.aux = [aux, aux_scaled]) cover
         the first n_valid tokens (all if None)."""
         assert self.has_bwd
         abi.moe_combine_bwd(dy, self.slot_to_row, self.k, self.dy_perm, stream)
-        self.experts_backward(w_gu, w_down, stream)
+        self.experts_backward(w_gu, w_down, stream, lora)
         abi.moe_route_bwd(self.topk_idx, self.topk_w, self.d_row_scale, self.slot_to_row,
                           self.E, self.d_topk_w, self.d_logits, stream)
         if aux_coeff != 0.0:
@@ -139,7 +164,15 @@ class MoEBlock:
         abi.moe_expert_load(self.topk_idx, n, self.E, self.load, self.ws, stream)
         abi.moe_bias_update(self.load, n, self.k, rate, sel_bias, stream)
 
-    def experts_backward(self, w_gu, w_down, stream=None):
+    def experts_backward(self, w_gu, w_down, stream=None, lora=None):
+        if self.lora_rank:
+            a_gu, b_gu, a_dn, b_dn = lora
+            abi.moe_grouped_ffn_bwd_lora(self.x_perm, self.gu, self.h, self.offsets, self.E, w_gu,
+                                         w_down, self.w_perm, self.dy_perm, a_gu, b_gu, a_dn,
+                                         b_dn, self.lora_scale, self.z_gu, self.z_dn, self.dgu,
+                                         self.dx_perm, self.d_row_scale, self.da_gu, self.db_gu,
+                                         self.da_dn, self.db_dn, self.ws, stream)
+            return
         abi.moe_grouped_ffn_bwd(self.x_perm, self.gu, self.h, self.offsets, self.E, w_gu,
                                 w_down, self.w_perm, self.dy_perm, self.dgu, self.dx_perm,
                                 self.dw_gu, self.dw_down, self.d_row_scale, self.ws, stream)

@@ -84,3 +84,58 @@ def test_grouped_lora_matches_oracle(w, r, scale):
     for e in np.where(counts == 0)[0]:
         for t in (dag, dbg, dad, dbd):
             assert float(t[e].abs().max()) == 0.0
+
+
+BLOCK_CASES = [(_case(300, 328, 6, 2, 200, "uniform", 41), 16),
+               (_case(512, 256, 16, 4, 384, "zipf", 42), 32)]
+
+
+@pytest.mark.parametrize("w,r", BLOCK_CASES, ids=["%s-r%d" % (c[0].name, c[1]) for c in BLOCK_CASES])
+def test_block_with_lora_matches_oracle(w, r):
+    """The whole block in LoRA mode (router, routing, permutation, LoRA grouped
+    FFN, combine and their backward) against the oracle's steps."""
+    import torch
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+    from tests.test_gpu_parity import check_forward
+    dev = need_gpu()
+    print("GPU case", w.name, "rank", r, flush=True)
+    a = I.make_inputs(w)
+    lf = I.make_lora_factors(w, r)
+    scale = 0.75
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev, lora_rank=r,
+                   lora_scale=scale)
+    x, wr, wgu, wd = (up(a[n], True, dev) for n in ("x", "w_r", "w_gu", "w_down"))
+    lora = tuple(up(lf[n], True, dev) for n in ("a_gu", "b_gu", "a_dn", "b_dn"))
+    bias = None if a["bias"] is None else up(a["bias"], False, dev)
+    blk.forward(x, wr, wgu, wd, bias, lora=lora)
+    blk.backward(x, wr, wgu, wd, up(a["dy"], True, dev), lora=lora)
+    torch.cuda.synchronize()
+    g = {n: down(getattr(blk, n)) for n in (
+        "logits", "topk_idx", "topk_w", "counts", "offsets", "slot_to_row", "row_to_slot",
+        "x_perm", "w_perm", "gu", "h", "y_perm", "y", "z_gu", "z_dn", "dgu", "dx_perm",
+        "d_row_scale", "d_logits", "dw_r", "dx", "da_gu", "db_gu", "da_dn", "db_dn")}
+    # oracle: the same steps with the LoRA grouped FFN
+    o = {}
+    o["logits"] = O.router_logits(a["x"], a["w_r"], a["bias"], a["noise"])
+    o["topk_idx"], o["topk_w"] = O.route(o["logits"], w.k)
+    o["counts"], o["offsets"], o["slot_to_row"], o["row_to_slot"] = O.permute_maps(o["topk_idx"], w.E)
+    o["x_perm"], o["w_perm"] = O.permute_rows(a["x"], o["topk_w"], o["row_to_slot"], w.k)
+    o["gu"], o["h"], o["y_perm"], o["z_gu"], o["z_dn"] = O.expert_ffn_fwd_lora(
+        o["x_perm"], o["offsets"], a["w_gu"], a["w_down"], o["w_perm"], lf["a_gu"], lf["b_gu"],
+        lf["a_dn"], lf["b_dn"], scale, True)
+    o["y"] = O.combine(o["y_perm"], o["slot_to_row"], w.T, w.k, True)
+    check_forward(g, o)
+    close("z_gu", g["z_gu"], o["z_gu"], flip=True)
+    close("z_dn", g["z_dn"], o["z_dn"], flip=True)
+    dyp = O.combine_bwd(a["dy"], o["slot_to_row"], w.k)
+    b = O.expert_ffn_bwd_lora(o["x_perm"], o["gu"], o["offsets"], a["w_gu"], a["w_down"],
+                              o["w_perm"], dyp, lf["a_gu"], lf["b_gu"], lf["a_dn"], lf["b_dn"],
+                              scale, o["z_gu"], o["z_dn"], True)
+    _, dl = O.route_bwd(o["topk_idx"], o["topk_w"], b["d_row_scale"], o["slot_to_row"], w.E)
+    dxr, dwr = O.router_logits_bwd(a["x"], a["w_r"], dl)
+    dx = O.permute_bwd(b["dx_perm"], o["slot_to_row"], w.T, w.k, dxr, True)
+    for n, ref in (("dgu", b["dgu"]), ("dx_perm", b["dx_perm"]), ("d_row_scale", b["d_row_scale"]),
+                   ("d_logits", dl), ("dw_r", dwr), ("da_gu", b["da_gu"]), ("db_gu", b["db_gu"]),
+                   ("da_dn", b["da_dn"]), ("db_dn", b["db_dn"])):
+        close(n, g[n], ref, flip=True)
+    close("dx", g["dx"], dx)
