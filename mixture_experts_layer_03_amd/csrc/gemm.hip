@@ -1188,11 +1188,12 @@ __global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in
   for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const int nsteps = (K + 31) / 32;
+  constexpr int U = NR == 1 ? 8 : 4;   // steps in flight per wave
   int st = wave;
-  for (; st + 12 < nsteps; st += 16) {   // four steps in flight
-    u32x4_t av[4], bv[4][NR];
+  for (; st + 4 * (U - 1) < nsteps; st += 4 * U) {
+    u32x4_t av[U], bv[U][NR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int k = (st + 4 * u) * 32 + ch * 8;
       const bool kv = k < K;
       av[u] = (rvalid && kv) ? *reinterpret_cast<const u32x4_t *>(arow + (st + 4 * u) * 32) : zero;
@@ -1202,7 +1203,7 @@ __global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in
                       : zero;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NR; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][j]),
@@ -1237,16 +1238,25 @@ __global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in
   }
 }
 
-// Ft[e][i][c] = F[e][c][i]  (F: [E, K, r] -> Ft: [E, r, K])
+// Ft[e][i][c] = F[e][c][i]  (F: [E, K, r] -> Ft: [E, r, K]).  One block per
+// (expert, 256 K-rows): the 256 x r slab is read row by row (coalesced) into
+// LDS and written rank by rank (coalesced).
 __global__ __launch_bounds__(256) void k_lora_transpose(const bf16_t *__restrict__ F, int E, int K,
                                                         int r, bf16_t *__restrict__ Ft) {
-  const int64_t n = (int64_t)E * K * r;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int64_t e = i / ((int64_t)K * r);
-  const int64_t rem = i - e * K * r;
-  const int rank = (int)(rem / K), c = (int)(rem - (int64_t)rank * K);
-  Ft[i] = F[(e * K + c) * r + rank];
+  __shared__ bf16_t t[256 * (kLoraMaxRank + 2)];
+  const int nblk = (K + 255) / 256;
+  const int e = blockIdx.x / nblk;
+  const int c0 = (blockIdx.x - e * nblk) * 256;
+  const int rows = min(256, K - c0);
+  const int ld = r + 2;   // odd word stride: the column reads spread over the banks
+  const bf16_t *src = F + ((int64_t)e * K + c0) * r;
+  for (int i = threadIdx.x; i < rows * r; i += 256) t[(i / r) * ld + i % r] = src[i];
+  __syncthreads();
+  bf16_t *dst = Ft + (int64_t)e * r * K + c0;
+  for (int i = threadIdx.x; i < rows * r; i += 256) {
+    const int rank = i / rows, c = i - rank * rows;
+    dst[(int64_t)rank * K + c] = t[c * ld + rank];
+  }
 }
 
 // LoRA factor gradient of expert e over its rows:
@@ -1263,7 +1273,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const bf16_t *__restrict__ M,
                                                    const bf16_t *__restrict__ Z,
                                                    const int32_t *__restrict__ offsets, int E,
                                                    int K, float *__restrict__ out) {
-  constexpr int BP = 256, BQ = 128, BK = 32, NW = 4, NS = 2;
+  constexpr int BP = 256, BQ = 128, BK = 32, NW = 4, NS = 4;
   constexpr int NR = R / 16;
   constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;
   constexpr int LOADS = BP * BK / 512 / NW + BQ * BK / 512 / NW;
@@ -1293,14 +1303,14 @@ __global__ __launch_bounds__(256) void k_lora_grad(const bf16_t *__restrict__ M,
     issue_stage<BP, true, false, NW, BK>(mb, mb, K, K - c0, Me, kt * BK, st, wave, lane);
     issue_stage<BQ, true, false, NW, BK>(zb, zb, R, R, Me, kt * BK, st + SP, wave, lane);
   };
-  if (nk > 0) issue(0);
+  for (int kt = 0; kt < NS - 1 && kt < nk; ++kt) issue(kt);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      issue(kt + 1);
-      wait_vm_lgkm0<LOADS>();
-    } else {
-      wait_vm_lgkm0<0>();
-    }
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);   // into the buffer of stage kt - 1
+    const int younger = min(nk - 1 - kt, NS - 1);
+    if (younger >= 3) wait_vm_lgkm0<3 * LOADS>();
+    else if (younger == 2) wait_vm_lgkm0<2 * LOADS>();
+    else if (younger == 1) wait_vm_lgkm0<LOADS>();
+    else wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();   // stage kt landed for every wave
     const LDS_AS char *sb = lds + (kt % NS) * (SS * 16);
     bf16x8_t pf[4], qf[NR];
@@ -1314,7 +1324,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const bf16_t *__restrict__ M,
       for (int j = 0; j < NR; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
     wait_vm_lgkm0<63>();            // this wave's reads of stage kt are done
-    __builtin_amdgcn_s_barrier();   // before its buffer takes stage kt + 2
+    __builtin_amdgcn_s_barrier();   // before its buffer takes stage kt + NS
   }
   // lane holds column c0 + 64*wave + 16*i + 4*(lane/16) + v, rank 16*j + lane%16
   float *oe = out + (int64_t)e * K * R;
@@ -1779,12 +1789,11 @@ extern "C" int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, cons
   a.f = f;
   // B factors with K contiguous for the projections
   {
-    const int64_t n1 = (int64_t)E * d * r, n2 = (int64_t)E * 2 * f * r;
     MOE_LAUNCH("lora_transpose", s,
-               k_lora_transpose<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
+               k_lora_transpose<<<(unsigned)(E * ((d + 255) / 256)), 256, 0, s>>>(
                    (const bf16_t *)b_dn, E, d, r, b_dn_t));
     MOE_LAUNCH("lora_transpose", s,
-               k_lora_transpose<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
+               k_lora_transpose<<<(unsigned)(E * ((2 * f + 255) / 256)), 256, 0, s>>>(
                    (const bf16_t *)b_gu, E, 2 * f, r, b_gu_t));
     rc = check_launch("moe_grouped_ffn_bwd_lora(transpose)");
     if (rc) return rc;
