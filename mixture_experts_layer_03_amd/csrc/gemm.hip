@@ -1189,13 +1189,14 @@ __global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const int nsteps = (K + 31) / 32;
   constexpr int U = NR == 1 ? 8 : 4;   // steps in flight per wave
-  int st = wave;
-  for (; st + 4 * (U - 1) < nsteps; st += 4 * U) {
+  // every pass issues the loads of U steps (steps past the end load zeros),
+  // so the last, partial pass keeps its loads in flight together too
+  for (int st = wave; st < nsteps; st += 4 * U) {
     u32x4_t av[U], bv[U][NR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = (st + 4 * u) * 32 + ch * 8;
-      const bool kv = k < K;
+      const bool kv = k < K;   // also false for steps past the end (K <= 32 * nsteps)
       av[u] = (rvalid && kv) ? *reinterpret_cast<const u32x4_t *>(arow + (st + 4 * u) * 32) : zero;
 #pragma unroll
       for (int j = 0; j < NR; ++j)
@@ -1208,18 +1209,6 @@ __global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in
       for (int j = 0; j < NR; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][j]),
                                                          acc[j], 0, 0, 0);
-  }
-  for (; st < nsteps; st += 4) {
-    const int k = st * 32 + ch * 8;
-    const bool kv = k < K;
-    const u32x4_t av = (rvalid && kv) ? *reinterpret_cast<const u32x4_t *>(arow + st * 32) : zero;
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const u32x4_t bv = kv ? *reinterpret_cast<const u32x4_t *>(Fe + (int64_t)j * 16 * K + st * 32)
-                            : zero;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[j], 0, 0,
-                                                       0);
-    }
   }
   // lane holds rows 4*(lane/16) + v, rank 16*j + lane%16
 #pragma unroll
@@ -1263,17 +1252,18 @@ __global__ __launch_bounds__(256) void k_lora_transpose(const bf16_t *__restrict
 //   G[c][i] = sum_{rows of e} M[row][c] * Z[row][i]     (M: [R, K], Z: [R, r])
 // stored as out[e][c][i] (KR) or out[e][i][c] (RK), fp32.  One block (4
 // waves) per (expert, 256-column slab of M); the rows of the expert are the
-// reduction, 32 per stage, both operands staged transposed into LDS by the
+// reduction, 64 per stage, both operands staged transposed into LDS by the
 // same direct loads as the weight-gradient GEMMs (Z padded to 128 columns,
 // the narrowest width whose transposed layout keeps the block swizzle inside
-// a k-row; columns past r are loaded but never used), double-buffered.  Wave w owns columns
-// 64w .. 64w+63 of the slab: 4 x (r/16) MFMA tiles.  Empty experts store zeros.
+// a k-row; columns past r are loaded but never used), three stages, two in
+// flight.  Wave w owns columns 64w .. 64w+63 of the slab: 4 x (r/16) MFMA
+// tiles.  Empty experts store zeros.
 template <int R, bool KR>
 __global__ __launch_bounds__(256) void k_lora_grad(const bf16_t *__restrict__ M,
                                                    const bf16_t *__restrict__ Z,
                                                    const int32_t *__restrict__ offsets, int E,
                                                    int K, float *__restrict__ out) {
-  constexpr int BP = 256, BQ = 128, BK = 32, NW = 4, NS = 4;
+  constexpr int BP = 256, BQ = 128, BK = 64, NW = 4, NS = 3;
   constexpr int NR = R / 16;
   constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;
   constexpr int LOADS = BP * BK / 512 / NW + BQ * BK / 512 / NW;
@@ -1307,22 +1297,25 @@ __global__ __launch_bounds__(256) void k_lora_grad(const bf16_t *__restrict__ M,
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + NS - 1 < nk) issue(kt + NS - 1);   // into the buffer of stage kt - 1
     const int younger = min(nk - 1 - kt, NS - 1);
-    if (younger >= 3) wait_vm_lgkm0<3 * LOADS>();
-    else if (younger == 2) wait_vm_lgkm0<2 * LOADS>();
+    static_assert(NS - 1 <= 2 && 2 * LOADS < 64, "waits cover two younger stages");
+    if (younger == 2) wait_vm_lgkm0<2 * LOADS>();
     else if (younger == 1) wait_vm_lgkm0<LOADS>();
     else wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();   // stage kt landed for every wave
     const LDS_AS char *sb = lds + (kt % NS) * (SS * 16);
-    bf16x8_t pf[4], qf[NR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf[i] = frag_at<true, false, BP, BK, 4>(sb, rdP, i, 0);
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8_t pf[4], qf[NR];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) qf[j] = frag_at<true, false, BQ, BK, NR>(sb, rdQ, j, 0);
+      for (int i = 0; i < 4; ++i) pf[i] = frag_at<true, false, BP, BK, 4>(sb, rdP, i, ks);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < NR; ++j) qf[j] = frag_at<true, false, BQ, BK, NR>(sb, rdQ, j, ks);
 #pragma unroll
-      for (int j = 0; j < NR; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[i], qf[j], acc[i][j], 0, 0, 0);
+    }
     wait_vm_lgkm0<63>();            // this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();   // before its buffer takes stage kt + NS
   }
