@@ -19,7 +19,7 @@ BK = 64   # K stage width of the kernels (two 32-wide MFMA k steps)
 TILES = {  # kind: (BP, BQ, P transposed, Q transposed, paired)
     "FWD_GU": (256, 256, False, False, True),
     "FWD_DOWN": (256, 256, False, False, False),
-    "BWD_DH": (256, 256, True, False, False),
+    "BWD_DH": (256, 128, True, False, False),
     "BWD_DX": (256, 256, True, False, False),
     "BWD_DWDOWN": (256, 256, True, True, False),
     "BWD_DWGU": (256, 256, True, True, False),
