@@ -7,8 +7,13 @@ A step is one full pass of the hot path over one batch of synthetic tokens:
 router logits -> top-k/softmax -> permute -> grouped gate/up GEMM + SwiGLU ->
 grouped down GEMM + row scale -> combine, then combine backward -> grouped FFN
 backward (dGU with dSwiGLU, dX, dW_down, dW_gate_up) -> route backward ->
-router backward -> permute backward.  Inputs are resident in HBM before the
-timed region starts.
+router backward -> permute backward.  By default (--rows gathered) the
+gate/up and dGU GEMMs read their token rows straight from X and dY (the
+permute gather and the combine-backward copy folded into their operand
+loads; X_perm is still stored for the dW_gate_up GEMM); --rows stored runs
+every step through stored X_perm / dY_perm.  Both are bit-identical; the
+JSON line also times the other arrangements.  Inputs are resident in HBM
+before the timed region starts.
 
 Prints one JSON line.  Besides throughput it reports the dominant kernel's
 roofline (its algorithmic FLOPs or HBM bytes per launch, whichever bounds it
@@ -121,6 +126,11 @@ def main():
                     help="extra steps with per-kernel event timing")
     ap.add_argument("--lora-rank", type=int, default=16,
                     help="also time the step with frozen experts and rank-r LoRA (0: skip)")
+    ap.add_argument("--rows", choices=("gathered", "stored"), default="gathered",
+                    help="token rows of the timed step: gathered by the GEMMs (X_perm kept "
+                         "for dW_gate_up) or stored X_perm / dY_perm")
+    ap.add_argument("--no-row-paths", action="store_true",
+                    help="skip timing the other row arrangements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (reference for HBM "
                          "byte counters)")
@@ -154,7 +164,8 @@ def main():
 
     x, wr, wgu, wd, dy = (up(a[n]) for n in ("x", "w_r", "w_gu", "w_down", "dy"))
     bias, noise = up(a["bias"], False), up(a["noise"], False)
-    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev)
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev,
+                   gather=args.rows == "gathered")
     stream = torch.cuda.current_stream()
 
     def step():
@@ -185,8 +196,10 @@ def main():
         abi.moe_timing_enable(False)
         names = ["router_logits", "route_topk", "permute_hist", "permute_scan", "permute_place",
                  "permute_rows", "tile_prefix", "gg_fwd_gate_up_swiglu", "gg_fwd_down_scale",
-                 "combine", "combine_bwd", "gg_bwd_dh_dswiglu", "drs_reduce", "gg_bwd_dx",
-                 "gg_bwd_dw_down", "gg_bwd_dw_gate_up", "route_bwd", "router_dx",
+                 "gg_fwd_gate_up_swiglu_gather", "combine", "combine_bwd", "gg_bwd_dh_dswiglu",
+                 "gg_bwd_dh_dswiglu_gather", "drs_reduce", "gg_bwd_dx",
+                 "row_scale", "gg_bwd_dw_down", "gg_bwd_dw_gate_up", "gg_bwd_dw_gate_up_gather",
+                 "route_bwd", "router_dx",
                  "router_dw_partial", "router_dw_reduce", "permute_bwd"]
         for n in names:
             ms, cnt = abi.moe_timing_query(n)
@@ -275,6 +288,34 @@ def main():
                     "kernels_us_per_step": lk}
         del lblk
 
+    # the same step with the other arrangements of the token rows: all stored
+    # (X_perm, dY_perm), gathered with X_perm kept for dW_gate_up, and
+    # gathered everywhere (X_perm never stored)
+    row_paths = None
+    if not args.no_row_paths:
+        row_paths = {("gathered" if args.rows == "gathered" else "stored"):
+                     {"ms_per_step": round(ms_per_step, 4)}}
+        for name, kw in (("stored", {"gather": False}), ("gathered", {"gather": True}),
+                         ("gathered_no_x_perm", {"gather": True, "store_x_perm": False})):
+            if name in row_paths:
+                continue
+            gblk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev, **kw)
+
+            def gstep():
+                gblk.forward(x, wr, wgu, wd, bias, noise)
+                gblk.backward(x, wr, wgu, wd, dy)
+
+            for _ in range(max(2, args.warmup)):
+                gstep()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                gstep()
+            torch.cuda.synchronize()
+            gel = time.perf_counter() - t0
+            row_paths[name] = {"ms_per_step": round(gel * 1e3 / args.steps, 4)}
+            del gblk
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -287,7 +328,13 @@ def main():
     R = w.R
     flops = gemm_flops(R, w.d, w.f)
     nbytes = gemm_bytes(R, w.d, w.f, w.E)
-    gemm_us = {n: kernels[n]["avg_us"] for n in flops if n in kernels}
+    # a gathered GEMM does the algorithmic work of its stored-row counterpart
+    gemm_us, launch_name = {}, {}
+    for n in flops:
+        for kn in (n, n + "_gather"):
+            if kn in kernels:
+                gemm_us[n] = kernels[kn]["avg_us"]
+                launch_name[n] = kn
     roofline = None
     gemm_frac = None
     gemm_roof_frac = None
@@ -300,19 +347,19 @@ def main():
         t = gemm_us[dom] * 1e-6
         if t_hbm[dom] > t_mfma[dom]:
             achieved = nbytes[dom] / t / 1e9
-            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+            roofline = {"bound": "hbm", "kernel": launch_name[dom], "achieved": round(achieved, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(achieved / PEAK_HBM_GBS, 4),
-                        "traffic": measured_traffic(dom, w.name),
+                        "traffic": measured_traffic(launch_name[dom], w.name),
                         "avg_launch_us": round(gemm_us[dom], 1),
                         "algorithmic_bytes_per_launch": nbytes[dom],
                         "algorithmic_flop_per_launch": flops[dom]}
         else:
             achieved = flops[dom] / t / 1e12
-            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+            roofline = {"bound": "mfma", "kernel": launch_name[dom], "achieved": round(achieved, 1),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                        "traffic": measured_traffic(dom, w.name),
+                        "traffic": measured_traffic(launch_name[dom], w.name),
                         "avg_launch_us": round(gemm_us[dom], 1),
                         "algorithmic_flop_per_launch": flops[dom],
                         "algorithmic_bytes_per_launch": nbytes[dom]}
@@ -340,7 +387,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.d, "experts": w.E,
-                   "top_k": w.k, "d_ff": w.f, "routed_rows": R, "passes": "fwd+bwd"},
+                   "top_k": w.k, "d_ff": w.f, "routed_rows": R, "passes": "fwd+bwd",
+                   "rows": args.rows},
         "grouped_gemm_frac_of_bf16_peak": None if gemm_frac is None else round(gemm_frac, 4),
         "grouped_gemm_roofline_frac": None if gemm_roof_frac is None else round(gemm_roof_frac, 4),
         "roofline": roofline,
@@ -348,6 +396,8 @@ def main():
         "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
         "router_variants": variants,
         "lora": lora_out,
+        "rows": args.rows,
+        "row_paths": row_paths,
     }
     print(json.dumps(out), flush=True)
 

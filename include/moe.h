@@ -160,6 +160,41 @@ int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const void *h,
                         float *dw_gu, float *dw_down, float *d_row_scale,
                         void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The grouped FFN with the row permutation folded into the GEMM operand
+ * loads: the tokens go to their experts as one grouped matmul over the rows
+ * sorted by expert ("Halo's 2.8x over TRL is not a kernel, and its own
+ * benchmark proves it", section "Where the gap actually is"), and the sorted
+ * rows are read from the token-major tensors where the GEMMs load them, so
+ * x_perm and dy_perm are never stored.  Row r of the expert-sorted order is
+ * token row_to_slot[r] / k (row_to_slot from moe_permute, which then needs no
+ * x / x_perm).
+ *
+ * moe_grouped_ffn_fwd_gather: the results of moe_grouped_ffn_fwd with
+ *   x_perm[r] = x[row_to_slot[r] / k]; x: [T,d] bf16, R = T*k.
+ * moe_grouped_ffn_bwd_gather: the results of moe_grouped_ffn_bwd with that
+ *   x_perm and dy_perm[r] = dy[row_to_slot[r] / k]; dy: [T,d] bf16.  x_perm:
+ *   [R,d] or NULL; when given (the forward's permuted rows), the dW_gu GEMM
+ *   reads it instead of gathering X, and x may be NULL.
+ * Every other argument, output and the workspace
+ * (moe_grouped_ffn_workspace_size(T*k, E, d, f, MOE_BF16)) are those of the
+ * plain calls; bf16 only.  Limits (else MOE_ERR_UNSUPPORTED): k <= 32,
+ * T*d < 2^30, T*k*k < 2^32.  row_to_slot must hold a permutation of
+ * 0..T*k-1 (as moe_permute writes it); other values are not checked and
+ * index outside x and dy.
+ */
+int moe_grouped_ffn_fwd_gather(const void *x, int64_t T, const int32_t *row_to_slot, int k,
+                               const int32_t *offsets, int E, int d, int f,
+                               const void *w_gu, const void *w_down, const float *row_scale,
+                               void *gu, void *h, void *y_perm,
+                               void *ws, size_t ws_bytes, void *stream);
+int moe_grouped_ffn_bwd_gather(const void *x, const void *x_perm, const void *dy, int64_t T,
+                               const int32_t *row_to_slot, int k, const void *gu, const void *h,
+                               const int32_t *offsets, int E, int d, int f,
+                               const void *w_gu, const void *w_down, const float *row_scale,
+                               void *dgu, void *dx_perm, float *dw_gu, float *dw_down,
+                               float *d_row_scale, void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- combine */
 
 /*
@@ -361,7 +396,9 @@ int moe_aux_loss(const float *logits, const int32_t *load, int64_t T, int64_t n_
  * gg_bwd_dw_down, gg_bwd_dw_gate_up, route_bwd, router_dx, router_dw_partial,
  * router_dw_reduce, router_dw_zero, permute_bwd, ffn_gu_f32, ffn_down_f32,
  * route_topk_biased, expert_load, expert_load_reduce, bias_update, aux_loss,
- * aux_loss_final, lora_proj, lora_transpose, lora_grad.
+ * aux_loss_final, lora_proj, lora_transpose, lora_grad,
+ * gg_fwd_gate_up_swiglu_gather, gg_bwd_dh_dswiglu_gather, row_scale,
+ * gg_bwd_dw_gate_up_gather.
  */
 int moe_timing_enable(int on);
 int moe_timing_reset(void);

@@ -52,6 +52,15 @@ struct GemmArgs {
   //   BWD_DX   P: A_gu [E,r,d] (transposed, like W_gu)     Q: u_gu [R,r] rows
   const bf16_t *lora_p, *lora_q;
   int lora_r;
+  // gathered operands (GATHER kernels): token rows of an unpermuted
+  // [gx_rows, ld] source, row r of the expert-sorted order being token
+  // row_to_slot[r] / k (kmagic = floor(2^32 / k) + 1):
+  //   FWD_GU   Q: X rows        BWD_DH   Q: dY rows
+  //   BWD_DWGU P: X columns (its k-rows are tokens)
+  const bf16_t *gx;
+  const int32_t *row_to_slot;
+  uint64_t kmagic;
+  int64_t gx_rows;
   int E, d, f;
   int PT;                      // tiles along P
   int QT;                      // tiles along Q (weight-gradient kinds)
@@ -94,6 +103,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 __device__ __forceinline__ void dma16(u32x4_t rs, u32x4_t *dst, uint32_t voff) {
   dma16_at(rs, lds_addr(dst), voff);
+}
+// The same with 4 bytes per lane (lane l at dst + 4*l).
+__device__ __forceinline__ void dma4_at(u32x4_t rs, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+
+// Token of top-k slot `slot` (slot / k): exact for slot * k < 2^32 with
+// kmagic = floor(2^32 / k) + 1 (the rounding error slot / 2^32 stays below
+// the 1/k gap to the next multiple).
+__device__ __forceinline__ uint32_t slot_token(int slot, uint64_t kmagic) {
+  return (uint32_t)(((uint64_t)(uint32_t)slot * kmagic) >> 32);
 }
 
 // s_waitcnt with vmcnt <= n (n < 64) and lgkmcnt = 0 (gfx9 encoding).
@@ -268,6 +291,58 @@ __device__ __forceinline__ void plan_operand(const bf16_t *base, const bf16_t *b
                                ? ((uint32_t)(krows - 1) * (uint32_t)ld + (uint32_t)cols) * 2u
                                : 0u;
     rs = make_rsrc(base + (int64_t)k0 * ld, bytes);
+  }
+}
+
+// Gathered K-contiguous operand: byte offsets (from the stage's k0) of this
+// wave's loads of tile rows q0.. of an expert segment, each the row of its
+// token in the [rows, ld] source; rows past the segment read nothing.  The
+// LDS placement is that of issue_stage.
+template <int ROWS, int NW, int BK>
+__device__ __forceinline__ void gather_rows_voff(const GemmArgs &a, int seg0, int q0, int Me,
+                                                 int ld, int wave, int lane,
+                                                 uint32_t (&voff)[ROWS * BK / 512 / NW]) {
+  constexpr int NI = ROWS * BK / 512 / NW, CPR = BK / 8, RPI = 64 / CPR;
+  int slot[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = q0 + RPI * (wave * NI + i) + lane / CPR;
+    slot[i] = q < Me ? a.row_to_slot[(int64_t)seg0 + q] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * (wave * NI + i) + lane / CPR;
+    const int ch = (lane % CPR) ^ kc_swz<BK>(row);
+    voff[i] = slot[i] >= 0
+                  ? (slot_token(slot[i], a.kmagic) * (uint32_t)ld + (uint32_t)ch * 8u) * 2u
+                  : kOOB;
+  }
+}
+
+// Plan a gathered K-contiguous stage at k0 (offsets from gather_rows_voff):
+// the resource spans the whole source from column k0.  A stage past kvalid
+// (K tail) is issued here with each lane's chunk masked, and its planned
+// loads then read nothing into `dummy`.
+template <int ROWS, int NW, int BK>
+__device__ __forceinline__ void plan_gather_rows(const GemmArgs &a, int ld, int kvalid, int k0,
+                                                 u32x4_t *tile, int wave, int lane,
+                                                 uint32_t dummy,
+                                                 const uint32_t (&voff)[ROWS * BK / 512 / NW],
+                                                 u32x4_t &rs, uint32_t &m, uint32_t &step) {
+  constexpr int NI = ROWS * BK / 512 / NW, CPR = BK / 8, RPI = 64 / CPR;
+  rs = make_rsrc(a.gx + k0, (uint32_t)((a.gx_rows * ld - k0) * 2));
+  m = lds_addr(tile + wave * NI * 64);
+  step = 1024;
+  if (k0 + BK > kvalid) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = RPI * (wave * NI + i) + lane / CPR;
+      const int ch = (lane % CPR) ^ kc_swz<BK>(row);
+      dma16(rs, tile + (wave * NI + i) * 64, k0 + ch * 8 < kvalid ? voff[i] : kOOB);
+    }
+    rs = make_rsrc(a.gx, 0);
+    m = dummy;
+    step = 0;
   }
 }
 
@@ -653,10 +728,16 @@ __device__ __forceinline__ void mfma_block(f32x4_t (&acc)[FP][FQ], const bf16x8_
 // the loads of stage n+NS), the wave reads stage n+1's fragments between the
 // MFMAs of stage n.  After a tile's epilogue, the next tile's first MFMAs are
 // issued before the wait, so the epilogue's stores drain under them.
-template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false>
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false,
+          bool GATHER = false>
 __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   using KT = KindTraits<KIND>;
   constexpr int NW = WP * WQ;
+  // gathered token rows: the Q operand of FWD_GU / BWD_DH, the P operand's
+  // k-rows of BWD_DWGU
+  constexpr bool GQ = GATHER && (KIND == FWD_GU || KIND == BWD_DH);
+  constexpr bool GP = GATHER && KIND == BWD_DWGU;
+  static_assert(!GATHER || ((GQ || GP) && !LORA), "gathered kinds");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int FP = BP / WP / 16;
   constexpr int FQ = BQ / WQ / 16;
@@ -669,7 +750,9 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   static_assert(BK == 32 || BK == 64, "stages of one or two 32-wide k steps");
   constexpr int KS = BK / 32;                                // k steps per stage
   constexpr int NIP = BP * BK / 512 / NW, NIQ = BQ * BK / 512 / NW;
-  constexpr int LOADS = NIP + NIQ;                           // direct loads per thread per stage
+  // direct loads per thread per stage (GP: one more, the token indices of
+  // the stage NS ahead)
+  constexpr int LOADS = NIP + NIQ + (GP ? 1 : 0);
   constexpr int SP = BP * BK / 8, SS = (BP + BQ) * BK / 8;   // 16-byte slots: P part, stage
   static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
   static_assert(3 * LOADS < 64, "vmcnt range");
@@ -680,6 +763,9 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   __shared__ int s_off[kMaxExperts + 1], s_ts[kMaxExperts + 1];
   __shared__ u32x4_t sdummy[64];   // target of loads that read nothing
   __shared__ int s_ring[16];       // token GEMMs: the block's tile sequence
+  // GP: per wave, a ring of 8 entries of 64 top-k slot indices (the wave's
+  // k-rows of one stage in the first KRW)
+  __shared__ int s_gidx[GP ? NW * 8 * 64 : 1];
   const LDS_AS char *lds = (const LDS_AS char *)smem;
 
   const int tid = threadIdx.x;
@@ -739,6 +825,12 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   uint32_t voffP[NIP < 2 ? NIP : 2], voffQ[NIQ < 2 ? NIQ : 2], vstrP, vstrQ;
   init_voff<BP, KT::PT_, KT::PAIRED, NW, BK>(pld, wave, lane, voffP, vstrP);
   init_voff<BQ, KT::QT_, false, NW, BK>(qld, wave, lane, voffQ, vstrQ);
+  // gathered operands: offsets per tile (GQ) or per stage (GP)
+  uint32_t gvoffQ[GQ ? NIQ : 1], gvoffP[GP ? NIP : 1];
+  // GP: the wave's NIP loads of a transposed stage cover KRW k-rows
+  constexpr int C16P = BP / 8, KRW = GP ? NIP * 64 / C16P : 1;
+  static_assert(!GP || (64 % C16P == 0 && KRW <= 64), "k-rows per wave");
+  const uint32_t xoff = lane < KRW ? (uint32_t)(KRW * wave + lane) * 4u : kOOB;
   uint32_t rdP[KT::PT_ ? FP : KS], rdQ[KT::QT_ ? FQ : KS];
   if constexpr (KT::PT_) {
 #pragma unroll
@@ -771,7 +863,53 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     ivalid = iL < cend;
     if (ivalid) it = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, iL);
   }
+  if constexpr (GQ) {
+    if (ivalid) gather_rows_voff<BQ, NW, BK>(a, it.seg0, it.q0, it.Me, qld, wave, lane, gvoffQ);
+  }
   int s_issued = 0, s_done = 0;
+
+  // GP index cursor: the stage NS ahead of the issue cursor (same tile walk);
+  // its top-k slots go into the wave's ring entry (stage % 8) with the loads
+  // of the stage NS before it, so they have landed when that stage is planned.
+  int xL = iL, xkt = 0, xseg0 = 0, xMe = 0, xnk = 0;
+  bool xvalid = ivalid;
+  if (GP && xvalid) { xseg0 = it.seg0; xMe = it.Me; xnk = it.nk; }
+  u32x4_t rsX = make_rsrc(a.offsets, 0);
+  uint32_t mX = 0;
+#define MOE_XPLAN(stage)                                                                      \
+  do {                                                                                        \
+    rsX = xvalid ? make_rsrc(a.row_to_slot + xseg0 + xkt * BK,                                \
+                             (uint32_t)max(0, xMe - xkt * BK) * 4u)                           \
+                 : make_rsrc(a.offsets, 0);                                                   \
+    mX = lds_addr(s_gidx + (wave * 8 + ((stage) & 7)) * 64);                                  \
+    if (xvalid && ++xkt >= xnk) {                                                             \
+      xkt = 0;                                                                                \
+      do {                                                                                    \
+        xL += per;                                                                            \
+        xvalid = xL < cend;                                                                   \
+        if (xvalid) {                                                                         \
+          const int xe_ = xL / (a.PT * a.QT);                                                 \
+          xseg0 = __builtin_amdgcn_readfirstlane(s_off[xe_]);                                 \
+          xMe = __builtin_amdgcn_readfirstlane(s_off[xe_ + 1]) - xseg0;                       \
+          xnk = (xMe + BK - 1) / BK;                                                          \
+        }                                                                                     \
+      } while (xvalid && xnk == 0);                                                           \
+    }                                                                                         \
+  } while (0)
+  // GP: the top-k slots of the stage to plan next (read one plan ahead)
+  int nslot[GP ? NIP : 1] = {};
+  if constexpr (GP) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      MOE_XPLAN(n);
+      dma4_at(rsX, mX, xoff);
+    }
+    wait_vm_lgkm0<0>();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NIP; ++i)
+      nslot[i] = s_gidx[wave * 8 * 64 + ((wave * NIP + i) * 64 + lane) / C16P - KRW * wave];
+  }
 
   // Loads of stage s_issued: planned once per stage (resources and LDS
   // destinations in scalar registers), issued one instruction at a time,
@@ -795,25 +933,73 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       stepP = stepQ = 0;                                                                      \
     } else if (ivalid) {                                                                      \
       u32x4_t *st_ = smem + ((unsigned)s_issued % NS) * SS;                                   \
-      plan_operand<BP, KT::PT_, KT::PAIRED, NW, BK>(it.pb, it.pb2, pld, it.prv, it.pkv,       \
-                                                    ikt * BK, st_, wave, lane, dummy, rsP,    \
-                                                    mP, stepP);                               \
-      plan_operand<BQ, KT::QT_, false, NW, BK>(it.qb, it.qb, qld, it.qrv, it.qkv, ikt * BK,   \
-                                               st_ + SP, wave, lane, dummy, rsQ, mQ, stepQ);  \
+      if constexpr (GP) {                                                                     \
+        MOE_GPLAN_P(st_);                                                                     \
+      } else {                                                                                \
+        plan_operand<BP, KT::PT_, KT::PAIRED, NW, BK>(it.pb, it.pb2, pld, it.prv, it.pkv,     \
+                                                      ikt * BK, st_, wave, lane, dummy, rsP,  \
+                                                      mP, stepP);                             \
+      }                                                                                       \
+      if constexpr (GQ) {                                                                     \
+        plan_gather_rows<BQ, NW, BK>(a, qld, it.qkv, ikt * BK, st_ + SP, wave, lane, dummy,   \
+                                     gvoffQ, rsQ, mQ, stepQ);                                 \
+      } else {                                                                                \
+        plan_operand<BQ, KT::QT_, false, NW, BK>(it.qb, it.qb, qld, it.qrv, it.qkv, ikt * BK, \
+                                                 st_ + SP, wave, lane, dummy, rsQ, mQ,        \
+                                                 stepQ);                                      \
+      }                                                                                       \
     } else {                                                                                  \
       rsP = make_rsrc(a.offsets, 0);                                                          \
       rsQ = rsP;                                                                              \
       mP = mQ = dummy;                                                                        \
       stepP = stepQ = 0;                                                                      \
     }                                                                                         \
+    if constexpr (GP) {                                                                       \
+      MOE_XPLAN(s_issued + NS);                                                               \
+      if (!ivalid) mX = dummy;                                                                \
+    }                                                                                         \
   } while (0)
 #define MOE_DMA(n)                                                                            \
   do {                                                                                        \
-    if ((n) < NIP)                                                                            \
-      dma16_at(rsP, mP + (n) * stepP, voffP[(n) % 2] + ((n) / 2) * vstrP);                    \
-    else                                                                                      \
-      dma16_at(rsQ, mQ + ((n) - NIP) * stepQ,                                                 \
-               voffQ[((n) - NIP) % 2] + (((n) - NIP) / 2) * vstrQ);                           \
+    if ((n) < NIP) {                                                                          \
+      if constexpr (GP)                                                                       \
+        dma16_at(rsP, mP + (n) * stepP, gvoffP[GP ? (n) : 0]);                                \
+      else                                                                                    \
+        dma16_at(rsP, mP + (n) * stepP, voffP[(n) % 2] + ((n) / 2) * vstrP);                  \
+    } else if ((n) < NIP + NIQ) {                                                             \
+      if constexpr (GQ)                                                                       \
+        dma16_at(rsQ, mQ + ((n) - NIP) * stepQ, gvoffQ[GQ ? (n) - NIP : 0]);                  \
+      else                                                                                    \
+        dma16_at(rsQ, mQ + ((n) - NIP) * stepQ,                                               \
+                 voffQ[((n) - NIP) % 2] + (((n) - NIP) / 2) * vstrQ);                         \
+    } else {                                                                                  \
+      dma4_at(rsX, mX, xoff);                                                                 \
+    }                                                                                         \
+  } while (0)
+// GP: this stage's X k-rows from the top-k slots read from the wave's ring
+// at the previous plan (entries land with the loads of the stage NS before
+// theirs, so the entry of the next stage is complete after this stage's
+// wait); k-rows past the expert's rows read nothing.  The resource starts at
+// the tile's first column: columns past d read the next token row (feeding
+// only masked outputs) or zeros.
+#define MOE_GPLAN_P(st_)                                                                      \
+  do {                                                                                        \
+    asm volatile("" ::: "memory");                                                            \
+    const int k0_ = ikt * BK;                                                                 \
+    const int *ent_ = s_gidx + (wave * 8 + ((s_issued + 1) & 7)) * 64;                        \
+    _Pragma("unroll") for (int i = 0; i < (GP ? NIP : 0); ++i) {                              \
+      const int lin_ = (wave * NIP + i) * 64 + lane;                                          \
+      const int kr_ = lin_ / C16P;                                                            \
+      const int c16_ = (lin_ % C16P) ^ (tr_swz(kr_) << 1);                                    \
+      gvoffP[GP ? i : 0] = k0_ + kr_ < it.Me ? (slot_token(nslot[GP ? i : 0], a.kmagic) *     \
+                                                    (uint32_t)pld +                           \
+                                                (uint32_t)c16_ * 8u) * 2u                     \
+                                             : kOOB;                                          \
+      nslot[GP ? i : 0] = ent_[kr_ - KRW * wave];                                             \
+    }                                                                                         \
+    rsP = make_rsrc(a.gx + it.p0, (uint32_t)((a.gx_rows * pld - it.p0) * 2));                 \
+    mP = lds_addr((st_) + wave * NIP * 64);                                                   \
+    stepP = 1024;                                                                             \
   } while (0)
 #define MOE_ADVANCE()                                                                         \
   do {                                                                                        \
@@ -834,6 +1020,9 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
           if (ivalid) {                                                                       \
             it = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, iL);                             \
             if (tid == 0) s_ring[(iseq + NS) & 15] = MOE_FETCH();                             \
+            if constexpr (GQ)                                                                 \
+              gather_rows_voff<BQ, NW, BK>(a, it.seg0, it.q0, it.Me, qld, wave, lane,         \
+                                           gvoffQ);                                           \
           }                                                                                   \
         }                                                                                     \
       }                                                                                       \
@@ -1017,6 +1206,8 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
 #undef MOE_DMA
 #undef MOE_ADVANCE
 #undef MOE_ISSUE_ALL
+#undef MOE_XPLAN
+#undef MOE_GPLAN_P
 #undef MOE_FETCH
 }
 
@@ -1353,6 +1544,8 @@ constexpr int FWD_BP = 256, FWD_BQ = 256, FWD_WP = 2, FWD_WQ = 4, FWD_NS = 2, FW
 constexpr int DN_BP = 256, DN_BQ = 256, DN_WP = 2, DN_WQ = 4, DN_NS = 2, DN_BK = 64;  // FWD_DOWN
 constexpr int DX_BP = 256, DX_BQ = 256, DX_WP = 2, DX_WQ = 4, DX_NS = 2, DX_BK = 64;  // BWD_DX
 constexpr int DH_BP = 256, DH_BQ = 128, DH_WP = 4, DH_WQ = 2, DH_NS = 3, DH_BK = 64;  // BWD_DH
+// gathered FWD_GU: 64x64 waves leave room for the per-row token offsets
+constexpr int FG_BP = 256, FG_BQ = 128, FG_WP = 4, FG_WQ = 2, FG_NS = 3, FG_BK = 64;
 constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK = 32;  // weight grads
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
@@ -1366,6 +1559,28 @@ __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy
   const int64_t r = i / nvec;
   const float wr = w ? w[r] : 1.0f;
   const u32x4_t v = reinterpret_cast<const u32x4_t *>(dy)[i];
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = pack_bf16x2(bf16_bits_to_f32(v[j] & 0xffffu) * wr, bf16_bits_to_f32(v[j] >> 16) * wr);
+  reinterpret_cast<u32x4_t *>(s)[i] = o;
+}
+
+// The same with the rows gathered from the unpermuted dY: S[r] =
+// store(w[r] * dY[token of row r]).
+__global__ __launch_bounds__(256) void k_row_scale_gather(const bf16_t *__restrict__ dy,
+                                                          const int32_t *__restrict__ row_to_slot,
+                                                          uint64_t kmagic,
+                                                          const float *__restrict__ w, int64_t R,
+                                                          int d, bf16_t *__restrict__ s) {
+  const int nvec = d / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * nvec) return;
+  const int64_t r = i / nvec;
+  const int64_t c = i - r * nvec;
+  const float wr = w ? w[r] : 1.0f;
+  const int64_t t = slot_token(row_to_slot[r], kmagic);
+  const u32x4_t v = reinterpret_cast<const u32x4_t *>(dy + t * d)[c];
   u32x4_t o;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -1401,7 +1616,8 @@ static int launch_tile_prefix(const GemmArgs &a, int BQa, int PTa, int32_t *tsa,
   return check_launch("tile_prefix");
 }
 
-template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false>
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false,
+          bool GATHER = false>
 static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start, const char *name,
                              hipStream_t s) {
   if (R == 0) return MOE_OK;
@@ -1411,17 +1627,20 @@ static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start,
   const int64_t bound = ((R + BQ - 1) / BQ + a.E) * (int64_t)PT;
   const int grid = persistent_grid(bound);
   MOE_LAUNCH(name, s,
-             (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK, LORA><<<grid, WP * WQ * 64, 0, s>>>(a)));
+             (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK, LORA, GATHER>
+              <<<grid, WP * WQ * 64, 0, s>>>(a)));
   return check_launch(name);
 }
 
-template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK>
+template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool GATHER = false>
 static int launch_wgrad_gemm(GemmArgs a, int Pdim, int Qdim, const char *name, hipStream_t s) {
   a.PT = (Pdim + BP - 1) / BP;
   a.QT = (Qdim + BQ - 1) / BQ;
   a.nlogical = a.E * a.PT * a.QT;
   const int grid = persistent_grid(a.nlogical);
-  MOE_LAUNCH(name, s, (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK><<<grid, WP * WQ * 64, 0, s>>>(a)));
+  MOE_LAUNCH(name, s,
+             (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK, false, GATHER>
+              <<<grid, WP * WQ * 64, 0, s>>>(a)));
   return check_launch(name);
 }
 
@@ -1456,6 +1675,27 @@ extern "C" size_t moe_grouped_ffn_workspace_size(int64_t R, int E, int d, int f,
   return 2 * tile_start_bytes(E) + drs_bytes(R, f) + align_up(2 * (size_t)R * d, 256);
 }
 
+// bf16 forward: gate/up GEMM + SwiGLU, down GEMM + row scale.  gather: the
+// gate/up GEMM reads its token rows from a.gx through a.row_to_slot.
+static int ffn_fwd_bf16(GemmArgs a, int64_t R, void *ws, hipStream_t s, bool gather) {
+  const int E = a.E, d = a.d, f = a.f;
+  int32_t *ts0 = (int32_t *)ws;
+  int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
+  static_assert(FG_BP == FWD_BP, "one gate/up P-tile count");
+  const int pt_gu = (f + FWD_BP / 2 - 1) / (FWD_BP / 2), pt_dn = (d + DN_BP - 1) / DN_BP;
+  int rc = launch_tile_prefix(a, gather ? FG_BQ : FWD_BQ, pt_gu, ts0, DN_BQ, pt_dn, ts1, s);
+  if (rc) return rc;
+  if (gather)
+    rc = launch_token_gemm<FWD_GU, FG_BP, FG_BQ, FG_WP, FG_WQ, FG_NS, FG_BK, false, true>(
+        a, R, pt_gu, ts0, "gg_fwd_gate_up_swiglu_gather", s);
+  else
+    rc = launch_token_gemm<FWD_GU, FWD_BP, FWD_BQ, FWD_WP, FWD_WQ, FWD_NS, FWD_BK>(
+        a, R, pt_gu, ts0, "gg_fwd_gate_up_swiglu", s);
+  if (rc) return rc;
+  return launch_token_gemm<FWD_DOWN, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK>(
+      a, R, pt_dn, ts1, "gg_fwd_down_scale", s);
+}
+
 extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, int E, int64_t R,
                                    int d, int f, const void *w_gu, const void *w_down,
                                    const float *row_scale, int dtype, void *gu, void *h,
@@ -1487,8 +1727,6 @@ extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, i
                    (float *)y_perm));
     return check_launch("moe_grouped_ffn_fwd(down f32)");
   }
-  int32_t *ts0 = (int32_t *)ws;
-  int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
   GemmArgs a{};
   a.x_perm = (const bf16_t *)x_perm;
   a.w_gu = (const bf16_t *)w_gu;
@@ -1502,14 +1740,77 @@ extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, i
   a.E = E;
   a.d = d;
   a.f = f;
-  const int pt_gu = (f + FWD_BP / 2 - 1) / (FWD_BP / 2), pt_dn = (d + DN_BP - 1) / DN_BP;
-  rc = launch_tile_prefix(a, FWD_BQ, pt_gu, ts0, DN_BQ, pt_dn, ts1, s);
+  return ffn_fwd_bf16(a, R, ws, s, false);
+}
+
+// bf16 backward: dH GEMM + dSwiGLU (+ d_row_scale), dX GEMM, the two
+// weight-gradient GEMMs.  gdy (gathered): the dH GEMM and S read the rows of
+// the unpermuted dY = gdy through a.row_to_slot, and without a.x_perm the
+// dW_gu GEMM reads X = a.gx the same way.
+static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, float *d_row_scale,
+                        const bf16_t *gdy, void *ws, hipStream_t s) {
+  const int E = a.E, d = a.d, f = a.f;
+  const bool gather = gdy != nullptr;
+  int32_t *ts0 = (int32_t *)ws;
+  int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
+  float *drs_part = (float *)((char *)ws + 2 * tile_start_bytes(E));
+  bf16_t *s_perm = (bf16_t *)((char *)ws + 2 * tile_start_bytes(E) + drs_bytes(R, f));
+  a.o_drs = drs_part;
+  const int pt_dh = (f + DH_BP - 1) / DH_BP, pt_dx = (d + DX_BP - 1) / DX_BP;
+  int rc = MOE_OK;
+  if (R > 0) {
+    rc = launch_tile_prefix(a, DH_BQ, pt_dh, ts0, DX_BQ, pt_dx, ts1, s);
+    if (rc) return rc;
+  }
+  // 1. dGU (and d_row_scale partials) from dY_perm and W_down
+  if (gather) {
+    GemmArgs g = a;
+    const bf16_t *x = a.gx;
+    g.gx = gdy;
+    rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ, DH_NS, DH_BK, false, true>(
+        g, R, pt_dh, ts0, "gg_bwd_dh_dswiglu_gather", s);
+    a.gx = x;
+  } else {
+    rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ, DH_NS, DH_BK>(a, R, pt_dh, ts0,
+                                                               "gg_bwd_dh_dswiglu", s);
+  }
   if (rc) return rc;
-  rc = launch_token_gemm<FWD_GU, FWD_BP, FWD_BQ, FWD_WP, FWD_WQ, FWD_NS, FWD_BK>(
-      a, R, pt_gu, ts0, "gg_fwd_gate_up_swiglu", s);
+  if (d_row_scale && R > 0) {
+    MOE_LAUNCH("drs_reduce", s,
+               k_drs_reduce<<<(unsigned)((R + 255) / 256), 256, 0, s>>>(drs_part, pt_dh * DH_WP, R,
+                                                                       d_row_scale));
+    rc = check_launch("moe_grouped_ffn_bwd(drs)");
+    if (rc) return rc;
+  }
+  // 2. dX_perm = dGU . W_gu
+  rc = launch_token_gemm<BWD_DX, DX_BP, DX_BQ, DX_WP, DX_WQ, DX_NS, DX_BK>(a, R, pt_dx, ts1,
+                                                             "gg_bwd_dx", s);
   if (rc) return rc;
-  return launch_token_gemm<FWD_DOWN, DN_BP, DN_BQ, DN_WP, DN_WQ, DN_NS, DN_BK>(
-      a, R, pt_dn, ts1, "gg_fwd_down_scale", s);
+  // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
+  if (R > 0) {
+    const int64_t n = R * (d / 8);
+    if (gather)
+      MOE_LAUNCH("row_scale", s,
+                 k_row_scale_gather<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+                     gdy, a.row_to_slot, a.kmagic, a.row_scale, R, d, s_perm));
+    else
+      MOE_LAUNCH("row_scale", s,
+                 k_row_scale<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+                     a.dy_perm, a.row_scale, R, d, s_perm));
+    rc = check_launch("moe_grouped_ffn_bwd(row scale)");
+    if (rc) return rc;
+  }
+  a.s_perm = s_perm;
+  a.o_dw = dw_down;
+  rc = launch_wgrad_gemm<BWD_DWDOWN, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, f, d, "gg_bwd_dw_down", s);
+  if (rc) return rc;
+  // 4. dW_gu[e] = dGU^T X_perm        -> [E, 2f, d]
+  a.o_dw = dw_gu;
+  if (gather && !a.x_perm)
+    return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK, true>(
+        a, d, 2 * f, "gg_bwd_dw_gate_up_gather", s);
+  return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, d, 2 * f, "gg_bwd_dw_gate_up",
+                                                                s);
 }
 
 extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const void *h,
@@ -1534,10 +1835,6 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: workspace %zu < %zu",
               ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
-  int32_t *ts0 = (int32_t *)ws;
-  int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
-  float *drs_part = (float *)((char *)ws + 2 * tile_start_bytes(E));
-  bf16_t *s_perm = (bf16_t *)((char *)ws + 2 * tile_start_bytes(E) + drs_bytes(R, f));
   GemmArgs a{};
   a.x_perm = (const bf16_t *)x_perm;
   a.w_gu = (const bf16_t *)w_gu;
@@ -1550,47 +1847,117 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   a.offsets = offsets;
   a.o_dgu = (bf16_t *)dgu;
   a.o_dx = (bf16_t *)dx_perm;
-  a.o_drs = drs_part;
   a.E = E;
   a.d = d;
   a.f = f;
-  const int pt_dh = (f + DH_BP - 1) / DH_BP, pt_dx = (d + DX_BP - 1) / DX_BP;
-  if (R > 0) {
-    rc = launch_tile_prefix(a, DH_BQ, pt_dh, ts0, DX_BQ, pt_dx, ts1, s);
-    if (rc) return rc;
-  }
-  // 1. dGU (and d_row_scale partials) from dY_perm and W_down
-  rc = launch_token_gemm<BWD_DH, DH_BP, DH_BQ, DH_WP, DH_WQ, DH_NS, DH_BK>(a, R, pt_dh, ts0,
-                                                             "gg_bwd_dh_dswiglu", s);
+  return ffn_bwd_bf16(a, R, dw_gu, dw_down, d_row_scale, nullptr, ws, s);
+}
+
+// ====================================================================== gathered rows
+
+static int check_gather(const char *fn, int64_t T, int k, int d, const int32_t *row_to_slot) {
+  MOE_REQUIRE(T >= 0 && k >= 1 && k <= 32, MOE_ERR_UNSUPPORTED, "%s: T=%lld k=%d", fn,
+              (long long)T, k);
+  MOE_REQUIRE(T * k < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
+  // byte offsets into the token-major sources and the slot -> token division
+  // stay exact in 32 bits
+  MOE_REQUIRE(T * (int64_t)d < ((int64_t)1 << 30), MOE_ERR_UNSUPPORTED,
+              "%s: T*d = %lld must be below 2^30", fn, (long long)(T * (int64_t)d));
+  MOE_REQUIRE(T * k * (int64_t)k < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED, "%s: T*k*k too large",
+              fn);
+  MOE_REQUIRE(T == 0 || row_to_slot, MOE_ERR_INVALID_ARG, "%s: null row_to_slot", fn);
+  return MOE_OK;
+}
+
+static uint64_t slot_kmagic(int k) { return (((uint64_t)1) << 32) / (uint64_t)k + 1; }
+
+extern "C" int moe_grouped_ffn_fwd_gather(const void *x, int64_t T, const int32_t *row_to_slot,
+                                          int k, const int32_t *offsets, int E, int d, int f,
+                                          const void *w_gu, const void *w_down,
+                                          const float *row_scale, void *gu, void *h, void *y_perm,
+                                          void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_gather("moe_grouped_ffn_fwd_gather", T, k, d, row_to_slot);
   if (rc) return rc;
-  if (d_row_scale && R > 0) {
-    MOE_LAUNCH("drs_reduce", s,
-               k_drs_reduce<<<(unsigned)((R + 255) / 256), 256, 0, s>>>(drs_part, pt_dh * DH_WP, R,
-                                                                       d_row_scale));
-    rc = check_launch("moe_grouped_ffn_bwd(drs)");
-    if (rc) return rc;
-  }
-  // 2. dX_perm = dGU . W_gu
-  rc = launch_token_gemm<BWD_DX, DX_BP, DX_BQ, DX_WP, DX_WQ, DX_NS, DX_BK>(a, R, pt_dx, ts1,
-                                                             "gg_bwd_dx", s);
+  const int64_t R = T * k;
+  rc = check_ffn("moe_grouped_ffn_fwd_gather", E, R, d, f, MOE_BF16);
   if (rc) return rc;
-  // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
-  if (R > 0) {
-    const int64_t n = R * (d / 8);
-    MOE_LAUNCH("row_scale", s,
-               k_row_scale<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-                   (const bf16_t *)dy_perm, row_scale, R, d, s_perm));
-    rc = check_launch("moe_grouped_ffn_bwd(row scale)");
-    if (rc) return rc;
-  }
-  a.s_perm = s_perm;
-  a.o_dw = dw_down;
-  rc = launch_wgrad_gemm<BWD_DWDOWN, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, f, d, "gg_bwd_dw_down", s);
+  if (R == 0) return MOE_OK;
+  MOE_REQUIRE(x && offsets && w_gu && w_down && h && y_perm, MOE_ERR_INVALID_ARG,
+              "moe_grouped_ffn_fwd_gather: null pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(w_gu) && aligned16(w_down) && aligned16(h) &&
+                  aligned16(y_perm) && (!gu || aligned16(gu)),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_fwd_gather: pointers must be 16-byte aligned");
+  const size_t need = moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_grouped_ffn_fwd_gather: workspace %zu < %zu", ws_bytes, need);
+  GemmArgs a{};
+  a.x_perm = (const bf16_t *)x;   // placeholder: the gathered kernel reads gx
+  a.gx = (const bf16_t *)x;
+  a.gx_rows = T;
+  a.row_to_slot = row_to_slot;
+  a.kmagic = slot_kmagic(k);
+  a.w_gu = (const bf16_t *)w_gu;
+  a.w_down = (const bf16_t *)w_down;
+  a.h = (const bf16_t *)h;
+  a.row_scale = row_scale;
+  a.offsets = offsets;
+  a.o_gu = (bf16_t *)gu;
+  a.o_h = (bf16_t *)h;
+  a.o_y = (bf16_t *)y_perm;
+  a.E = E;
+  a.d = d;
+  a.f = f;
+  return ffn_fwd_bf16(a, R, ws, (hipStream_t)stream, true);
+}
+
+extern "C" int moe_grouped_ffn_bwd_gather(const void *x, const void *x_perm, const void *dy,
+                                          int64_t T,
+                                          const int32_t *row_to_slot, int k, const void *gu,
+                                          const void *h, const int32_t *offsets, int E, int d,
+                                          int f, const void *w_gu, const void *w_down,
+                                          const float *row_scale, void *dgu, void *dx_perm,
+                                          float *dw_gu, float *dw_down, float *d_row_scale,
+                                          void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_gather("moe_grouped_ffn_bwd_gather", T, k, d, row_to_slot);
   if (rc) return rc;
-  // 4. dW_gu[e] = dGU^T X_perm        -> [E, 2f, d]
-  a.o_dw = dw_gu;
-  return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, d, 2 * f, "gg_bwd_dw_gate_up",
-                                                                s);
+  const int64_t R = T * k;
+  rc = check_ffn("moe_grouped_ffn_bwd_gather", E, R, d, f, MOE_BF16);
+  if (rc) return rc;
+  MOE_REQUIRE(offsets && w_gu && w_down && dw_gu && dw_down, MOE_ERR_INVALID_ARG,
+              "moe_grouped_ffn_bwd_gather: null pointer");
+  MOE_REQUIRE(R == 0 || ((x || x_perm) && dy && gu && h && dgu && dx_perm), MOE_ERR_INVALID_ARG,
+              "moe_grouped_ffn_bwd_gather: null activation pointer");
+  MOE_REQUIRE(aligned16(w_gu) && aligned16(w_down) && aligned16(dw_gu) && aligned16(dw_down) &&
+                  (R == 0 || (aligned16(x) && aligned16(x_perm) && aligned16(dy) &&
+                              aligned16(gu) && aligned16(h) && aligned16(dgu) &&
+                              aligned16(dx_perm))),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd_gather: pointers must be 16-byte aligned");
+  const size_t need = moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_grouped_ffn_bwd_gather: workspace %zu < %zu", ws_bytes, need);
+  GemmArgs a{};
+  a.x_perm = (const bf16_t *)x_perm;   // null: the dW_gu GEMM gathers X
+  a.dy_perm = (const bf16_t *)dy;      // placeholder: the gathered kernels read dY as gx
+  a.gx = (const bf16_t *)(x ? x : x_perm);
+  a.gx_rows = T;
+  a.row_to_slot = row_to_slot;
+  a.kmagic = slot_kmagic(k);
+  a.w_gu = (const bf16_t *)w_gu;
+  a.w_down = (const bf16_t *)w_down;
+  a.h = (const bf16_t *)h;
+  a.gu = (const bf16_t *)gu;
+  a.dgu = (const bf16_t *)dgu;
+  a.row_scale = row_scale;
+  a.offsets = offsets;
+  a.o_dgu = (bf16_t *)dgu;
+  a.o_dx = (bf16_t *)dx_perm;
+  a.E = E;
+  a.d = d;
+  a.f = f;
+  return ffn_bwd_bf16(a, R, dw_gu, dw_down, d_row_scale, (const bf16_t *)dy, ws,
+                      (hipStream_t)stream);
 }
 
 // ====================================================================== grouped LoRA

@@ -14,6 +14,13 @@ on one stream, with no host synchronisation in between:
             stores dx_router and moe_permute_bwd adds it)
   balance : moe_expert_load -> moe_bias_update (selection-bias step)
 
+With ``gather`` the grouped GEMMs read the token rows of X and dY where they
+load them (moe_grouped_ffn_fwd_gather / moe_grouped_ffn_bwd_gather):
+dY_perm is never stored and moe_combine_bwd drops out.  X_perm is still
+written by moe_permute for the dW_gu GEMM (its stored rows are the faster
+operand there) unless ``store_x_perm`` is False; then moe_permute writes only
+the maps and w_perm and the dW_gu GEMM gathers X too.
+
 With ``lora_rank`` set the experts are frozen and carry LoRA factors:
 moe_grouped_ffn_fwd_lora / moe_grouped_ffn_bwd_lora replace the grouped-FFN
 calls, and the backward forms the LoRA factor gradients instead of the expert
@@ -37,7 +44,12 @@ from . import abi
 class MoEBlock:
     def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype=torch.bfloat16,
                  device="cuda", backward: bool = True, fuse_router_dx: bool = True,
-                 lora_rank: int = 0, lora_scale: float = 1.0):
+                 lora_rank: int = 0, lora_scale: float = 1.0, gather: bool = False,
+                 store_x_perm: bool = True):
+        if gather and (lora_rank or dtype != torch.bfloat16):
+            raise ValueError("gather needs bf16 experts without LoRA")
+        self.gather = gather
+        self.store_x_perm = store_x_perm or not gather
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.fuse_router_dx = fuse_router_dx
         self.lora_rank, self.lora_scale = lora_rank, lora_scale
@@ -57,7 +69,7 @@ class MoEBlock:
         self.offsets = z(E + 1, dt=i32)
         self.slot_to_row = z(R, dt=i32)
         self.row_to_slot = z(R, dt=i32)
-        self.x_perm = z(R, d)
+        self.x_perm = z(R, d) if self.store_x_perm else None
         self.w_perm = z(R, dt=f32)
         self.gu = z(R, 2 * f)
         self.h = z(R, f)
@@ -78,7 +90,7 @@ class MoEBlock:
         self.aux = z(2, dt=f32)
         self.has_bwd = backward
         if backward:
-            self.dy_perm = z(R, d)
+            self.dy_perm = None if gather else z(R, d)
             self.dgu = z(R, 2 * f)
             self.dx_perm = z(R, d)
             self.d_row_scale = z(R, dt=f32)
@@ -107,17 +119,25 @@ class MoEBlock:
         else:
             abi.moe_route_biased(self.logits, sel_bias, self.k, self.topk_idx, self.topk_w, stream)
         self.permute(x, stream)
-        self.experts_forward(w_gu, w_down, stream, lora)
+        self.experts_forward(w_gu, w_down, stream, lora, x=x)
         abi.moe_combine(self.y_perm, self.slot_to_row, self.T, self.k, self.y, stream)
         return self.y
 
     def permute(self, x, stream=None):
+        if not self.store_x_perm:
+            x = None   # maps and w_perm only
         abi.moe_permute(x, self.topk_idx, self.topk_w, self.T, self.d, self.E, self.k,
                         self.counts, self.offsets, self.slot_to_row, self.row_to_slot,
                         self.x_perm, self.w_perm, self.ws, dtype=self.dcode, stream=stream)
 
-    def experts_forward(self, w_gu, w_down, stream=None, lora=None):
-        """lora: (a_gu, b_gu, a_dn, b_dn) device tensors when lora_rank is set."""
+    def experts_forward(self, w_gu, w_down, stream=None, lora=None, x=None):
+        """lora: (a_gu, b_gu, a_dn, b_dn) device tensors when lora_rank is set;
+        x: the token rows, read by the gathered GEMM."""
+        if self.gather:
+            abi.moe_grouped_ffn_fwd_gather(x, self.row_to_slot, self.k, self.offsets, self.E,
+                                           w_gu, w_down, self.w_perm, self.gu, self.h,
+                                           self.y_perm, self.ws, stream)
+            return
         if self.lora_rank:
             a_gu, b_gu, a_dn, b_dn = lora
             abi.moe_grouped_ffn_fwd_lora(self.x_perm, self.offsets, self.E, w_gu, w_down,
@@ -135,8 +155,9 @@ class MoEBlock:
         the router's; its statistics (and self.aux = [aux, aux_scaled]) cover
         the first n_valid tokens (all if None)."""
         assert self.has_bwd
-        abi.moe_combine_bwd(dy, self.slot_to_row, self.k, self.dy_perm, stream)
-        self.experts_backward(w_gu, w_down, stream, lora)
+        if not self.gather:
+            abi.moe_combine_bwd(dy, self.slot_to_row, self.k, self.dy_perm, stream)
+        self.experts_backward(w_gu, w_down, stream, lora, x=x, dy=dy)
         abi.moe_route_bwd(self.topk_idx, self.topk_w, self.d_row_scale, self.slot_to_row,
                           self.E, self.d_topk_w, self.d_logits, stream)
         if aux_coeff != 0.0:
@@ -164,7 +185,14 @@ class MoEBlock:
         abi.moe_expert_load(self.topk_idx, n, self.E, self.load, self.ws, stream)
         abi.moe_bias_update(self.load, n, self.k, rate, sel_bias, stream)
 
-    def experts_backward(self, w_gu, w_down, stream=None, lora=None):
+    def experts_backward(self, w_gu, w_down, stream=None, lora=None, x=None, dy=None):
+        if self.gather:
+            abi.moe_grouped_ffn_bwd_gather(x, dy, self.row_to_slot, self.k, self.gu, self.h,
+                                           self.offsets, self.E, w_gu, w_down, self.w_perm,
+                                           self.dgu, self.dx_perm, self.dw_gu, self.dw_down,
+                                           self.d_row_scale, self.ws, stream,
+                                           x_perm=self.x_perm)
+            return
         if self.lora_rank:
             a_gu, b_gu, a_dn, b_dn = lora
             abi.moe_grouped_ffn_bwd_lora(self.x_perm, self.gu, self.h, self.offsets, self.E, w_gu,

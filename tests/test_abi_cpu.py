@@ -123,6 +123,44 @@ def test_router_variant_validation_rejects_before_launch():
     assert L.moe_aux_loss(P, P, 100, 100, 2000, 2, F(0.1), P, None, P, wsz, None) == -2
 
 
+def test_gather_ffn_validation_rejects_before_launch():
+    L = abi.lib()
+    ws = L.moe_grouped_ffn_workspace_size(400, 8, 64, 64, 1)
+    fwd = L.moe_grouped_ffn_fwd_gather
+    # good shape, missing row_to_slot
+    assert fwd(P, 100, None, 4, P, 8, 64, 64, P, P, None, P, P, P, P, ws, None) == -1
+    # k out of range, d not a multiple of 8, E out of range
+    assert fwd(P, 100, P, 33, P, 8, 64, 64, P, P, None, P, P, P, P, ws, None) == -2
+    assert fwd(P, 100, P, 4, P, 8, 60, 64, P, P, None, P, P, P, P, ws, None) == -2
+    assert fwd(P, 100, P, 4, P, 2000, 64, 64, P, P, None, P, P, P, P, ws, None) == -2
+    # 32-bit offset limits: T*d and T*k*k
+    rc, msg = _rc_msg(fwd(P, 1 << 25, P, 1, P, 8, 64, 64, P, P, None, P, P, P, P, ws, None))
+    assert rc == -2 and "T*d" in msg, msg
+    assert fwd(P, 1 << 24, P, 32, P, 8, 8, 64, P, P, None, P, P, P, P, ws, None) == -2
+    # misaligned, small workspace, empty
+    assert fwd(ctypes.c_void_p(0x1008), 100, P, 4, P, 8, 64, 64, P, P, None, P, P, P, P, ws,
+               None) == -1
+    assert fwd(P, 100, P, 4, P, 8, 64, 64, P, P, None, P, P, P, P, 16, None) == -3
+    assert fwd(None, 0, None, 4, None, 8, 64, 64, None, None, None, None, None, None, None, 0,
+               None) == 0
+    bwd = L.moe_grouped_ffn_bwd_gather
+    args = [P, None, P, 100, P, 4, P, P, P, 8, 64, 64, P, P, None, P, P, P, P, None, P, ws, None]
+    a = list(args); a[2] = None                      # dy
+    assert bwd(*a) == -1
+    a = list(args); a[0] = None                      # neither x nor x_perm
+    assert bwd(*a) == -1
+    a = list(args); a[4] = None                      # row_to_slot
+    assert bwd(*a) == -1
+    a = list(args); a[5] = 0                         # k
+    assert bwd(*a) == -2
+    a = list(args); a[21] = 16                       # workspace
+    assert bwd(*a) == -3
+    a = list(args); a[17] = ctypes.c_void_p(0x1004)  # dw_gu alignment
+    assert bwd(*a) == -1
+    a = list(args); a[1] = ctypes.c_void_p(0x1008)   # x_perm alignment
+    assert bwd(*a) == -1
+
+
 def test_empty_inputs_are_ok_without_launch():
     L = abi.lib()
     assert L.moe_router_logits(None, None, None, None, 1, 0, 16, 4, None, None) == 0

@@ -196,3 +196,112 @@ def test_load_slots_cover_the_stage_once():
                 for lane in range(64):
                     seen.add(voff_full(rows, trans, False, nw, bk, ld, wave, lane, i))
         assert len(seen) == rows * bk // 8
+
+
+# --------------------------------------------------------------------------
+# Gathered loads (moe_grouped_ffn_*_gather): restate the per-lane offsets of
+# the gathered token rows (K-contiguous, per tile) and of the gathered X
+# k-rows of the dW_gu GEMM (transposed, per stage, from a per-wave ring of
+# top-k slots), and check that every LDS slot of every stage receives what
+# the stored-row load puts there -- row r of the expert-sorted order being
+# token row_to_slot[r] // k.
+
+def slot_token(slot, k):
+    """The kernel's division: (slot * (floor(2^32 / k) + 1)) >> 32."""
+    return (slot * ((1 << 32) // k + 1)) >> 32
+
+
+@pytest.mark.parametrize("k", list(range(1, 33)))
+def test_slot_token_division_is_exact_up_to_the_limit(k):
+    T = ((1 << 32) - 1) // (k * k)        # largest T with T*k*k < 2^32
+    T = min(T, (1 << 31) // k - 1)
+    top = T * k
+    slots = np.concatenate([np.arange(0, min(top, 4096)), np.arange(max(0, top - 4096), top),
+                            np.random.default_rng(k).integers(0, top, 4096)])
+    for s in slots.tolist():
+        assert slot_token(s, k) == s // k
+
+
+def _perm_case(T, E, k, seed):
+    from oracle import moe_oracle as O
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, s2r, r2s = O.permute_maps(idx, E)
+    return offsets, r2s
+
+
+def _kc_stage(src, ld, rows, bk, nw, k0, kvalid, row_src):
+    """LDS slots of a K-contiguous stage: slot -> 8 values.  row_src(row)
+    gives the source row of tile row `row` or None (reads zeros)."""
+    ni = rows * bk // 512 // nw
+    cpr, rpi = bk // 8, 64 // (bk // 8)
+    out = {}
+    for wave in range(nw):
+        for i in range(ni):
+            for lane in range(64):
+                row = rpi * (wave * ni + i) + lane // cpr
+                ch = (lane % cpr) ^ kc_swz(row, cpr)
+                r = row_src(row)
+                ok = r is not None and k0 + ch * 8 < kvalid
+                out[(wave * ni + i) * 64 + lane] = (
+                    tuple(src[r, k0 + ch * 8:k0 + ch * 8 + 8]) if ok else (0,) * 8)
+    return out
+
+
+@pytest.mark.parametrize("T,d,E,k,bq", [(300, 328, 6, 2, 256), (257, 128, 5, 5, 128),
+                                        (64, 72, 3, 1, 256)])
+def test_gathered_token_rows_land_where_stored_rows_do(T, d, E, k, bq):
+    nw, bk = 8, BK
+    offsets, r2s = _perm_case(T, E, k, 7)
+    x = np.arange(T * d, dtype=np.int64).reshape(T, d) + 1        # distinct values
+    x_perm = x[r2s // k]
+    tok = [slot_token(int(s), k) for s in r2s]
+    for e in range(E):
+        seg0, Me = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+        for q0 in range(0, Me, bq):
+            for k0 in range(0, d, bk):
+                # stored rows: tile rows past the segment read nothing
+                st = _kc_stage(x_perm, d, bq, bk, nw, k0, d,
+                               lambda row: seg0 + q0 + row if q0 + row < Me else None)
+                # gathered: row -> token of the sorted row
+                ga = _kc_stage(x, d, bq, bk, nw, k0, d,
+                               lambda row: tok[seg0 + q0 + row] if q0 + row < Me else None)
+                assert st == ga, (e, q0, k0)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 328, 6, 2), (200, 520, 3, 3)])
+def test_gathered_x_krows_land_where_stored_rows_do(T, d, E, k):
+    """dW_gu's X operand: a stage of 32 token k-rows x 256 columns; the ring
+    entry of wave w holds the slots of k-rows KRW*w .. KRW*w + KRW-1, loaded by
+    lanes 0..KRW-1; columns past d feed only masked outputs and are skipped."""
+    nw, bk, rows, ni = 8, 32, 256, 2
+    c16n = rows // 8
+    krw = ni * 64 // c16n
+    offsets, r2s = _perm_case(T, E, k, 9)
+    x = np.arange(T * d, dtype=np.int64).reshape(T, d) + 1
+    x_perm = x[r2s // k]
+    for e in range(E):
+        seg0, Me = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+        for p0 in range(0, d, rows):
+            for k0 in range(0, Me, bk):
+                for wave in range(nw):
+                    # the ring entry: lane l < KRW loads row_to_slot[seg0 + k0 + KRW*wave + l]
+                    # from a resource of max(0, Me - k0) slots (zero past it)
+                    ent = [int(r2s[seg0 + k0 + krw * wave + l]) if krw * wave + l < Me - k0 else 0
+                           for l in range(krw)]
+                    for i in range(ni):
+                        for lane in range(64):
+                            lin = (wave * ni + i) * 64 + lane
+                            kr = lin // c16n
+                            c16 = (lin % c16n) ^ (tr_swz(kr) << 1)
+                            assert 0 <= kr - krw * wave < krw
+                            col = p0 + c16 * 8
+                            if col >= d:
+                                continue
+                            if k0 + kr < Me:
+                                want = tuple(x_perm[seg0 + k0 + kr, col:col + 8])
+                                t = slot_token(ent[kr - krw * wave], k)
+                                got = tuple(x[t, col:col + 8])
+                            else:
+                                want = got = (0,) * 8
+                            assert got == want, (e, p0, k0, wave, i, lane)

@@ -1,0 +1,124 @@
+"""GPU parity of the gathered grouped FFN (moe_grouped_ffn_fwd_gather,
+moe_grouped_ffn_bwd_gather): the block with dY_perm never stored, the GEMMs
+reading token rows of X and dY through row_to_slot -- with X_perm still
+stored for the dW_gu GEMM (the block's default gathered mode) and with
+X_perm never stored either (the dW_gu GEMM gathering X too).
+
+The gathered kernels load the same values into the same places and add them
+in the same order as the stored-row path, so every output must equal the
+stored-row block's bit for bit.  The gathered block is also checked against
+the oracle directly, with the block bounds (max-abs 2e-2, rel-L2 5e-3; the
+one-bf16-ulp allowance for sums of bf16-stored intermediates).
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_layer_03_amd import inputs as I
+from tests.gpu_util import close, down, need_gpu, up
+from tests.test_gpu_parity import FLIP_BWD, SMALL, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "slot_to_row", "row_to_slot",
+        "w_perm", "gu", "h", "y_perm", "y", "dgu", "dx_perm", "d_row_scale", "d_topk_w",
+        "d_logits", "dw_r", "dw_gu", "dw_down", "dx")
+
+
+def run_block(w, a, gather, store_x_perm=True):
+    import torch
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+    dev = need_gpu()
+    print("GPU case", w.name, "gather" if gather else "stored rows",
+          "" if store_x_perm else "(no x_perm)", flush=True)
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, device=dev, gather=gather, store_x_perm=store_x_perm)
+    assert (blk.dy_perm is None) == gather
+    assert (blk.x_perm is None) == (gather and not store_x_perm)
+    x, wr, wgu, wd = (up(a[n], True, dev) for n in ("x", "w_r", "w_gu", "w_down"))
+    bias = None if a["bias"] is None else up(a["bias"], False, dev)
+    noise = None if a["noise"] is None else up(a["noise"], False, dev)
+    blk.forward(x, wr, wgu, wd, bias, noise)
+    blk.backward(x, wr, wgu, wd, up(a["dy"], True, dev))
+    torch.cuda.synchronize()
+    return {n: down(getattr(blk, n)) for n in OUTS}
+
+
+def _same_bits(n, g, p):
+    g, p = np.asarray(g), np.asarray(p)
+    assert g.dtype == p.dtype and g.shape == p.shape, n
+    assert np.array_equal(g.view(np.uint8), p.view(np.uint8)), n
+
+
+def check_against_oracle(g, o, b):
+    for n in ("logits", "topk_idx", "counts", "offsets", "slot_to_row", "row_to_slot"):
+        assert np.array_equal(np.asarray(g[n]).view(np.uint8), np.asarray(o[n]).view(np.uint8)), n
+    close("topk_w", g["topk_w"], o["topk_w"], max_abs=1e-6, rel_l2=1e-6)
+    for n in ("gu", "h", "y_perm"):
+        close(n, g[n], o[n], flip=True)
+    close("y", g["y"], o["y"])
+    for n in FLIP_BWD:
+        close(n, g[n], b[n], flip=True)
+    close("dx", g["dx"], b["dx"])
+
+
+CASES = [w for w in SMALL if w.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_gathered_block_equals_stored_rows_and_matches_oracle(w):
+    a = I.make_inputs(w)
+    g = run_block(w, a, True)
+    n_ = run_block(w, a, True, store_x_perm=False)
+    p = run_block(w, a, False)
+    for n in OUTS:
+        _same_bits(n, g[n], p[n])
+        _same_bits(n, n_[n], p[n])
+    o, b = run_oracle(w, a)
+    check_against_oracle(g, o, b)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("w", [I.GPTOSS, I.GPTOSS_SKEW, I.QWEN3],
+                         ids=[w.name for w in (I.GPTOSS, I.GPTOSS_SKEW, I.QWEN3)])
+def test_gathered_block_equals_stored_rows_full_size(w):
+    """At the full workload sizes (the stored-row block is checked against the
+    oracle at these sizes by the full-size tests): bit for bit."""
+    a = I.make_inputs(w)
+    p = run_block(w, a, False)
+    for store in (True, False):
+        g = run_block(w, a, True, store_x_perm=store)
+        for n in OUTS:
+            _same_bits(n, g[n], p[n])
+        del g
+
+
+def test_gathered_calls_with_external_routing():
+    """Every token of one expert (the others empty), then k = 1 with the
+    token order reversed: the gathered calls against the stored-row calls on
+    the same maps."""
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+    dev = need_gpu()
+    T, d, E, f = 333, 200, 5, 72
+    w = I.Workload("external-T%d-d%d-E%d-f%d" % (T, d, E, f), T, d, E, 1, f, "bf16", True,
+                   "uniform", seed=31)
+    a = I.make_inputs(w)
+    x, wgu, wd, dy = (up(a[n], True, dev) for n in ("x", "w_gu", "w_down", "dy"))
+    for idx in (np.full((T, 1), 2, np.int32), (np.arange(T)[::-1] % E).astype(np.int32)[:, None]):
+        print("GPU case external routing", idx[:4, 0].tolist(), flush=True)
+        res = []
+        for gather, store in ((True, False), (True, True), (False, True)):
+            blk = MoEBlock(T, d, E, 1, f, device=dev, gather=gather, store_x_perm=store)
+            blk.topk_idx.copy_(torch.from_numpy(idx))
+            blk.topk_w.fill_(1.0)
+            blk.permute(x)
+            blk.experts_forward(wgu, wd, x=x)
+            if not gather:
+                abi.moe_combine_bwd(dy, blk.slot_to_row, 1, blk.dy_perm)
+            blk.experts_backward(wgu, wd, x=x, dy=dy)
+            torch.cuda.synchronize()
+            res.append({n: down(getattr(blk, n)) for n in (
+                "gu", "h", "y_perm", "dgu", "dx_perm", "d_row_scale", "dw_gu", "dw_down")})
+        for n in res[0]:
+            _same_bits(n, res[0][n], res[2][n])
+            _same_bits(n, res[1][n], res[2][n])
