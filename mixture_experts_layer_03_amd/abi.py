@@ -13,7 +13,9 @@ import ctypes
 import os
 from typing import Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# the in-tree build; MOE_LIBRARY names another build of the same sources
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK = 0
 MOE_F32 = 0
