@@ -1549,43 +1549,42 @@ constexpr int FG_BP = 256, FG_BQ = 128, FG_WP = 4, FG_WQ = 2, FG_NS = 3, FG_BK =
 constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK = 32;  // weight grads
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
-// down-projection weight gradient (bf16 rounding of the fp32 product).
+// down-projection weight gradient (bf16 rounding of the fp32 product).  One
+// wave per row r (four per block), 16-byte chunks; GATHER: dY_perm[r] is row
+// row_to_slot[r] / k of the unpermuted dY.
+template <bool GATHER>
 __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy,
-                                                   const float *__restrict__ w, int64_t R, int d,
-                                                   bf16_t *__restrict__ s) {
-  const int nvec = d / 8;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= R * nvec) return;
-  const int64_t r = i / nvec;
+                                                   const int32_t *__restrict__ row_to_slot,
+                                                   uint64_t kmagic, const float *__restrict__ w,
+                                                   int64_t R, int d, bf16_t *__restrict__ s) {
+  const int64_t r =
+      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (r >= R) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t src = GATHER ? (int64_t)slot_token(row_to_slot[r], kmagic) : r;
   const float wr = w ? w[r] : 1.0f;
-  const u32x4_t v = reinterpret_cast<const u32x4_t *>(dy)[i];
-  u32x4_t o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = pack_bf16x2(bf16_bits_to_f32(v[j] & 0xffffu) * wr, bf16_bits_to_f32(v[j] >> 16) * wr);
-  reinterpret_cast<u32x4_t *>(s)[i] = o;
-}
-
-// The same with the rows gathered from the unpermuted dY: S[r] =
-// store(w[r] * dY[token of row r]).
-__global__ __launch_bounds__(256) void k_row_scale_gather(const bf16_t *__restrict__ dy,
-                                                          const int32_t *__restrict__ row_to_slot,
-                                                          uint64_t kmagic,
-                                                          const float *__restrict__ w, int64_t R,
-                                                          int d, bf16_t *__restrict__ s) {
+  const u32x4_t *in = reinterpret_cast<const u32x4_t *>(dy + src * d);
+  u32x4_t *out = reinterpret_cast<u32x4_t *>(s + r * d);
   const int nvec = d / 8;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= R * nvec) return;
-  const int64_t r = i / nvec;
-  const int64_t c = i - r * nvec;
-  const float wr = w ? w[r] : 1.0f;
-  const int64_t t = slot_token(row_to_slot[r], kmagic);
-  const u32x4_t v = reinterpret_cast<const u32x4_t *>(dy + t * d)[c];
-  u32x4_t o;
+  for (int c0 = 0; c0 < nvec; c0 += 256) {
+    u32x4_t v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = pack_bf16x2(bf16_bits_to_f32(v[j] & 0xffffu) * wr, bf16_bits_to_f32(v[j] >> 16) * wr);
-  reinterpret_cast<u32x4_t *>(s)[i] = o;
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + j * 64 + lane;
+      if (c < nvec) v[j] = in[c];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + j * 64 + lane;
+      if (c >= nvec) continue;
+      u32x4_t o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(bf16_bits_to_f32(v[j][q] & 0xffffu) * wr,
+                           bf16_bits_to_f32(v[j][q] >> 16) * wr);
+      out[c] = o;
+    }
+  }
 }
 
 static inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
@@ -1788,15 +1787,15 @@ static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, flo
   if (rc) return rc;
   // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
   if (R > 0) {
-    const int64_t n = R * (d / 8);
+    const unsigned blocks = (unsigned)((R + 3) / 4);
     if (gather)
       MOE_LAUNCH("row_scale", s,
-                 k_row_scale_gather<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-                     gdy, a.row_to_slot, a.kmagic, a.row_scale, R, d, s_perm));
+                 k_row_scale<true><<<blocks, 256, 0, s>>>(gdy, a.row_to_slot, a.kmagic,
+                                                          a.row_scale, R, d, s_perm));
     else
       MOE_LAUNCH("row_scale", s,
-                 k_row_scale<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-                     a.dy_perm, a.row_scale, R, d, s_perm));
+                 k_row_scale<false><<<blocks, 256, 0, s>>>(a.dy_perm, nullptr, 0, a.row_scale,
+                                                           R, d, s_perm));
     rc = check_launch("moe_grouped_ffn_bwd(row scale)");
     if (rc) return rc;
   }
@@ -2202,10 +2201,9 @@ extern "C" int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, cons
   if (rc) return rc;
   // 3. S = store(w dY_perm) for dB_dn
   if (R > 0) {
-    const int64_t n = R * (d / 8);
     MOE_LAUNCH("row_scale", s,
-               k_row_scale<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-                   (const bf16_t *)dy_perm, row_scale, R, d, s_perm));
+               k_row_scale<false><<<(unsigned)((R + 3) / 4), 256, 0, s>>>(
+                   (const bf16_t *)dy_perm, nullptr, 0, row_scale, R, d, s_perm));
     rc = check_launch("moe_grouped_ffn_bwd_lora(row scale)");
     if (rc) return rc;
   }
