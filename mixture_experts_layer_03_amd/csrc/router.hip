@@ -338,7 +338,22 @@ __global__ __launch_bounds__(256) void k_router_dw_partial(const float *__restri
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int n = 0; n < total; ++n) {
+    // four rows' loads in flight, then their fmas in token order
+    int n = 0;
+    for (; n + 4 <= total; n += 4) {
+      Raw8 r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8_raw(x + (tbeg + s_tok[n + u]) * d + c, r[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float a = s_val[n + u];
+        float xv[8];
+        widen8<T>(r[u], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(a, xv[i], acc[i]);
+      }
+    }
+    for (; n < total; ++n) {
       const int64_t t = tbeg + s_tok[n];
       const float a = s_val[n];
       Raw8 r;
@@ -360,8 +375,18 @@ __global__ __launch_bounds__(256) void k_router_dw_reduce(const float *__restric
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)E * d) return;
   const int64_t e = i / d, c = i % d;
+  const float *p = partial + e * nchunk * d + c;
+  // eight chunks' loads in flight, summed in chunk order
   float s = 0.0f;
-  for (int ch = 0; ch < nchunk; ++ch) s += partial[(e * nchunk + ch) * d + c];
+  int ch = 0;
+  for (; ch + 8 <= nchunk; ch += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(ch + u) * d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; ch < nchunk; ++ch) s += p[(int64_t)ch * d];
   dw[i] = s;
 }
 
