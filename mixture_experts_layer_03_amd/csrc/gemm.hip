@@ -62,6 +62,7 @@ struct GemmArgs {
   uint64_t kmagic;
   int64_t gx_rows;
   int E, d, f;
+  const int32_t *wg_bounds;    // weight-gradient kinds: [9] per-XCD chunk bounds, or null
   int PT;                      // tiles along P
   int QT;                      // tiles along Q (weight-gradient kinds)
   int nlogical;                // weight-gradient kinds: E*PT*QT
@@ -789,9 +790,16 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     total = a.tile_start[a.E];
   }
   total = __builtin_amdgcn_readfirstlane(total);
+  // Token tiles cost about the same: equal counts per XCD.  A weight-gradient
+  // tile costs its expert's M_e K rows, so those chunks come cost-balanced
+  // from k_wg_bounds.
   const int chunk = (total + 7) >> 3;
-  const int cbeg = (blockIdx.x & 7) * chunk;
-  const int cend = min(total, cbeg + chunk);
+  int cbeg = (blockIdx.x & 7) * chunk;
+  int cend = min(total, cbeg + chunk);
+  if (KT::WG && a.wg_bounds) {
+    cbeg = __builtin_amdgcn_readfirstlane(a.wg_bounds[blockIdx.x & 7]);
+    cend = __builtin_amdgcn_readfirstlane(a.wg_bounds[(blockIdx.x & 7) + 1]);
+  }
   const int first = cbeg + (blockIdx.x >> 3);
   int32_t *const ctr = KT::WG ? nullptr : a.counters + (blockIdx.x & 7);
 #define MOE_FETCH() ({                                                                        \
@@ -1245,6 +1253,57 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict_
   if (e < 8) tsa[E + 1 + e] = tsb[E + 1 + e] = 0;   // the GEMMs' per-XCD tile counters
 }
 
+// Chunk bounds of the two weight-gradient GEMMs of a backward pass (PTa x QTa
+// and PTb x QTb tiles per expert, expert-major): 8 contiguous chunks of equal
+// modelled cost, one per XCD.  A tile of expert e costs ceil(M_e / BK) K
+// stages plus kWgTileCost stages' worth for its epilogue (an empty expert's
+// tiles only store zeros).  Bounds are rounded to multiples of the blocks per
+// XCD (pera, perb), which deal a chunk's tiles round-robin: when the costs
+// are even, chunks then split into whole rounds as equal counts would.
+// Chunk x is [bounds[x], bounds[x+1]).  One block.
+constexpr int kWgTileCost = 8;
+__global__ __launch_bounds__(1024) void k_wg_bounds(const int32_t *__restrict__ offsets, int E,
+                                                    int BK, int na, int pera,
+                                                    int32_t *__restrict__ ba, int nb, int perb,
+                                                    int32_t *__restrict__ bb) {
+  __shared__ long long s[1024];
+  const int e = threadIdx.x;
+  long long w = 0;
+  if (e < E) w = (offsets[e + 1] - offsets[e] + BK - 1) / BK + kWgTileCost;
+  s[e] = w;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // inclusive prefix of the per-tile costs
+    const long long t = e >= off ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += t;
+    __syncthreads();
+  }
+  // with n tiles per expert, the tiles before expert e cost n*lo and the
+  // whole GEMM n*W; chunk x starts at the first tile before which the cost
+  // reaches x*n*W/8: e*n + ceil((x*n*W/8 - n*lo) / w) for the expert holding
+  // that point
+  const long long W = s[E - 1], hi = s[e], lo = hi - w;
+  if (e < E) {
+#pragma unroll
+    for (int x = 1; x < 8; ++x) {
+      const long long ta = (long long)x * na * W / 8, tb = (long long)x * nb * W / 8;
+      if ((long long)na * lo <= ta && ta < (long long)na * hi) {
+        const int L = e * na + (int)((ta - (long long)na * lo + w - 1) / w);
+        ba[x] = min(E * na, (L + pera / 2) / pera * pera);
+      }
+      if ((long long)nb * lo <= tb && tb < (long long)nb * hi) {
+        const int L = e * nb + (int)((tb - (long long)nb * lo + w - 1) / w);
+        bb[x] = min(E * nb, (L + perb / 2) / perb * perb);
+      }
+    }
+  }
+  if (e == 0) {
+    ba[0] = bb[0] = 0;
+    ba[8] = E * na;
+    bb[8] = E * nb;
+  }
+}
+
 // d_row_scale[r] = sum of its partials in fixed order
 __global__ __launch_bounds__(256) void k_drs_reduce(const float *__restrict__ part, int nparts,
                                                     int64_t R, float *__restrict__ drs) {
@@ -1671,8 +1730,9 @@ static size_t drs_bytes(int64_t R, int f) {
 extern "C" size_t moe_grouped_ffn_workspace_size(int64_t R, int E, int d, int f, int dtype) {
   (void)dtype;
   if (R < 0 || E < 1 || f < 1 || d < 1) return 0;
-  // tile prefixes, d_row_scale partials, S = w * dY_perm (bf16)
-  return 2 * tile_start_bytes(E) + drs_bytes(R, f) + align_up(2 * (size_t)R * d, 256);
+  // tile prefixes, d_row_scale partials, S = w * dY_perm (bf16), the weight-
+  // gradient chunk bounds
+  return 2 * tile_start_bytes(E) + drs_bytes(R, f) + align_up(2 * (size_t)R * d, 256) + 256;
 }
 
 // bf16 forward: gate/up GEMM + SwiGLU, down GEMM + row scale.  gather: the
@@ -1800,12 +1860,25 @@ static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, flo
     rc = check_launch("moe_grouped_ffn_bwd(row scale)");
     if (rc) return rc;
   }
+  // weight-gradient chunks of equal modelled cost per XCD (skewed experts)
+  int32_t *wgb = (int32_t *)((char *)s_perm + align_up(2 * (size_t)R * d, 256));
+  const int pt_wd = (f + WG_BP - 1) / WG_BP, qt_wd = (d + WG_BQ - 1) / WG_BQ;
+  const int pt_wg = (d + WG_BP - 1) / WG_BP, qt_wg = (2 * f + WG_BQ - 1) / WG_BQ;
+  const int per_wd = persistent_grid((int64_t)E * pt_wd * qt_wd) / 8;
+  const int per_wg = persistent_grid((int64_t)E * pt_wg * qt_wg) / 8;
+  MOE_LAUNCH("wg_bounds", s,
+             k_wg_bounds<<<1, 1024, 0, s>>>(a.offsets, E, WG_BK, pt_wd * qt_wd, per_wd, wgb,
+                                            pt_wg * qt_wg, per_wg, wgb + 16));
+  rc = check_launch("moe_grouped_ffn_bwd(wg bounds)");
+  if (rc) return rc;
   a.s_perm = s_perm;
   a.o_dw = dw_down;
+  a.wg_bounds = wgb;
   rc = launch_wgrad_gemm<BWD_DWDOWN, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK>(a, f, d, "gg_bwd_dw_down", s);
   if (rc) return rc;
   // 4. dW_gu[e] = dGU^T X_perm        -> [E, 2f, d]
   a.o_dw = dw_gu;
+  a.wg_bounds = wgb + 16;
   if (gather && !a.x_perm)
     return launch_wgrad_gemm<BWD_DWGU, WG_BP, WG_BQ, WG_WP, WG_WQ, WG_NS, WG_BK, true>(
         a, d, 2 * f, "gg_bwd_dw_gate_up_gather", s);
