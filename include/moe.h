@@ -173,15 +173,17 @@ int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const void *h,
  * moe_grouped_ffn_fwd_gather: the results of moe_grouped_ffn_fwd with
  *   x_perm[r] = x[row_to_slot[r] / k]; x: [T,d] bf16, R = T*k.
  * moe_grouped_ffn_bwd_gather: the results of moe_grouped_ffn_bwd with that
- *   x_perm and dy_perm[r] = dy[row_to_slot[r] / k]; dy: [T,d] bf16.  x_perm:
+ *   x_perm and dy_perm[r] = dy[row_to_slot[r] / k]; dy: [T,d] bf16;
+ *   slot_to_row: [R], the inverse of row_to_slot (moe_permute writes both;
+ *   S = w * dY_perm is formed from dY in token order through it).  x_perm:
  *   [R,d] or NULL; when given (the forward's permuted rows), the dW_gu GEMM
  *   reads it instead of gathering X, and x may be NULL.
  * Every other argument, output and the workspace
  * (moe_grouped_ffn_workspace_size(T*k, E, d, f, MOE_BF16)) are those of the
  * plain calls; bf16 only.  Limits (else MOE_ERR_UNSUPPORTED): k <= 32,
  * T*d < 2^30, T*k*k < 2^32.  row_to_slot must hold a permutation of
- * 0..T*k-1 (as moe_permute writes it); other values are not checked and
- * index outside x and dy.
+ * 0..T*k-1 and slot_to_row its inverse (as moe_permute writes them); other
+ * values are not checked and index outside x, dy and the outputs.
  */
 int moe_grouped_ffn_fwd_gather(const void *x, int64_t T, const int32_t *row_to_slot, int k,
                                const int32_t *offsets, int E, int d, int f,
@@ -189,7 +191,8 @@ int moe_grouped_ffn_fwd_gather(const void *x, int64_t T, const int32_t *row_to_s
                                void *gu, void *h, void *y_perm,
                                void *ws, size_t ws_bytes, void *stream);
 int moe_grouped_ffn_bwd_gather(const void *x, const void *x_perm, const void *dy, int64_t T,
-                               const int32_t *row_to_slot, int k, const void *gu, const void *h,
+                               const int32_t *row_to_slot, const int32_t *slot_to_row, int k,
+                               const void *gu, const void *h,
                                const int32_t *offsets, int E, int d, int f,
                                const void *w_gu, const void *w_down, const float *row_scale,
                                void *dgu, void *dx_perm, float *dw_gu, float *dw_down,

@@ -80,8 +80,8 @@ _SIGS = {
     "moe_grouped_ffn_fwd_gather": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p, _i32,
                                           _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                           _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
-    "moe_grouped_ffn_bwd_gather": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i32,
-                                          _c_void_p,
+    "moe_grouped_ffn_bwd_gather": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _i32, _c_void_p,
                                           _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                           _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
@@ -203,14 +203,15 @@ def moe_grouped_ffn_fwd_gather(x, row_to_slot, k, offsets, E, w_gu, w_down, row_
         _p(gu), _p(h), _p(y_perm), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def moe_grouped_ffn_bwd_gather(x, dy, row_to_slot, k, gu, h, offsets, E, w_gu, w_down, row_scale,
-                               dgu, dx_perm, dw_gu, dw_down, d_row_scale, ws, stream=None,
-                               x_perm=None):
+def moe_grouped_ffn_bwd_gather(x, dy, row_to_slot, slot_to_row, k, gu, h, offsets, E, w_gu,
+                               w_down, row_scale, dgu, dx_perm, dw_gu, dw_down, d_row_scale, ws,
+                               stream=None, x_perm=None):
     """x_perm given: the dW_gu GEMM reads it instead of gathering x."""
     T, d = dy.shape
     f = w_down.shape[2]
     _check("moe_grouped_ffn_bwd_gather", lib().moe_grouped_ffn_bwd_gather(
-        _p(x), _p(x_perm), _p(dy), T, _p(row_to_slot), k, _p(gu), _p(h), _p(offsets), E, d, f,
+        _p(x), _p(x_perm), _p(dy), T, _p(row_to_slot), _p(slot_to_row), k, _p(gu), _p(h),
+        _p(offsets), E, d, f,
         _p(w_gu), _p(w_down), _p(row_scale), _p(dgu), _p(dx_perm), _p(dw_gu), _p(dw_down),
         _p(d_row_scale), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 

@@ -1610,20 +1610,16 @@ constexpr int WG_BP = 256, WG_BQ = 256, WG_WP = 2, WG_WQ = 4, WG_NS = 4, WG_BK =
 
 // S = store(w * dY_perm): the row-scaled upstream gradient of the
 // down-projection weight gradient (bf16 rounding of the fp32 product).  One
-// wave per row r (four per block), 16-byte chunks; GATHER: dY_perm[r] is row
-// row_to_slot[r] / k of the unpermuted dY.
-template <bool GATHER>
+// wave per row r (four per block), 16-byte chunks.
 __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy,
-                                                   const int32_t *__restrict__ row_to_slot,
-                                                   uint64_t kmagic, const float *__restrict__ w,
-                                                   int64_t R, int d, bf16_t *__restrict__ s) {
+                                                   const float *__restrict__ w, int64_t R, int d,
+                                                   bf16_t *__restrict__ s) {
   const int64_t r =
       (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (r >= R) return;
   const int lane = threadIdx.x & 63;
-  const int64_t src = GATHER ? (int64_t)slot_token(row_to_slot[r], kmagic) : r;
   const float wr = w ? w[r] : 1.0f;
-  const u32x4_t *in = reinterpret_cast<const u32x4_t *>(dy + src * d);
+  const u32x4_t *in = reinterpret_cast<const u32x4_t *>(dy + r * d);
   u32x4_t *out = reinterpret_cast<u32x4_t *>(s + r * d);
   const int nvec = d / 8;
   for (int c0 = 0; c0 < nvec; c0 += 256) {
@@ -1644,6 +1640,47 @@ __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy
                            bf16_bits_to_f32(v[j][q] >> 16) * wr);
       out[c] = o;
     }
+  }
+}
+
+// The same from the unpermuted dY in token order: each token row is read
+// once and its k scaled copies written, S[slot_to_row[t*k+j]] =
+// store(w[that row] * dY[t]).  One wave per (token, piece of 128 16-byte
+// chunks), two chunks per lane.
+constexpr int kRsPiece = 128;
+__global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restrict__ dy,
+                                                           const int32_t *__restrict__ slot_to_row,
+                                                           const float *__restrict__ w,
+                                                           int64_t ntok, int d, int k,
+                                                           bf16_t *__restrict__ s) {
+  const int nvec = d / 8;
+  const int pieces = (nvec + kRsPiece - 1) / kRsPiece;
+  const int64_t wid =
+      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t t = wid / pieces;
+  if (t >= ntok) return;
+  const int lane = threadIdx.x & 63;
+  const int ca = (int)(wid - t * pieces) * kRsPiece + lane, cb = ca + 64;
+  const bool va = ca < nvec, vb = cb < nvec;
+  const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
+  const float myw = (myr >= 0 && w) ? w[myr] : 1.0f;
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(dy + t * d);
+  u32x4_t xa = {0u, 0u, 0u, 0u}, xb = xa;
+  if (va) xa = src[ca];
+  if (vb) xb = src[cb];
+  for (int j = 0; j < k; ++j) {
+    const int r = __builtin_amdgcn_readlane(myr, j);
+    if (r < 0) continue;
+    const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), j));
+    u32x4_t *o = reinterpret_cast<u32x4_t *>(s + (int64_t)r * d);
+    u32x4_t ya, yb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ya[q] = pack_bf16x2(bf16_bits_to_f32(xa[q] & 0xffffu) * wr, bf16_bits_to_f32(xa[q] >> 16) * wr);
+      yb[q] = pack_bf16x2(bf16_bits_to_f32(xb[q] & 0xffffu) * wr, bf16_bits_to_f32(xb[q] >> 16) * wr);
+    }
+    if (va) o[ca] = ya;
+    if (vb) o[cb] = yb;
   }
 }
 
@@ -1808,7 +1845,8 @@ extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, i
 // the unpermuted dY = gdy through a.row_to_slot, and without a.x_perm the
 // dW_gu GEMM reads X = a.gx the same way.
 static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, float *d_row_scale,
-                        const bf16_t *gdy, void *ws, hipStream_t s) {
+                        const bf16_t *gdy, const int32_t *slot_to_row, int k, void *ws,
+                        hipStream_t s) {
   const int E = a.E, d = a.d, f = a.f;
   const bool gather = gdy != nullptr;
   int32_t *ts0 = (int32_t *)ws;
@@ -1849,14 +1887,15 @@ static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, flo
   // 3. dW_down[e] = S^T H with S = store(w*dY_perm)   -> [E, d, f]
   if (R > 0) {
     const unsigned blocks = (unsigned)((R + 3) / 4);
-    if (gather)
+    if (gather) {
+      const int64_t T = R / k;
+      const int64_t waves = T * ((d / 8 + kRsPiece - 1) / kRsPiece);
       MOE_LAUNCH("row_scale", s,
-                 k_row_scale<true><<<blocks, 256, 0, s>>>(gdy, a.row_to_slot, a.kmagic,
-                                                          a.row_scale, R, d, s_perm));
-    else
+                 k_row_scale_scatter<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(
+                     gdy, slot_to_row, a.row_scale, T, d, k, s_perm));
+    } else
       MOE_LAUNCH("row_scale", s,
-                 k_row_scale<false><<<blocks, 256, 0, s>>>(a.dy_perm, nullptr, 0, a.row_scale,
-                                                           R, d, s_perm));
+                 k_row_scale<<<blocks, 256, 0, s>>>(a.dy_perm, a.row_scale, R, d, s_perm));
     rc = check_launch("moe_grouped_ffn_bwd(row scale)");
     if (rc) return rc;
   }
@@ -1923,7 +1962,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *x_perm, const void *gu, const voi
   a.E = E;
   a.d = d;
   a.f = f;
-  return ffn_bwd_bf16(a, R, dw_gu, dw_down, d_row_scale, nullptr, ws, s);
+  return ffn_bwd_bf16(a, R, dw_gu, dw_down, d_row_scale, nullptr, nullptr, 1, ws, s);
 }
 
 // ====================================================================== gathered rows
@@ -1985,8 +2024,8 @@ extern "C" int moe_grouped_ffn_fwd_gather(const void *x, int64_t T, const int32_
 }
 
 extern "C" int moe_grouped_ffn_bwd_gather(const void *x, const void *x_perm, const void *dy,
-                                          int64_t T,
-                                          const int32_t *row_to_slot, int k, const void *gu,
+                                          int64_t T, const int32_t *row_to_slot,
+                                          const int32_t *slot_to_row, int k, const void *gu,
                                           const void *h, const int32_t *offsets, int E, int d,
                                           int f, const void *w_gu, const void *w_down,
                                           const float *row_scale, void *dgu, void *dx_perm,
@@ -2000,8 +2039,8 @@ extern "C" int moe_grouped_ffn_bwd_gather(const void *x, const void *x_perm, con
   if (rc) return rc;
   MOE_REQUIRE(offsets && w_gu && w_down && dw_gu && dw_down, MOE_ERR_INVALID_ARG,
               "moe_grouped_ffn_bwd_gather: null pointer");
-  MOE_REQUIRE(R == 0 || ((x || x_perm) && dy && gu && h && dgu && dx_perm), MOE_ERR_INVALID_ARG,
-              "moe_grouped_ffn_bwd_gather: null activation pointer");
+  MOE_REQUIRE(R == 0 || ((x || x_perm) && dy && gu && h && dgu && dx_perm && slot_to_row),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd_gather: null activation or map pointer");
   MOE_REQUIRE(aligned16(w_gu) && aligned16(w_down) && aligned16(dw_gu) && aligned16(dw_down) &&
                   (R == 0 || (aligned16(x) && aligned16(x_perm) && aligned16(dy) &&
                               aligned16(gu) && aligned16(h) && aligned16(dgu) &&
@@ -2029,7 +2068,7 @@ extern "C" int moe_grouped_ffn_bwd_gather(const void *x, const void *x_perm, con
   a.E = E;
   a.d = d;
   a.f = f;
-  return ffn_bwd_bf16(a, R, dw_gu, dw_down, d_row_scale, (const bf16_t *)dy, ws,
+  return ffn_bwd_bf16(a, R, dw_gu, dw_down, d_row_scale, (const bf16_t *)dy, slot_to_row, k, ws,
                       (hipStream_t)stream);
 }
 
@@ -2276,8 +2315,8 @@ extern "C" int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, cons
   // 3. S = store(w dY_perm) for dB_dn
   if (R > 0) {
     MOE_LAUNCH("row_scale", s,
-               k_row_scale<false><<<(unsigned)((R + 3) / 4), 256, 0, s>>>(
-                   (const bf16_t *)dy_perm, nullptr, 0, row_scale, R, d, s_perm));
+               k_row_scale<<<(unsigned)((R + 3) / 4), 256, 0, s>>>(
+                   (const bf16_t *)dy_perm, row_scale, R, d, s_perm));
     rc = check_launch("moe_grouped_ffn_bwd_lora(row scale)");
     if (rc) return rc;
   }

@@ -187,7 +187,8 @@ class MoEBlock:
 
     def experts_backward(self, w_gu, w_down, stream=None, lora=None, x=None, dy=None):
         if self.gather:
-            abi.moe_grouped_ffn_bwd_gather(x, dy, self.row_to_slot, self.k, self.gu, self.h,
+            abi.moe_grouped_ffn_bwd_gather(x, dy, self.row_to_slot, self.slot_to_row, self.k,
+                                           self.gu, self.h,
                                            self.offsets, self.E, w_gu, w_down, self.w_perm,
                                            self.dgu, self.dx_perm, self.dw_gu, self.dw_down,
                                            self.d_row_scale, self.ws, stream,

@@ -144,18 +144,23 @@ def test_gather_ffn_validation_rejects_before_launch():
     assert fwd(None, 0, None, 4, None, 8, 64, 64, None, None, None, None, None, None, None, 0,
                None) == 0
     bwd = L.moe_grouped_ffn_bwd_gather
-    args = [P, None, P, 100, P, 4, P, P, P, 8, 64, 64, P, P, None, P, P, P, P, None, P, ws, None]
+    # x, x_perm, dy, T, row_to_slot, slot_to_row, k, gu, h, offsets, E, d, f, w_gu, w_down,
+    # row_scale, dgu, dx_perm, dw_gu, dw_down, d_row_scale, ws, ws_bytes, stream
+    args = [P, None, P, 100, P, P, 4, P, P, P, 8, 64, 64, P, P, None, P, P, P, P, None, P, ws,
+            None]
     a = list(args); a[2] = None                      # dy
     assert bwd(*a) == -1
     a = list(args); a[0] = None                      # neither x nor x_perm
     assert bwd(*a) == -1
     a = list(args); a[4] = None                      # row_to_slot
     assert bwd(*a) == -1
-    a = list(args); a[5] = 0                         # k
+    a = list(args); a[5] = None                      # slot_to_row
+    assert bwd(*a) == -1
+    a = list(args); a[6] = 0                         # k
     assert bwd(*a) == -2
-    a = list(args); a[21] = 16                       # workspace
+    a = list(args); a[22] = 16                       # workspace
     assert bwd(*a) == -3
-    a = list(args); a[17] = ctypes.c_void_p(0x1004)  # dw_gu alignment
+    a = list(args); a[18] = ctypes.c_void_p(0x1004)  # dw_gu alignment
     assert bwd(*a) == -1
     a = list(args); a[1] = ctypes.c_void_p(0x1008)   # x_perm alignment
     assert bwd(*a) == -1
