@@ -646,6 +646,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
     const int Pdim = (KIND == BWD_DWDOWN) ? f : d;
     const int Qdim = (KIND == BWD_DWDOWN) ? d : (int)f2;
     float *out = a.o_dw + (int64_t)t.e * Pdim * Qdim;
+    // The fp32 gradients are written once and not read again here: the
+    // stores are non-temporal, so they do not displace the operand slabs the
+    // tiles in flight share in L2 (measured: dW_down -3.5%, dW_gu -1.4%).
     // Fragments i and i+1 (P rows 16 apart) are stored together: lane
     // (g, c) of fragment i+1, rotated by 8 within its 16-lane row, trades
     // places so that one store covers Q rows c%8 with P columns 0..31 of the
@@ -671,9 +674,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
         }
         const int pA = pa + prow[i], pB = pb_ + prow[i];
         if (qA < Qdim && pA < Pdim)
-          *reinterpret_cast<f32x4_t *>(out + (int64_t)qA * Pdim + pA) = A;
+          __builtin_nontemporal_store(A, reinterpret_cast<f32x4_t *>(out + (int64_t)qA * Pdim + pA));
         if (qB < Qdim && pB < Pdim)
-          *reinterpret_cast<f32x4_t *>(out + (int64_t)qB * Pdim + pB) = B;
+          __builtin_nontemporal_store(B, reinterpret_cast<f32x4_t *>(out + (int64_t)qB * Pdim + pB));
       }
     }
   }
