@@ -66,6 +66,20 @@ def gemm_bytes(R, d, f, E):
     }
 
 
+def row_bytes(T, d, E, k):
+    """Algorithmic HBM bytes of the row kernels (bf16 rows, int32 maps, fp32
+    weights): each token row and each routed row read or written once."""
+    R = T * k
+    tok, rows = 2.0 * T * d, 2.0 * R * d
+    return {
+        "permute_rows": tok + rows + 4.0 * R + 4.0 * R + 4.0 * R,  # + slot_to_row, topk_w, w_perm
+        "combine": rows + tok + 4.0 * R,
+        "combine_bwd": tok + rows + 4.0 * R,
+        "row_scale": tok + rows + 4.0 * R + 4.0 * R,                # dY once (token order) + w
+        "permute_bwd": rows + tok + 4.0 * R + 4.0 * T * E + 2.0 * E * d,  # + d_logits, W_r
+    }
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/hbm_traffic.json), or None if the summary is for another
@@ -368,6 +382,22 @@ def main():
         gemm_frac = tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS
         gemm_roof_frac = sum(max(t_mfma[n], t_hbm[n]) for n in gemm_us) / tot_t
 
+    # row kernels (permute, combine and their adjoints, S) against HBM, and the
+    # layer's roofline fraction: the summed roofline times of the GEMMs and
+    # row kernels over the measured step
+    rows_out, layer_roof_frac = {}, None
+    rb = row_bytes(w.T, w.d, w.E, w.k)
+    for n, b in rb.items():
+        if n in kernels:
+            us = kernels[n]["avg_us"]
+            gbs = b / (us * 1e-6) / 1e9
+            rows_out[n] = {"avg_us": round(us, 1), "algorithmic_bytes": b,
+                           "GB_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if gemm_us:
+        roof = sum(max(t_mfma[n], t_hbm[n]) for n in gemm_us)
+        roof += sum(rb[n] / (PEAK_HBM_GBS * 1e9) for n in rows_out)
+        layer_roof_frac = roof / (ms_per_step * 1e-3)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
@@ -394,6 +424,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
+        "row_kernels": rows_out,
+        "layer_roofline_frac": None if layer_roof_frac is None else round(layer_roof_frac, 4),
         "router_variants": variants,
         "lora": lora_out,
         "rows": args.rows,
