@@ -61,17 +61,29 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t *__restrict__ idx, i
 }
 
 // Exclusive scan of n = E*nchunk ints (expert-major) by one block of 1024.
+// Each thread sums a contiguous run (eight loads in flight at a time), the
+// run sums are scanned in LDS, then each run is rescanned into base[];
+// counts come from the per-expert offsets.
 __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ hist, int E, int nchunk,
                                                int32_t *__restrict__ base,
                                                int32_t *__restrict__ counts,
                                                int32_t *__restrict__ offsets) {
   __shared__ int part[1024];
+  __shared__ int s_off[kMaxExperts + 1];
   const int64_t n = (int64_t)E * nchunk;
   const int64_t per = (n + 1023) / 1024;
   const int64_t b = threadIdx.x * per;
   const int64_t e_ = min(b + per, n);
   int sum = 0;
-  for (int64_t i = b; i < e_; ++i) sum += hist[i];
+  int64_t i = b;
+  for (; i + 8 <= e_; i += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hist[i + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; i < e_; ++i) sum += hist[i];
   part[threadIdx.x] = sum;
   __syncthreads();
   // Hillis-Steele inclusive scan over the 1024 partial sums
@@ -82,16 +94,28 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t *__restrict__ hist,
     __syncthreads();
   }
   int run = threadIdx.x ? part[threadIdx.x - 1] : 0;
-  for (int64_t i = b; i < e_; ++i) {
-    if (i % nchunk == 0) offsets[i / nchunk] = run;   // first chunk of expert i/nchunk
+  i = b;
+  for (; i + 8 <= e_; i += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hist[i + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if ((i + u) % nchunk == 0) s_off[(i + u) / nchunk] = run;   // first chunk of an expert
+      base[i + u] = run;
+      run += v[u];
+    }
+  }
+  for (; i < e_; ++i) {
+    if (i % nchunk == 0) s_off[i / nchunk] = run;
     base[i] = run;
     run += hist[i];
   }
-  if (threadIdx.x == 1023) offsets[E] = part[1023];
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    int c = 0;
-    for (int ch = 0; ch < nchunk; ++ch) c += hist[(int64_t)e * nchunk + ch];
-    counts[e] = c;
+  if (threadIdx.x == 1023) s_off[E] = part[1023];
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += 1024) {
+    offsets[e] = s_off[e];
+    if (e < E) counts[e] = s_off[e + 1] - s_off[e];
   }
 }
 

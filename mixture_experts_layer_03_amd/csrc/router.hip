@@ -178,7 +178,8 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 
 // With a selection bias (nullable) the compared value is the fp32 sum
 // logit + sel_bias[e]; the softmax always takes the selected logits alone.
-template <int G>
+// VPL: experts per lane, ceil(E / G) rounded up to a power of two.
+template <int G, int VPL>
 __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
                                                const float *__restrict__ sel_bias, int64_t ntok,
                                                int E, int k, int32_t *__restrict__ topk_idx,
@@ -187,11 +188,12 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
   const int s = lane % G;
   const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G;
   const bool live = t < ntok;
+  static_assert(VPL >= 1 && VPL <= kMaxPerLane, "experts per lane");
   const int vpl = (E + G - 1) / G;
-  float val[kMaxPerLane];
+  float val[VPL];
   unsigned taken = 0u;
 #pragma unroll
-  for (int v = 0; v < kMaxPerLane; ++v) {
+  for (int v = 0; v < VPL; ++v) {
     const int e = s + v * G;
     const bool ok = v < vpl && e < E;
     val[v] = (live && ok) ? logits[t * E + e] : 0.0f;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
     float bv = 0.0f;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int v = 0; v < kMaxPerLane; ++v) {
+    for (int v = 0; v < VPL; ++v) {
       if (taken & (1u << v)) continue;
       const int e = s + v * G;
       if (bi == 0x7fffffff || better(val[v], e, bv, bi)) {
@@ -495,14 +497,27 @@ static int route_impl(const float *logits, const float *sel_bias, int64_t T, int
   const int64_t threads = T * G;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   const char *name = sel_bias ? "route_topk_biased" : "route_topk";
-#define ROUTE_CASE(GV)                                                                        \
-  case GV:                                                                                    \
-    MOE_LAUNCH(name, s,                                                                       \
-               k_route<GV><<<blocks, 256, 0, s>>>(logits, sel_bias, T, E, k, topk_idx, topk_w)); \
-    break
+  int vpl = 1;   // experts per lane of a 64-lane group, a power of two
+  while (vpl * G < E) vpl <<= 1;
+#define ROUTE_CASE(GV, VV)                                                                    \
+  MOE_LAUNCH(name, s,                                                                         \
+             (k_route<GV, VV><<<blocks, 256, 0, s>>>(logits, sel_bias, T, E, k, topk_idx,      \
+                                                     topk_w)))
   switch (G) {
-    ROUTE_CASE(1); ROUTE_CASE(2); ROUTE_CASE(4); ROUTE_CASE(8);
-    ROUTE_CASE(16); ROUTE_CASE(32); ROUTE_CASE(64);
+    case 1: ROUTE_CASE(1, 1); break;
+    case 2: ROUTE_CASE(2, 1); break;
+    case 4: ROUTE_CASE(4, 1); break;
+    case 8: ROUTE_CASE(8, 1); break;
+    case 16: ROUTE_CASE(16, 1); break;
+    case 32: ROUTE_CASE(32, 1); break;
+    default:
+      switch (vpl) {
+        case 1: ROUTE_CASE(64, 1); break;
+        case 2: ROUTE_CASE(64, 2); break;
+        case 4: ROUTE_CASE(64, 4); break;
+        case 8: ROUTE_CASE(64, 8); break;
+        default: ROUTE_CASE(64, 16); break;
+      }
   }
 #undef ROUTE_CASE
   return check_launch(fn);
