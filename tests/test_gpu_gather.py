@@ -122,3 +122,41 @@ def test_gathered_calls_with_external_routing():
         for n in res[0]:
             _same_bits(n, res[0][n], res[2][n])
             _same_bits(n, res[1][n], res[2][n])
+
+
+def test_gathered_forward_without_saved_gu_and_empty_batch():
+    """Forward only (gu not kept): H and Y_perm as with gu kept.  An empty
+    batch: the gathered backward writes zero weight gradients."""
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+    dev = need_gpu()
+    w = CASES[0]
+    print("GPU case gathered forward without gu", w.name, flush=True)
+    a = I.make_inputs(w)
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, device=dev, gather=True)
+    x, wr, wgu, wd = (up(a[n], True, dev) for n in ("x", "w_r", "w_gu", "w_down"))
+    blk.forward(x, wr, wgu, wd)
+    torch.cuda.synchronize()
+    h1, y1 = down(blk.h), down(blk.y_perm)
+    blk.h.zero_()
+    blk.y_perm.zero_()
+    abi.moe_grouped_ffn_fwd_gather(x, blk.row_to_slot, w.k, blk.offsets, w.E, wgu, wd,
+                                   blk.w_perm, None, blk.h, blk.y_perm, blk.ws)
+    torch.cuda.synchronize()
+    _same_bits("h", down(blk.h), h1)
+    _same_bits("y_perm", down(blk.y_perm), y1)
+
+    print("GPU case gathered empty batch", flush=True)
+    E, d, f = 4, 64, 64
+    e = MoEBlock(0, d, E, 2, f, device=dev, gather=True)
+    z = torch.zeros(0, d, dtype=torch.bfloat16, device=dev)
+    wr0 = torch.zeros(E, d, dtype=torch.bfloat16, device=dev)
+    wgu0 = torch.zeros(E, 2 * f, d, dtype=torch.bfloat16, device=dev)
+    wd0 = torch.zeros(E, d, f, dtype=torch.bfloat16, device=dev)
+    e.forward(z, wr0, wgu0, wd0)
+    e.dw_gu.fill_(7.0)
+    e.dw_down.fill_(7.0)
+    e.backward(z, wr0, wgu0, wd0, z)
+    torch.cuda.synchronize()
+    assert float(e.dw_gu.abs().max()) == 0.0 and float(e.dw_down.abs().max()) == 0.0
