@@ -1447,7 +1447,7 @@ __global__ __launch_bounds__(256) void k_lora_proj(const bf16_t *__restrict__ in
   for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const int nsteps = (K + 31) / 32;
-  constexpr int U = NR == 1 ? 8 : 4;   // steps in flight per wave
+  constexpr int U = NR == 1 ? 16 : 8;   // steps in flight per wave
   // every pass issues the loads of U steps (steps past the end load zeros),
   // so the last, partial pass keeps its loads in flight together too
   for (int st = wave; st < nsteps; st += 4 * U) {
