@@ -393,6 +393,29 @@ def main():
             gbs = b / (us * 1e-6) / 1e9
             rows_out[n] = {"avg_us": round(us, 1), "algorithmic_bytes": b,
                            "GB_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    # context for the row kernels: a plain device copy (torch's) moving as
+    # many bytes as the forward permute (half read, half written), timed per
+    # launch with events like the library's kernels
+    copy_out = None
+    if "permute_rows" in rows_out:
+        cb = int(rb["permute_rows"]) // 2 // 16 * 16
+        csrc = torch.ones(cb // 4, dtype=torch.float32, device=dev)
+        cdst = torch.empty_like(csrc)
+        for _ in range(3):
+            cdst.copy_(csrc)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            cdst.copy_(csrc)
+            e1.record()
+        torch.cuda.synchronize()
+        us = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / len(evs)
+        gbs = 2 * cb / (us * 1e-6) / 1e9
+        copy_out = {"bytes": 2 * cb, "avg_us": round(us, 1), "GB_s": round(gbs, 1),
+                    "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del csrc, cdst
     if gemm_us:
         roof = sum(max(t_mfma[n], t_hbm[n]) for n in gemm_us)
         roof += sum(rb[n] / (PEAK_HBM_GBS * 1e9) for n in rows_out)
@@ -425,6 +448,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {n: round(v["avg_us"], 1) for n, v in kernels.items()},
         "row_kernels": rows_out,
+        "device_copy_same_bytes": copy_out,
         "layer_roofline_frac": None if layer_roof_frac is None else round(layer_roof_frac, 4),
         "router_variants": variants,
         "lora": lora_out,

@@ -1648,9 +1648,9 @@ __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy
 
 // The same from the unpermuted dY in token order: each token row is read
 // once and its k scaled copies written, S[slot_to_row[t*k+j]] =
-// store(w[that row] * dY[t]).  One wave per (token, piece of 128 16-byte
-// chunks), two chunks per lane.
-constexpr int kRsPiece = 128;
+// store(w[that row] * dY[t]).  One wave per (token, piece of 192 16-byte
+// chunks), three chunks per lane (two pieces per 2880-wide bf16 row).
+constexpr int kRsNch = 3, kRsPiece = 64 * kRsNch;
 __global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restrict__ dy,
                                                            const int32_t *__restrict__ slot_to_row,
                                                            const float *__restrict__ w,
@@ -1663,27 +1663,29 @@ __global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restr
   const int64_t t = wid / pieces;
   if (t >= ntok) return;
   const int lane = threadIdx.x & 63;
-  const int ca = (int)(wid - t * pieces) * kRsPiece + lane, cb = ca + 64;
-  const bool va = ca < nvec, vb = cb < nvec;
+  const int c0 = (int)(wid - t * pieces) * kRsPiece + lane;   // chunk h: c0 + 64 h
   const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
   const float myw = (myr >= 0 && w) ? w[myr] : 1.0f;
   const u32x4_t *src = reinterpret_cast<const u32x4_t *>(dy + t * d);
-  u32x4_t xa = {0u, 0u, 0u, 0u}, xb = xa;
-  if (va) xa = src[ca];
-  if (vb) xb = src[cb];
+  u32x4_t x[kRsNch];
+#pragma unroll
+  for (int h = 0; h < kRsNch; ++h) {
+    x[h] = u32x4_t{0u, 0u, 0u, 0u};
+    if (c0 + 64 * h < nvec) x[h] = src[c0 + 64 * h];
+  }
   for (int j = 0; j < k; ++j) {
     const int r = __builtin_amdgcn_readlane(myr, j);
     if (r < 0) continue;
     const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), j));
     u32x4_t *o = reinterpret_cast<u32x4_t *>(s + (int64_t)r * d);
-    u32x4_t ya, yb;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ya[q] = pack_bf16x2(bf16_bits_to_f32(xa[q] & 0xffffu) * wr, bf16_bits_to_f32(xa[q] >> 16) * wr);
-      yb[q] = pack_bf16x2(bf16_bits_to_f32(xb[q] & 0xffffu) * wr, bf16_bits_to_f32(xb[q] >> 16) * wr);
+    for (int h = 0; h < kRsNch; ++h) {
+      u32x4_t y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        y[q] = pack_bf16x2(bf16_bits_to_f32(x[h][q] & 0xffffu) * wr, bf16_bits_to_f32(x[h][q] >> 16) * wr);
+      if (c0 + 64 * h < nvec) o[c0 + 64 * h] = y;
     }
-    if (va) o[ca] = ya;
-    if (vb) o[cb] = yb;
   }
 }
 

@@ -185,13 +185,17 @@ __global__ __launch_bounds__(256) void k_place(const int32_t *__restrict__ idx, 
 
 // ------------------------------------------------------------------ rows
 //
-// One wave per piece of kRowPiece 16-byte chunks of a token row (a 2880-wide
-// bf16 row is three pieces), so that many waves have loads in flight.  A
+// One wave per piece of a token row (kScatterPiece or kRowPiece 16-byte
+// chunks), so that many waves have loads in flight.  A
 // token row is read once and written to its k rows (forward permute, combine
 // bwd), or its k rows are gathered and summed in fp32, j ascending (combine,
 // permute bwd).
 
-constexpr int kRowPiece = 128;   // 16-byte chunks of a row per wave
+// 16-byte chunks per lane: 3 for the row copies (two pieces per 2880-wide
+// bf16 row; measured 21.1 against 21.8 us for the gpt-oss-20b-like forward
+// permute), 2 for the gathered sums (three pieces; 3 and 4 were slower)
+constexpr int kScatterNch = 3, kScatterPiece = 64 * kScatterNch;
+constexpr int kRowNch = 2, kRowPiece = 64 * kRowNch;
 
 template <typename T>
 struct Vec16 {
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
                                                       int d, int k, T *__restrict__ dst,
                                                       float *__restrict__ w_dst) {
   const int nvec = src ? d * (int)sizeof(T) / 16 : 0;
-  const int pieces = nvec > 0 ? (nvec + kRowPiece - 1) / kRowPiece : 1;
+  const int pieces = nvec > 0 ? (nvec + kScatterPiece - 1) / kScatterPiece : 1;
   const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t t = wid / pieces;
   if (t >= ntok) return;
@@ -243,18 +247,21 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
   const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
   if (w_dst && piece == 0 && lane < k && myr >= 0) w_dst[myr] = w_src[t * k + lane];
   if (!src) return;
-  const int ca = piece * kRowPiece + lane, cb = ca + 64;
-  const bool va = ca < nvec, vb = cb < nvec;
+  const int c0 = piece * kScatterPiece + lane;
   const u32x4_t *s = reinterpret_cast<const u32x4_t *>(src + t * d);
-  u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = v0;
-  if (va) v0 = s[ca];
-  if (vb) v1 = s[cb];
+  u32x4_t v[kScatterNch];
+#pragma unroll
+  for (int h = 0; h < kScatterNch; ++h) {
+    v[h] = u32x4_t{0u, 0u, 0u, 0u};
+    if (c0 + 64 * h < nvec) v[h] = s[c0 + 64 * h];
+  }
   for (int j = 0; j < k; ++j) {
     const int r = __builtin_amdgcn_readlane(myr, j);
     if (r < 0) continue;
     u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + (int64_t)r * d);
-    if (va) o[ca] = v0;
-    if (vb) o[cb] = v1;
+#pragma unroll
+    for (int h = 0; h < kScatterNch; ++h)
+      if (c0 + 64 * h < nvec) o[c0 + 64 * h] = v[h];
   }
 }
 
@@ -271,8 +278,8 @@ static unsigned row_blocks(int64_t ntok, int d, bool rows = true, int piece = kR
 // gradient, d_logits[t,:] . w_r, formed here as an fma chain over the experts
 // in ascending order that skips zero entries (the same chain, bit for bit, as
 // the router's own dX kernel), so it is never stored.
-// One wave per (token, 128-chunk piece of the row): lane l covers 16-byte
-// chunks l and l + 64 of the piece.  Row indices are held one per lane and
+// One wave per (token, piece of 64 * kRowNch chunks of the row; 64 with the
+// router term): lane l covers 16-byte chunks l, l + 64, ... of the piece.  Row indices are held one per lane and
 // read out with readlane; four rows' loads (and four router rows' loads) are
 // issued before their adds.
 
@@ -286,33 +293,38 @@ __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
   constexpr int N = Vec16<T>::N;
   const int nvec = d * (int)sizeof(T) / 16;
   // the router term needs more registers: one chunk per lane, more waves
-  constexpr int PIECE = ROUTER ? 64 : kRowPiece;
+  constexpr int NCH = ROUTER ? 1 : kRowNch;
+  constexpr int PIECE = 64 * NCH;
   const int pieces = (nvec + PIECE - 1) / PIECE;
   const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t t = wid / pieces;
   if (t >= ntok) return;
-  const int c0 = (int)(wid - t * pieces) * PIECE;
   const int lane = threadIdx.x & 63;
+  const int c0 = (int)(wid - t * pieces) * PIECE + lane;   // chunk h of the lane: c0 + 64 h
   const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
   // router: this lane's entry of the first 64 experts and the nonzero ones
   const float dl0 = ROUTER && lane < E ? d_logits[t * E + lane] : 0.0f;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  const int ca = c0 + lane, cb = ca + 64;
-  const bool va = ca < nvec, vb = PIECE > 64 && cb < nvec;
-  float acc_a[N], acc_b[N];
+  bool vh[NCH];
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc_a[i] = acc_b[i] = 0.0f;
+  for (int h = 0; h < NCH; ++h) vh[h] = c0 + 64 * h < nvec;
+  float acc[NCH][N];
+#pragma unroll
+  for (int h = 0; h < NCH; ++h)
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[h][i] = 0.0f;
   // Up to four router rows (the first nonzero experts) are loaded with the
   // first four gathered rows; their fmas come after the row sums.
   uint64_t nz = ROUTER ? __ballot(dl0 != 0.0f) : 0;
   int ev[4];
   float g[4];
-  u32x4_t wa[4], wb[4];
+  u32x4_t wv[4][NCH];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     ev[u] = -1;
     g[u] = 0.0f;
-    wa[u] = wb[u] = zero;
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) wv[u][h] = zero;
   }
   auto load_router = [&](int e0, float dl) {
 #pragma unroll
@@ -324,58 +336,61 @@ __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
         ev[u] = e;
         g[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), e));
         const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(w_r + (int64_t)(e0 + e) * d);
-        wa[u] = va ? wr[ca] : zero;
-        wb[u] = vb ? wr[cb] : zero;
+#pragma unroll
+        for (int h = 0; h < NCH; ++h) wv[u][h] = vh[h] ? wr[c0 + 64 * h] : zero;
       }
     }
   };
   if (ROUTER) load_router(0, dl0);
   for (int j = 0; j < k; j += 4) {
-    u32x4_t xa[4], xb[4];
+    u32x4_t xv[4][NCH];
     int r[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       r[u] = j + u < k ? __builtin_amdgcn_readlane(myr, j + u) : -1;
-      xa[u] = xb[u] = zero;
+#pragma unroll
+      for (int h = 0; h < NCH; ++h) xv[u][h] = zero;
       if (r[u] >= 0) {
         const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + (int64_t)r[u] * d);
-        if (va) xa[u] = row[ca];
-        if (vb) xb[u] = row[cb];
+#pragma unroll
+        for (int h = 0; h < NCH; ++h)
+          if (vh[h]) xv[u][h] = row[c0 + 64 * h];
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (r[u] < 0) continue;
-      float f[N];
-      unpack16(xa[u], f, (const T *)nullptr);
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc_a[i] += f[i];
-      unpack16(xb[u], f, (const T *)nullptr);
+      for (int h = 0; h < NCH; ++h) {
+        float f[N];
+        unpack16(xv[u][h], f, (const T *)nullptr);
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc_b[i] += f[i];
+        for (int i = 0; i < N; ++i) acc[h][i] += f[i];
+      }
     }
   }
   if (add) {
     const float *ar = add + t * d;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = h ? cb : ca;
-      if (!(h ? vb : va)) continue;
-      float *acc = h ? acc_b : acc_a;
+    for (int h = 0; h < NCH; ++h) {
+      if (!vh[h]) continue;
+      const int64_t c = (int64_t)(c0 + 64 * h) * N;
 #pragma unroll
       for (int i = 0; i < N; i += 4) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(ar + (int64_t)c * N + i);
-        acc[i] += a4.x;
-        acc[i + 1] += a4.y;
-        acc[i + 2] += a4.z;
-        acc[i + 3] += a4.w;
+        const float4 a4 = *reinterpret_cast<const float4 *>(ar + c + i);
+        acc[h][i] += a4.x;
+        acc[h][i + 1] += a4.y;
+        acc[h][i + 2] += a4.z;
+        acc[h][i + 3] += a4.w;
       }
     }
   }
   if (ROUTER) {
-    float ra[N], rb[N];
+    float ra[NCH][N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) ra[i] = rb[i] = 0.0f;
+    for (int h = 0; h < NCH; ++h)
+#pragma unroll
+      for (int i = 0; i < N; ++i) ra[h][i] = 0.0f;
     for (int e0 = 0; e0 < E; e0 += 64) {
       float dl = dl0;
       if (e0 > 0) {
@@ -387,13 +402,12 @@ __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (ev[u] < 0) continue;
-          float fa[N], fb[N];
-          unpack16(wa[u], fa, (const T *)nullptr);
-          unpack16(wb[u], fb, (const T *)nullptr);
 #pragma unroll
-          for (int i = 0; i < N; ++i) {
-            ra[i] = fmaf(g[u], fa[i], ra[i]);
-            rb[i] = fmaf(g[u], fb[i], rb[i]);
+          for (int h = 0; h < NCH; ++h) {
+            float fw[N];
+            unpack16(wv[u][h], fw, (const T *)nullptr);
+#pragma unroll
+            for (int i = 0; i < N; ++i) ra[h][i] = fmaf(g[u], fw[i], ra[h][i]);
           }
         }
         if (!nz) break;
@@ -401,14 +415,14 @@ __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
       }
     }
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      acc_a[i] += ra[i];
-      acc_b[i] += rb[i];
-    }
+    for (int h = 0; h < NCH; ++h)
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[h][i] += ra[h][i];
   }
   u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + t * d);
-  if (va) o[ca] = pack16(acc_a, (const T *)nullptr);
-  if (vb) o[cb] = pack16(acc_b, (const T *)nullptr);
+#pragma unroll
+  for (int h = 0; h < NCH; ++h)
+    if (vh[h]) o[c0 + 64 * h] = pack16(acc[h], (const T *)nullptr);
 }
 
 
@@ -479,8 +493,9 @@ extern "C" int moe_permute(const void *x, const int32_t *topk_idx, const float *
   rc = check_launch("moe_permute(maps)");
   if (rc) return rc;
   if (x || w_perm) {
-    const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d, x != nullptr)
-                                              : row_blocks<float>(T, d, x != nullptr);
+    const unsigned blocks = dtype == MOE_BF16
+                                ? row_blocks<bf16_t>(T, d, x != nullptr, kScatterPiece)
+                                : row_blocks<float>(T, d, x != nullptr, kScatterPiece);
     if (dtype == MOE_BF16)
       MOE_LAUNCH("permute_rows", s,
                  k_scatter_rows<bf16_t><<<blocks, 256, 0, s>>>(
@@ -528,7 +543,8 @@ extern "C" int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int d
   MOE_REQUIRE(dy && slot_to_row && dy_perm && aligned16(dy) && aligned16(dy_perm),
               MOE_ERR_INVALID_ARG, "moe_combine_bwd: null or misaligned pointer");
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d) : row_blocks<float>(T, d);
+  const unsigned blocks = dtype == MOE_BF16 ? row_blocks<bf16_t>(T, d, true, kScatterPiece)
+                                            : row_blocks<float>(T, d, true, kScatterPiece);
   if (dtype == MOE_BF16)
     MOE_LAUNCH("combine_bwd", s,
                k_scatter_rows<bf16_t><<<blocks, 256, 0, s>>>((const bf16_t *)dy, slot_to_row,
