@@ -1663,15 +1663,19 @@ __global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restr
   const int64_t t = wid / pieces;
   if (t >= ntok) return;
   const int lane = threadIdx.x & 63;
-  const int c0 = (int)(wid - t * pieces) * kRsPiece + lane;   // chunk h: c0 + 64 h
+  // equal pieces of whole 64-chunk columns (256 chunks: 128 + 128)
+  const int pw = ((nvec + pieces - 1) / pieces + 63) / 64 * 64;
+  const int c0 = (int)(wid - t * pieces) * pw + lane;   // chunk h: c0 + 64 h
   const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
   const float myw = (myr >= 0 && w) ? w[myr] : 1.0f;
   const u32x4_t *src = reinterpret_cast<const u32x4_t *>(dy + t * d);
   u32x4_t x[kRsNch];
+  bool ok[kRsNch];
 #pragma unroll
   for (int h = 0; h < kRsNch; ++h) {
+    ok[h] = 64 * h < pw && c0 + 64 * h < nvec;
     x[h] = u32x4_t{0u, 0u, 0u, 0u};
-    if (c0 + 64 * h < nvec) x[h] = src[c0 + 64 * h];
+    if (ok[h]) x[h] = src[c0 + 64 * h];
   }
   for (int j = 0; j < k; ++j) {
     const int r = __builtin_amdgcn_readlane(myr, j);
@@ -1684,7 +1688,7 @@ __global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restr
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         y[q] = pack_bf16x2(bf16_bits_to_f32(x[h][q] & 0xffffu) * wr, bf16_bits_to_f32(x[h][q] >> 16) * wr);
-      if (c0 + 64 * h < nvec) o[c0 + 64 * h] = y;
+      if (ok[h]) o[c0 + 64 * h] = y;
     }
   }
 }

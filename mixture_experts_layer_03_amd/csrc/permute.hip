@@ -247,13 +247,18 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
   const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
   if (w_dst && piece == 0 && lane < k && myr >= 0) w_dst[myr] = w_src[t * k + lane];
   if (!src) return;
-  const int c0 = piece * kScatterPiece + lane;
+  // the row's pieces are made equal (whole 64-chunk columns): 256 chunks
+  // split 128 + 128, not 192 + 64
+  const int pw = ((nvec + pieces - 1) / pieces + 63) / 64 * 64;
+  const int c0 = piece * pw + lane;
   const u32x4_t *s = reinterpret_cast<const u32x4_t *>(src + t * d);
   u32x4_t v[kScatterNch];
+  bool ok[kScatterNch];
 #pragma unroll
   for (int h = 0; h < kScatterNch; ++h) {
+    ok[h] = 64 * h < pw && c0 + 64 * h < nvec;
     v[h] = u32x4_t{0u, 0u, 0u, 0u};
-    if (c0 + 64 * h < nvec) v[h] = s[c0 + 64 * h];
+    if (ok[h]) v[h] = s[c0 + 64 * h];
   }
   for (int j = 0; j < k; ++j) {
     const int r = __builtin_amdgcn_readlane(myr, j);
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const T *__restrict__ src,
     u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + (int64_t)r * d);
 #pragma unroll
     for (int h = 0; h < kScatterNch; ++h)
-      if (c0 + 64 * h < nvec) o[c0 + 64 * h] = v[h];
+      if (ok[h]) o[c0 + 64 * h] = v[h];
   }
 }
 

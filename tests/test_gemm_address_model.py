@@ -305,3 +305,24 @@ def test_gathered_x_krows_land_where_stored_rows_do(T, d, E, k):
                             else:
                                 want = got = (0,) * 8
                             assert got == want, (e, p0, k0, wave, i, lane)
+
+
+@pytest.mark.parametrize("nch", [2, 3])
+def test_row_pieces_cover_each_chunk_once(nch):
+    """The row copies (csrc/permute.hip, csrc/gemm.hip) split a row of nvec
+    16-byte chunks into ceil(nvec / (64 nch)) equal pieces of whole 64-chunk
+    columns; lane l of a piece's wave takes chunks start + l + 64 h for the
+    h with 64 h below the piece width.  Every chunk must be taken exactly
+    once, by at most nch chunks per lane."""
+    for nvec in range(1, 1500):
+        pieces = (nvec + 64 * nch - 1) // (64 * nch)
+        pw = ((nvec + pieces - 1) // pieces + 63) // 64 * 64
+        assert pw <= 64 * nch
+        seen = np.zeros(nvec, np.int64)
+        for piece in range(pieces):
+            for h in range(nch):
+                if 64 * h >= pw:
+                    continue
+                c = piece * pw + 64 * h + np.arange(64)
+                seen[c[c < nvec]] += 1
+        assert (seen == 1).all(), nvec
