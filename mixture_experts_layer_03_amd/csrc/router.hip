@@ -19,7 +19,7 @@ namespace moe {
 // per SIMD).  With many chains (T*E >= 2^20) a lane runs 4 tokens x 1 expert
 // or 2 x 2 and the block covers 4 (2) times the tokens (and 2 times the
 // experts): each LDS read then feeds several chains (the kernel reads both
-// operands from LDS for every fma, so LDS bandwidth bounds it).  Operands
+// operands from LDS for every fma: LDS reads and instruction issue bound it).  Operands
 // come from LDS tiles of kLogitCk columns (fp32, rows
 // padded so that the 8 distinct rows one read touches fall on distinct
 // banks; the 8 lanes that share a row read it as a broadcast); the next
