@@ -212,6 +212,14 @@ int moe_combine(const void *y_perm, const int32_t *slot_to_row, int dtype,
 /*
  * Adjoint of moe_combine: a copy of each token's gradient to its k rows,
  *   dy_perm[slot_to_row[t*k+j]] = dy[t].
+ * The combine returns each expert output row to its token ("Halo's 2.8x over
+ * TRL is not a kernel, and its own benchmark proves it", section "Where the
+ * gap actually is", EP token-routing figure); its adjoint is written as this
+ * copy through the forward's own map, a gather with no atomic adds ("Halo:
+ * Frontier-Lab Training for Everyone", section "Some of the hard problems
+ * along the way", on the atomic-free routing backward).  dy: [T,d] (dtype);
+ * slot_to_row: [T*k] int32 from moe_permute; dy_perm: [T*k,d] (out, every row
+ * written once).  Errors as moe_combine.
  */
 int moe_combine_bwd(const void *dy, const int32_t *slot_to_row, int dtype,
                     int64_t T, int d, int k, void *dy_perm, void *stream);
@@ -269,6 +277,20 @@ int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, const void *h,
                              void *stream);
 
 /*
+ * Where moe_grouped_ffn_bwd_lora leaves its stored rank-r rows in the
+ * workspace `ws` it was given (same R, E, d, f, r): u_dn = store(s dY_perm
+ * B_dn), uw_dn = store(w u_dn) (written only when row_scale was given) and
+ * u_gu = store(s dGU B_gu), each [R,r] bf16 row-major.  The values are those
+ * of the last backward call on that workspace, in stream order.  For
+ * inspection and tests; the pointers alias ws and are not to be freed.
+ * Errors: NULL pointers or r not in {16,32,48,64}: MOE_ERR_INVALID_ARG;
+ * ws_bytes below moe_grouped_ffn_lora_workspace_size: MOE_ERR_WORKSPACE.
+ */
+int moe_grouped_ffn_lora_bwd_saved(const void *ws, size_t ws_bytes, int64_t R, int E, int d,
+                                   int f, int r, const void **u_dn, const void **uw_dn,
+                                   const void **u_gu);
+
+/*
  * moe_permute_bwd with the router's share of the token gradient formed in the
  * same pass instead of read from memory:
  *   dx[t] = store(sum_{j asc} fp32(dx_perm[slot_to_row[t*k+j]]) + r[t]),
@@ -289,12 +311,22 @@ int moe_permute_bwd_router(const void *dx_perm, const int32_t *slot_to_row, cons
 /* ---------------------------------------------------------------- router bwd */
 
 /*
- * Adjoint of the softmax over the selected logits.  With g_j =
+ * Adjoint of the softmax over the selected logits.  The routers are trained:
+ * they receive the gradient of the loss through the combine weights (the
+ * TorchTurbo page, "inclusionAI open-sources TorchTurbo, a SuperNode-native
+ * post-training engine", section "Adapter": the routers apply the gradient of
+ * the auxiliary loss, so they carry gradients), and the combine weights are
+ * the top-k probabilities of the fp32 router ("Halo's 2.8x over TRL is not a
+ * kernel, and its own benchmark proves it", section "Where the gap actually
+ * is", EP token-routing figure).  With g_j =
  * d_row_scale[slot_to_row[t*k+j]] (the gradient of the loss with respect to
  * topk_w[t,j]):
  *   d_topk_w[t,j] = g_j                         (d_topk_w may be NULL)
  *   d_logits[t,topk_idx[t,j]] = w_j * (g_j - sum_i w_i g_i), 0 elsewhere.
- * All fp32; d_logits: [T,E] (out, fully written).
+ * All fp32; d_logits: [T,E] (out, fully written).  topk_idx / topk_w: [T,k]
+ * from moe_route; d_row_scale: [T*k] from moe_grouped_ffn_bwd; slot_to_row:
+ * [T*k] from moe_permute.  Invalid sizes or NULL required pointers:
+ * MOE_ERR_INVALID_ARG, nothing launched.
  */
 int moe_route_bwd(const int32_t *topk_idx, const float *topk_w, const float *d_row_scale,
                   const int32_t *slot_to_row, int64_t T, int E, int k,
@@ -303,10 +335,19 @@ int moe_route_bwd(const int32_t *topk_idx, const float *topk_w, const float *d_r
 size_t moe_router_logits_bwd_workspace_size(int64_t T, int d, int E);
 
 /*
- * Adjoint of the router linear map (bias and added noise carry no gradient):
+ * Adjoint of the router linear map that forms the fp32 router logits ("fp32
+ * router logits" in the EP forward path, "Halo's 2.8x over TRL is not a
+ * kernel, and its own benchmark proves it", section "Where the gap actually
+ * is"; the routers are trained, the TorchTurbo page, section "Adapter").  Bias
+ * and added noise carry no gradient:
  *   dx_router = d_logits . w_r    ([T,d] fp32, or NULL to skip)
  *   dw_r      = d_logits^T . x    ([E,d] fp32, or NULL to skip)
- * fp32 accumulation in a fixed order.  dtype must be MOE_BF16.
+ * fp32 accumulation in a fixed order: dx_router as an fma chain over e
+ * ascending (zero entries skipped), dw_r as per-chunk partials over 256-token
+ * chunks summed in chunk order.  x: [T,d], w_r: [E,d] (dtype); d_logits:
+ * [T,E] fp32.  dtype must be MOE_BF16.  ws:
+ * moe_router_logits_bwd_workspace_size(T,d,E) bytes (MOE_ERR_WORKSPACE if
+ * smaller).
  */
 int moe_router_logits_bwd(const void *x, const void *w_r, const float *d_logits, int dtype,
                           int64_t T, int d, int E, float *dx_router, float *dw_r,

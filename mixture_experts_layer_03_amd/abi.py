@@ -77,6 +77,9 @@ _SIGS = {
                                         ctypes.c_float, _c_void_p, _c_void_p, _i32, _c_void_p,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                         _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_lora_bwd_saved": (_i32, [_c_void_p, _sz, _i64, _i32, _i32, _i32, _i32,
+                                              ctypes.POINTER(_c_void_p), ctypes.POINTER(_c_void_p),
+                                              ctypes.POINTER(_c_void_p)]),
     "moe_grouped_ffn_fwd_gather": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p, _i32,
                                           _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                           _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
@@ -323,6 +326,23 @@ def moe_grouped_ffn_bwd_lora(x_perm, gu, h, offsets, E, w_gu, w_down, row_scale,
         _p(dy_perm), _p(a_gu), _p(b_gu), _p(a_dn), _p(b_dn), r, float(scale), _p(z_gu), _p(z_dn),
         _dtype_code(w_gu), _p(dgu), _p(dx_perm), _p(d_row_scale), _p(da_gu), _p(db_gu),
         _p(da_dn), _p(db_dn), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn_lora_bwd_saved(ws, R, E, d, f, r):
+    """Views [R, r] (bf16) of u_dn, store(w u_dn) and u_gu inside the LoRA
+    backward's workspace ws (a uint8 device tensor)."""
+    import torch
+    ptrs = [_c_void_p(), _c_void_p(), _c_void_p()]
+    nbytes = ws.numel() * ws.element_size()
+    _check("moe_grouped_ffn_lora_bwd_saved", lib().moe_grouped_ffn_lora_bwd_saved(
+        _p(ws), nbytes, R, E, d, f, r, ctypes.byref(ptrs[0]), ctypes.byref(ptrs[1]),
+        ctypes.byref(ptrs[2])))
+    base = ws.data_ptr()
+    out = []
+    for p in ptrs:
+        off = int(p.value) - base
+        out.append(ws[off:off + 2 * R * r].view(torch.bfloat16).view(R, r))
+    return tuple(out)
 
 
 def moe_timing_enable(on: bool):

@@ -2103,6 +2103,48 @@ extern "C" size_t moe_grouped_ffn_lora_workspace_size(int64_t R, int E, int d, i
   return moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16) + lora_extra_bytes(R, E, d, f, r);
 }
 
+// Byte offsets inside the LoRA workspace of the backward's rank-r rows:
+// u_dn, store(w u_dn) and u_gu, each [R, r] bf16 (after the tile starts of
+// the rank-r projections and the transposed B factors).
+struct LoraBwdLayout {
+  size_t ts16, b_dn_t, b_gu_t, u_dn, uw_dn, u_gu;
+};
+static LoraBwdLayout lora_bwd_layout(int64_t R, int E, int d, int f, int r) {
+  LoraBwdLayout L;
+  size_t o = moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16);
+  L.ts16 = o;
+  o += tile_start_bytes(E);
+  L.b_dn_t = o;
+  o += align_up(2 * (size_t)E * r * d, 256);
+  L.b_gu_t = o;
+  o += align_up(2 * (size_t)E * r * 2 * f, 256);
+  L.u_dn = o;
+  o += align_up(2 * (size_t)R * r, 256);
+  L.uw_dn = o;
+  o += align_up(2 * (size_t)R * r, 256);
+  L.u_gu = o;
+  return L;
+}
+
+extern "C" int moe_grouped_ffn_lora_bwd_saved(const void *ws, size_t ws_bytes, int64_t R, int E,
+                                              int d, int f, int r, const void **u_dn,
+                                              const void **uw_dn, const void **u_gu) {
+  clear_error();
+  MOE_REQUIRE(ws && u_dn && uw_dn && u_gu, MOE_ERR_INVALID_ARG,
+              "moe_grouped_ffn_lora_bwd_saved: null pointer");
+  MOE_REQUIRE(R >= 0 && E >= 1 && d > 0 && f > 0 && (r == 16 || r == 32 || r == 48 || r == 64),
+              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_lora_bwd_saved: bad sizes");
+  const size_t need = moe_grouped_ffn_lora_workspace_size(R, E, d, f, r);
+  MOE_REQUIRE(ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_grouped_ffn_lora_bwd_saved: workspace %zu < %zu", ws_bytes, need);
+  const LoraBwdLayout L = lora_bwd_layout(R, E, d, f, r);
+  const char *w = (const char *)ws;
+  *u_dn = w + L.u_dn;
+  *uw_dn = w + L.uw_dn;
+  *u_gu = w + L.u_gu;
+  return MOE_OK;
+}
+
 template <int RK>
 static int launch_lora_proj(const bf16_t *in, const bf16_t *F, const int32_t *offsets,
                             const int32_t *ts, int E, int64_t R, int K, float scale, const float *w,
@@ -2245,18 +2287,13 @@ extern "C" int moe_grouped_ffn_bwd_lora(const void *x_perm, const void *gu, cons
   int32_t *ts1 = (int32_t *)(wb + tile_start_bytes(E));
   float *drs_part = (float *)(wb + 2 * tile_start_bytes(E));
   bf16_t *s_perm = (bf16_t *)(wb + 2 * tile_start_bytes(E) + drs_bytes(R, f));
-  char *lw = wb + moe_grouped_ffn_workspace_size(R, E, d, f, MOE_BF16);
-  int32_t *ts16 = (int32_t *)lw;
-  lw += tile_start_bytes(E);
-  bf16_t *b_dn_t = (bf16_t *)lw;   // [E, r, d]
-  lw += align_up(2 * (size_t)E * r * d, 256);
-  bf16_t *b_gu_t = (bf16_t *)lw;   // [E, r, 2f]
-  lw += align_up(2 * (size_t)E * r * 2 * f, 256);
-  bf16_t *u_dn = (bf16_t *)lw;
-  lw += align_up(2 * (size_t)R * r, 256);
-  bf16_t *uw_dn = (bf16_t *)lw;
-  lw += align_up(2 * (size_t)R * r, 256);
-  bf16_t *u_gu = (bf16_t *)lw;
+  const LoraBwdLayout L = lora_bwd_layout(R, E, d, f, r);
+  int32_t *ts16 = (int32_t *)(wb + L.ts16);
+  bf16_t *b_dn_t = (bf16_t *)(wb + L.b_dn_t);   // [E, r, d]
+  bf16_t *b_gu_t = (bf16_t *)(wb + L.b_gu_t);   // [E, r, 2f]
+  bf16_t *u_dn = (bf16_t *)(wb + L.u_dn);
+  bf16_t *uw_dn = (bf16_t *)(wb + L.uw_dn);
+  bf16_t *u_gu = (bf16_t *)(wb + L.u_gu);
   GemmArgs a{};
   a.x_perm = (const bf16_t *)x_perm;
   a.w_gu = (const bf16_t *)w_gu;

@@ -84,8 +84,11 @@ class MoEBlock:
             ws_ffn = abi.moe_grouped_ffn_lora_workspace_size(R, E, d, f, lora_rank)
             self.z_gu = z(R, lora_rank)
             self.z_dn = z(R, lora_rank)
-        self.ws = torch.empty(max(ws_perm, ws_ffn, ws_rtr, ws_stat, 256), dtype=torch.uint8,
+        # the grouped FFN's workspace is its own, so that what its backward
+        # leaves there (e.g. the LoRA rank-r rows) survives the router calls
+        self.ws = torch.empty(max(ws_perm, ws_rtr, ws_stat, 256), dtype=torch.uint8,
                               device=device)
+        self.ws_ffn = torch.empty(max(ws_ffn, 256), dtype=torch.uint8, device=device)
         self.load = z(E, dt=i32)
         self.aux = z(2, dt=f32)
         self.has_bwd = backward
@@ -136,17 +139,17 @@ class MoEBlock:
         if self.gather:
             abi.moe_grouped_ffn_fwd_gather(x, self.row_to_slot, self.k, self.offsets, self.E,
                                            w_gu, w_down, self.w_perm, self.gu, self.h,
-                                           self.y_perm, self.ws, stream)
+                                           self.y_perm, self.ws_ffn, stream)
             return
         if self.lora_rank:
             a_gu, b_gu, a_dn, b_dn = lora
             abi.moe_grouped_ffn_fwd_lora(self.x_perm, self.offsets, self.E, w_gu, w_down,
                                          self.w_perm, a_gu, b_gu, a_dn, b_dn, self.lora_scale,
                                          self.z_gu, self.z_dn, self.gu, self.h, self.y_perm,
-                                         self.ws, stream)
+                                         self.ws_ffn, stream)
             return
         abi.moe_grouped_ffn_fwd(self.x_perm, self.offsets, self.E, w_gu, w_down, self.w_perm,
-                                self.gu, self.h, self.y_perm, self.ws, stream)
+                                self.gu, self.h, self.y_perm, self.ws_ffn, stream)
 
     # ------------------------------------------------------------ backward
     def backward(self, x, w_r, w_gu, w_down, dy, stream=None, aux_coeff: float = 0.0,
@@ -191,7 +194,7 @@ class MoEBlock:
                                            self.gu, self.h,
                                            self.offsets, self.E, w_gu, w_down, self.w_perm,
                                            self.dgu, self.dx_perm, self.dw_gu, self.dw_down,
-                                           self.d_row_scale, self.ws, stream,
+                                           self.d_row_scale, self.ws_ffn, stream,
                                            x_perm=self.x_perm)
             return
         if self.lora_rank:
@@ -200,11 +203,11 @@ class MoEBlock:
                                          w_down, self.w_perm, self.dy_perm, a_gu, b_gu, a_dn,
                                          b_dn, self.lora_scale, self.z_gu, self.z_dn, self.dgu,
                                          self.dx_perm, self.d_row_scale, self.da_gu, self.db_gu,
-                                         self.da_dn, self.db_dn, self.ws, stream)
+                                         self.da_dn, self.db_dn, self.ws_ffn, stream)
             return
         abi.moe_grouped_ffn_bwd(self.x_perm, self.gu, self.h, self.offsets, self.E, w_gu,
                                 w_down, self.w_perm, self.dy_perm, self.dgu, self.dx_perm,
-                                self.dw_gu, self.dw_down, self.d_row_scale, self.ws, stream)
+                                self.dw_gu, self.dw_down, self.d_row_scale, self.ws_ffn, stream)
 
 
 class ExpertShare:

@@ -351,8 +351,8 @@ def expert_ffn_fwd_lora(x_perm, offsets, w_gu, w_down, row_scale, a_gu, b_gu, a_
 def expert_ffn_bwd_lora(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, a_gu, b_gu,
                         a_dn, b_dn, scale: float, z_gu, z_dn, bf16=True):
     """Backward with frozen experts.  Returns dict with dGU, dX_perm,
-    d_row_scale, u_gu, u_dn (stored) and dA_gu[E,r,d], dB_gu[E,2f,r],
-    dA_dn[E,r,f], dB_dn[E,d,r] (fp32)."""
+    d_row_scale, u_gu, u_dn, uw_dn = store(w u_dn) (stored) and dA_gu[E,r,d],
+    dB_gu[E,2f,r], dA_dn[E,r,f], dB_dn[E,d,r] (fp32)."""
     R, d = x_perm.shape
     E, f2, _ = w_gu.shape
     f = f2 // 2
@@ -363,6 +363,7 @@ def expert_ffn_bwd_lora(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, a
         "d_row_scale": np.zeros(R, np.float32),
         "u_gu": np.zeros((R, r), np.float32),
         "u_dn": np.zeros((R, r), np.float32),
+        "uw_dn": np.zeros((R, r), np.float32),
         "da_gu": np.zeros((E, r, d), np.float32),
         "db_gu": np.zeros((E, 2 * f, r), np.float32),
         "da_dn": np.zeros((E, r, f), np.float32),
@@ -396,7 +397,9 @@ def expert_ffn_bwd_lora(x_perm, gu, offsets, w_gu, w_down, row_scale, dy_perm, a
         out["db_gu"][e] = (_f64(dgu).T @ _f64(z_gu[a:b])).astype(np.float32)
         out["da_gu"][e] = (_f64(u_gu).T @ _f64(xr)).astype(np.float32)
         out["db_dn"][e] = (_f64(s_).T @ _f64(z_dn[a:b])).astype(np.float32)
-        out["da_dn"][e] = (_f64(store(w[:, None] * _f64(u_dn), bf16)).T @ _f64(h)).astype(np.float32)
+        uw_dn = store(w[:, None] * _f64(u_dn), bf16)
+        out["uw_dn"][a:b] = uw_dn
+        out["da_dn"][e] = (_f64(uw_dn).T @ _f64(h)).astype(np.float32)
     return out
 
 
@@ -606,11 +609,13 @@ def ffn_bwd_sampled_rows(x_perm, offsets, w_gu, w_down, row_scale, dy_perm, rows
 
 
 def weight_grads_sampled_cols(x_perm, offsets, w_gu, w_down, row_scale, dy_perm, e: int,
-                              cols, bf16=True):
+                              cols, bf16=True, operands=False):
     """For expert e and hidden-unit columns c in ``cols`` (0 <= c < f):
     dW_gu[e][c, :], dW_gu[e][f+c, :] and dW_down[e][:, c], from only the
     columns of GU, H and dGU that they need.  Returns (dw_gate[len,d],
-    dw_up[len,d], dw_down_cols[d,len])."""
+    dw_up[len,d], dw_down_cols[d,len]), and with operands=True also a dict of
+    the stored operands they are summed from (the expert's rows of the dGU
+    gate and up columns, the H columns and S)."""
     cols = np.asarray(cols, np.int64)
     f = w_gu.shape[1] // 2
     a, b = int(offsets[e]), int(offsets[e + 1])
@@ -630,5 +635,8 @@ def weight_grads_sampled_cols(x_perm, offsets, w_gu, w_down, row_scale, dy_perm,
     dg = _f64(store(dh * u * sg * (1.0 + g * (1.0 - sg)), bf16))
     du = _f64(store(dh * g * sg, bf16))
     s = _f64(store(w[:, None] * dyr, bf16))
-    return ((dg.T @ xr).astype(np.float32), (du.T @ xr).astype(np.float32),
-            (s.T @ h).astype(np.float32))
+    out = ((dg.T @ xr).astype(np.float32), (du.T @ xr).astype(np.float32),
+           (s.T @ h).astype(np.float32))
+    if operands:
+        return out + ({"dg": dg, "du": du, "h": h, "s": s},)
+    return out

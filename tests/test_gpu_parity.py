@@ -2,17 +2,19 @@
 
 Bit-exact: router logits, top-k indices, counts, offsets, slot_to_row,
 row_to_slot, the permuted rows (exact copies), the copied upstream gradient.
-The block's outputs and gradients (Y, dX, dx_router, topk_w): max-abs 2e-2 and
-relative-L2 5e-3 of the oracle.  Tensors that are, or sum over, bf16-stored
-accumulated intermediates (GU, H, Y_perm, dGU, dX_perm, d_row_scale, d_topk_w,
-d_logits, dW_r, dW_gu, dW_down): relative-L2 5e-3 and max-abs within
-max(2e-2, one bf16 ulp at the tensor's largest magnitude) -- see close().
+Floating-point outputs and gradients: max-abs 2e-2 and relative-L2 5e-3 of
+the oracle (topk_w: 1e-6); an element's max-abs bound is widened only by what
+its own step's arithmetic explains -- its rounding, the observed deviation of
+its stored inputs (each checked in turn) and fp32 accumulation
+(tests/tolerance.py, tests/parity.py; pinned by tests/test_tolerance_model.py).
 """
 import numpy as np
 import pytest
 
 from mixture_experts_layer_03_amd import inputs as I
 from oracle import moe_oracle as O
+from tests import parity as PC
+from tests import tolerance as TB
 from tests.gpu_util import close, down, need_gpu, up, up_i32
 
 pytestmark = pytest.mark.gpu
@@ -78,29 +80,19 @@ def _bits(a):
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-def check_forward(g, o):
+def check_exact(g, o, b=None):
+    """Routing, maps and copies: bit for bit.  w_perm must be an exact copy of
+    the device's own topk_w."""
     for n in EXACT_FWD:
         assert np.array_equal(_bits(g[n]), _bits(o[n])), n
-    # the combine weights are computed in fp32 on the device (fp64 in the oracle);
-    # w_perm must be an exact copy of the device's own topk_w
-    close("topk_w", g["topk_w"], o["topk_w"], max_abs=1e-6, rel_l2=1e-6)
     assert np.array_equal(_bits(g["w_perm"]), _bits(g["topk_w"].ravel()[g["row_to_slot"]]))
-    close("gu", g["gu"], o["gu"], flip=True)
-    close("h", g["h"], o["h"], flip=True)
-    close("y_perm", g["y_perm"], o["y_perm"], flip=True)
-    close("y", g["y"], o["y"])
+    if b is not None and "dy_perm" in g:
+        assert np.array_equal(g["dy_perm"], b["dy_perm"]), "dy_perm"
 
 
-FLIP_BWD = ("dgu", "dx_perm", "d_row_scale", "d_topk_w", "d_logits", "dw_r", "dw_gu", "dw_down")
-
-
-def check_backward(g, b):
-    assert np.array_equal(g["dy_perm"], b["dy_perm"]), "dy_perm"
-    for n in FLIP_BWD:
-        close(n, g[n], b[n], flip=True)
-    if "dx_router" in g:
-        close("dx_router", g["dx_router"], b["dx_router"])
-    close("dx", g["dx"], b["dx"])
+def check_block(g, o, b, a, k, backward=True, bf16=True):
+    check_exact(g, o, b if backward else None)
+    PC.check_layer(g, o, b, a, k, backward=backward, bf16=bf16)
 
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
@@ -108,8 +100,7 @@ def test_layer_forward_backward_matches_oracle(w):
     a = I.make_inputs(w)
     g = run_gpu(w, a)
     o, b = run_oracle(w, a)
-    check_forward(g, o)
-    check_backward(g, b)
+    check_block(g, o, b, a, w.k)
 
 
 @pytest.mark.parametrize("w", SMALL[:2] + SMALL[4:5], ids=[w.name for w in SMALL[:2] + SMALL[4:5]])
@@ -121,9 +112,12 @@ def test_router_dx_fused_matches_stored_path(w):
     g_f = run_gpu(w, a)
     g_u = run_gpu(w, a, fuse_router_dx=False)
     assert np.array_equal(np.asarray(g_f["dx"]).view(np.uint32), np.asarray(g_u["dx"]).view(np.uint32))
-    _, b = run_oracle(w, a)
-    close("dx_router", g_u["dx_router"], b["dx_router"])
-    check_backward(g_u, b)
+    o, b = run_oracle(w, a)
+    ddl = g_u["d_logits"].astype(np.float64) - b["d_logits"]
+    wr = np.abs(a["w_r"].astype(np.float64))
+    close("dx_router", g_u["dx_router"], b["dx_router"],
+          bound=TB.absdot(ddl, wr) + w.E * TB.U32 * (np.abs(g_u["d_logits"]) @ wr))
+    check_block(g_u, o, b, a, w.k)
 
 
 def test_tiny_fp32_forward_matches_oracle():
@@ -131,7 +125,7 @@ def test_tiny_fp32_forward_matches_oracle():
     a = I.make_inputs(w)
     g = run_gpu(w, a, backward=False)
     o, _ = run_oracle(w, a, backward=False)
-    check_forward(g, o)
+    check_block(g, o, None, a, w.k, backward=False, bf16=False)
 
 
 def test_bitwise_repeatable():
@@ -181,14 +175,7 @@ def test_prerouted_share_matches_oracle():
     sh.forward(xp, off, wgu, wd, wp)
     sh.backward(xp, off, wgu, wd, wp, dyp)
     torch.cuda.synchronize()
-    gu, h, y = O.expert_ffn_fwd(a["x_perm"], offsets, a["w_gu"], a["w_down"], a["w_perm"], True)
-    close("gu", down(sh.gu), gu, flip=True)
-    close("h", down(sh.h), h, flip=True)
-    close("y_perm", down(sh.y_perm), y, flip=True)
-    b = O.expert_ffn_bwd(a["x_perm"], gu, offsets, a["w_gu"], a["w_down"], a["w_perm"],
-                         a["dy_perm"], True)
-    for n in ("dgu", "dx_perm", "d_row_scale", "dw_gu", "dw_down"):
-        close(n, down(getattr(sh, n)), b[n], flip=True)
+    check_share(sh, a, offsets)
 
 
 def test_all_rows_one_expert_and_empty_experts():
@@ -218,11 +205,25 @@ def test_all_rows_one_expert_and_empty_experts():
     assert np.array_equal(down(blk.slot_to_row), s2r)
     xp, wp = O.permute_rows(a["x"], wts, r2s, k)
     gu, h, y = O.expert_ffn_fwd(xp, offsets, a["w_gu"], a["w_down"], wp, True)
-    close("y_perm", down(blk.y_perm), y, flip=True)
-    close("y", down(blk.y), O.combine(y, s2r, T, k, True))
     dyp = O.combine_bwd(a["dy"], s2r, k)
-    b = O.expert_ffn_bwd(xp, gu, offsets, a["w_gu"], a["w_down"], wp, dyp, True)
-    for n in ("dgu", "dx_perm", "dw_gu", "dw_down", "d_row_scale"):
-        close(n, down(getattr(blk, n)), b[n], flip=True)
+    ref = dict(gu=gu, h=h, y_perm=y)
+    ref.update(O.expert_ffn_bwd(xp, gu, offsets, a["w_gu"], a["w_down"], wp, dyp, True))
+    got = {n: down(getattr(blk, n)) for n in PC.ROW_FWD + PC.ROW_BWD + ("dw_gu", "dw_down")}
+    dev = PC.check_ffn(got, ref, xp, offsets, a["w_gu"], a["w_down"], wp, wp, dyp)
+    y_ref = O.combine(y, s2r, T, k, True)
+    close("y", down(blk.y), y_ref,
+          bound=TB.b_sum_rows(down(blk.y), y_ref, [got["y_perm"][s2r]], [dev["y_perm"][s2r]]))
     dwg = down(blk.dw_gu)
     assert np.all(dwg[[0, 1, 3, 4]] == 0)
+
+
+def check_share(sh, a, offsets):
+    """One expert-parallel rank's grouped FFN (ExpertShare) against the
+    oracle: rows arrive sorted by expert with their combine weights."""
+    gu, h, y = O.expert_ffn_fwd(a["x_perm"], offsets, a["w_gu"], a["w_down"], a["w_perm"], True)
+    ref = dict(gu=gu, h=h, y_perm=y)
+    ref.update(O.expert_ffn_bwd(a["x_perm"], gu, offsets, a["w_gu"], a["w_down"], a["w_perm"],
+                                a["dy_perm"], True))
+    got = {n: down(getattr(sh, n)) for n in PC.ROW_FWD + PC.ROW_BWD + ("dw_gu", "dw_down")}
+    PC.check_ffn(got, ref, a["x_perm"], offsets, a["w_gu"], a["w_down"], a["w_perm"],
+                 a["w_perm"], a["dy_perm"])

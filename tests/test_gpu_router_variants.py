@@ -162,7 +162,7 @@ LAYER_CASES = [_layer_case(300, 328, 6, 2, 200, 21), _layer_case(512, 256, 16, 4
 def test_block_with_selection_bias_and_aux_loss_matches_oracle(w):
     import torch
     from mixture_experts_layer_03_amd.layer import MoEBlock
-    from tests.test_gpu_parity import check_backward, check_forward
+    from tests.test_gpu_parity import check_block
     dev = need_gpu()
     print("GPU case", w.name, flush=True)
     a = I.make_inputs(w)
@@ -183,8 +183,7 @@ def test_block_with_selection_bias_and_aux_loss_matches_oracle(w):
     o = O.layer_forward(a["x"], a["w_r"], a["w_gu"], a["w_down"], w.k, sel_bias=b)
     bo = O.layer_backward(o, a["x"], a["w_r"], a["w_gu"], a["w_down"], a["dy"], w.k,
                           aux_coeff=coeff, n_valid=n_valid)
-    check_forward(g, o)
-    check_backward(g, bo)
+    check_block(g, o, bo, a, w.k)
     assert np.array_equal(g["load"], bo["load"])
     assert abs(g["aux"][0] - bo["aux"]) <= 1e-5 * bo["aux"]
     assert abs(g["aux"][1] - bo["aux_scaled"]) <= 1e-5 * bo["aux_scaled"]

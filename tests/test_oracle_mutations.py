@@ -54,12 +54,34 @@ MUTATIONS = [
      "u_dn = store((_f64(dyr) @ _f64(b_dn[e])), bf16)"),
     ("LoRA term missing from dX", "dx = store(_f64(dgu) @ _f64(w_gu[e]) + _f64(u_gu) @ _f64(a_gu[e]), bf16)",
      "dx = store(_f64(dgu) @ _f64(w_gu[e]), bf16)"),
-    ("LoRA dA_dn without the row weight", "(_f64(store(w[:, None] * _f64(u_dn), bf16)).T @ _f64(h))",
-     "(_f64(u_dn).T @ _f64(h))"),
+    ("LoRA dA_dn without the row weight", "uw_dn = store(w[:, None] * _f64(u_dn), bf16)",
+     "uw_dn = store(_f64(u_dn), bf16)"),
     ("LoRA dB_dn from dY instead of S", "(_f64(s_).T @ _f64(z_dn[a:b]))", "(_f64(dyr).T @ _f64(z_dn[a:b]))"),
     ("LoRA down term added after the row weight",
      "    y = _f64(h) @ _f64(w_down_e).T + _f64(z_dn) @ _f64(b_dn_e).T\n    if wr is not None:\n        y = _f64(wr)[:, None] * y\n    return gu, h, store(y, bf16), z_gu, z_dn",
      "    y = _f64(h) @ _f64(w_down_e).T\n    if wr is not None:\n        y = _f64(wr)[:, None] * y\n    y = y + _f64(z_dn) @ _f64(b_dn_e).T\n    return gu, h, store(y, bf16), z_gu, z_dn"),
+    ("S not rounded to bf16", "s = store(w[:, None] * _f64(dyr), bf16)\n    return dgu",
+     "s = w[:, None] * _f64(dyr)\n    return dgu"),
+    ("H recomputed in the backward without its rounding",
+     "h = store(silu(g) * u, bf16)                     # recomputed",
+     "h = silu(g) * u                                  # recomputed"),
+    ("dGU not rounded before dX and dW_gu",
+     "dgu = store(np.concatenate([dg, du], axis=1), bf16)\n    dx = store(_f64(dgu) @ _f64(w_gu_e), bf16)",
+     "dgu = np.concatenate([dg, du], axis=1)\n    dx = store(_f64(dgu) @ _f64(w_gu_e), bf16)"),
+    ("LoRA z_gu not rounded", "z_gu = store(scale * (_f64(xr) @ _f64(a_gu_e).T), bf16)",
+     "z_gu = scale * (_f64(xr) @ _f64(a_gu_e).T)"),
+    ("LoRA z_dn not rounded", "z_dn = store(scale * (_f64(h) @ _f64(a_dn_e).T), bf16)",
+     "z_dn = scale * (_f64(h) @ _f64(a_dn_e).T)"),
+    ("LoRA u_dn not rounded", "u_dn = store(scale * (_f64(dyr) @ _f64(b_dn[e])), bf16)",
+     "u_dn = scale * (_f64(dyr) @ _f64(b_dn[e]))"),
+    ("LoRA u_gu not rounded", "u_gu = store(scale * (_f64(dgu) @ _f64(b_gu[e])), bf16)",
+     "u_gu = scale * (_f64(dgu) @ _f64(b_gu[e]))"),
+    ("LoRA row-weighted u_dn not rounded", "uw_dn = store(w[:, None] * _f64(u_dn), bf16)",
+     "uw_dn = w[:, None] * _f64(u_dn)"),
+    ("LoRA S not rounded", "s_ = store(w[:, None] * _f64(dyr), bf16)", "s_ = w[:, None] * _f64(dyr)"),
+    ("LoRA dGU not rounded",
+     "dgu = store(np.concatenate([dg, du], axis=1), bf16)\n        u_gu",
+     "dgu = np.concatenate([dg, du], axis=1)\n        u_gu"),
 ]
 
 PIN_TESTS = [
@@ -80,6 +102,8 @@ PIN_TESTS = [
     lambda: P.test_lora_with_zero_b_is_the_plain_block(),
     lambda: P.test_lora_forward_is_the_merged_weight_block(),
     lambda: P.test_lora_gradients_match_torch_autograd(),
+    lambda: P.test_expert_backward_storage_points_by_torch(61),
+    lambda: P.test_lora_storage_points_by_torch(71),
 ]
 
 

@@ -529,3 +529,133 @@ def test_lora_gradients_match_torch_autograd():
     assert _rel(lo["y"], ref["y"]) < 1e-6
     for n in ("dx", "da_gu", "db_gu", "da_dn", "db_dn"):
         assert _rel(lo[n], ref[n]) < 1e-5, (n, _rel(lo[n], ref[n]))
+
+
+# ---------------------------------------------------------------- storage points, rebuilt in torch
+#
+# One expert with row weights in (0, 1), rebuilt with torch: fp64 matmuls,
+# torch's own fp32 -> bf16 conversion at exactly the block's storage points,
+# and the SwiGLU adjoint from torch autograd.  Stored bf16 tensors must be
+# equal; fp32 gradients within one fp32 ulp.  Dropping any one rounding moves
+# a stored tensor by a bf16 ulp somewhere or a gradient by ~1e-3 relative.
+
+def _t64(v):
+    import torch
+    return torch.from_numpy(np.asarray(v, np.float64).copy())
+
+
+def _tbf(v):
+    """torch's rounding to bf16 (through fp32), back in fp64."""
+    import torch
+    return v.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def _swiglu_adjoint(g, u, dh):
+    import torch
+    g = g.clone().requires_grad_(True)
+    u = u.clone().requires_grad_(True)
+    h = torch.nn.functional.silu(g) * u
+    dg, du = torch.autograd.grad(h, (g, u), dh)
+    return dg.detach(), du.detach()
+
+
+def _one_expert(seed, M=45, d=40, f=24, r=None):
+    rng = _rng(seed)
+    c = dict(
+        x=O.to_bf16(rng.standard_normal((M, d)).astype(np.float32)),
+        w_gu=O.to_bf16((rng.standard_normal((1, 2 * f, d)) / np.sqrt(d)).astype(np.float32)),
+        w_down=O.to_bf16((rng.standard_normal((1, d, f)) / np.sqrt(f)).astype(np.float32)),
+        dy=O.to_bf16(rng.standard_normal((M, d)).astype(np.float32)),
+        w=(rng.random(M, dtype=np.float32) * 0.9 + 0.05).astype(np.float32),
+        off=np.array([0, M], np.int32), f=f)
+    if r is not None:
+        c["a_gu"] = O.to_bf16((rng.standard_normal((1, r, d)) / np.sqrt(d)).astype(np.float32))
+        c["b_gu"] = O.to_bf16((rng.standard_normal((1, 2 * f, r)) * 0.4).astype(np.float32))
+        c["a_dn"] = O.to_bf16((rng.standard_normal((1, r, f)) / np.sqrt(f)).astype(np.float32))
+        c["b_dn"] = O.to_bf16((rng.standard_normal((1, d, r)) * 0.4).astype(np.float32))
+        c["scale"] = 0.75
+    return c
+
+
+def _same_stored(name, got, ref):
+    ref = ref.numpy().astype(np.float32)
+    assert np.array_equal(np.asarray(got, np.float32), ref), (
+        name, int(np.count_nonzero(np.asarray(got, np.float32) != ref)))
+
+
+def _same_fp32(name, got, ref):
+    ref = ref.numpy()
+    got = np.asarray(got, np.float64)
+    tol = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= tol), (name, float(np.max(np.abs(got - ref))))
+
+
+@pytest.mark.parametrize("seed", [61, 62])
+def test_expert_backward_storage_points_by_torch(seed):
+    import torch
+    c = _one_expert(seed)
+    f = c["f"]
+    gu_o, h_o, y_o = O.expert_ffn_fwd(c["x"], c["off"], c["w_gu"], c["w_down"], c["w"], True)
+    b = O.expert_ffn_bwd(c["x"], gu_o, c["off"], c["w_gu"], c["w_down"], c["w"], c["dy"], True)
+    X, Wg, Wd, dY, w = (_t64(c[n]) for n in ("x", "w_gu", "w_down", "dy", "w"))
+    Wg, Wd, w = Wg[0], Wd[0], w[:, None]
+    gu = _tbf(X @ Wg.T)
+    g, u = gu[:, :f], gu[:, f:]
+    h = _tbf(torch.nn.functional.silu(g) * u)
+    y = _tbf(w * (h @ Wd.T))
+    _same_stored("gu", gu_o, gu)
+    _same_stored("h", h_o, h)
+    _same_stored("y_perm", y_o, y)
+    gd = dY @ Wd                                   # d(loss)/d(w * h W_down^T) pulled to h
+    drs = (h * gd).sum(1)
+    dg, du = _swiglu_adjoint(g, u, w * gd)
+    dgu = _tbf(torch.cat([dg, du], 1))
+    dx = _tbf(dgu @ Wg)
+    S = _tbf(w * dY)                               # the row-weighted upstream gradient, stored
+    _same_stored("dgu", b["dgu"], dgu)
+    _same_stored("dx_perm", b["dx_perm"], dx)
+    _same_fp32("d_row_scale", b["d_row_scale"], drs)
+    _same_fp32("dw_down", b["dw_down"][0], S.T @ h)
+    _same_fp32("dw_gu", b["dw_gu"][0], dgu.T @ X)
+
+
+@pytest.mark.parametrize("seed", [71, 72])
+def test_lora_storage_points_by_torch(seed):
+    import torch
+    c = _one_expert(seed, r=8)
+    f, s = c["f"], c["scale"]
+    gu_o, h_o, y_o, zg_o, zd_o = O.expert_ffn_fwd_lora(
+        c["x"], c["off"], c["w_gu"], c["w_down"], c["w"], c["a_gu"], c["b_gu"], c["a_dn"],
+        c["b_dn"], s, True)
+    b = O.expert_ffn_bwd_lora(c["x"], gu_o, c["off"], c["w_gu"], c["w_down"], c["w"], c["dy"],
+                              c["a_gu"], c["b_gu"], c["a_dn"], c["b_dn"], s, zg_o, zd_o, True)
+    X, Wg, Wd, dY, w = (_t64(c[n]) for n in ("x", "w_gu", "w_down", "dy", "w"))
+    Ag, Bg, Ad, Bd = (_t64(c[n])[0] for n in ("a_gu", "b_gu", "a_dn", "b_dn"))
+    Wg, Wd, w = Wg[0], Wd[0], w[:, None]
+    # forward: the rank-r activations are stored, the products join the accumulation
+    z_gu = _tbf(s * (X @ Ag.T))
+    gu = _tbf(X @ Wg.T + z_gu @ Bg.T)
+    g, u = gu[:, :f], gu[:, f:]
+    h = _tbf(torch.nn.functional.silu(g) * u)
+    z_dn = _tbf(s * (h @ Ad.T))
+    y = _tbf(w * (h @ Wd.T + z_dn @ Bd.T))
+    for n, got, ref in (("z_gu", zg_o, z_gu), ("gu", gu_o, gu), ("h", h_o, h),
+                        ("z_dn", zd_o, z_dn), ("y_perm", y_o, y)):
+        _same_stored(n, got, ref)
+    # backward with frozen experts
+    u_dn = _tbf(s * (dY @ Bd))
+    gd = dY @ Wd + u_dn @ Ad
+    dg, du = _swiglu_adjoint(g, u, w * gd)
+    dgu = _tbf(torch.cat([dg, du], 1))
+    u_gu = _tbf(s * (dgu @ Bg))
+    dx = _tbf(dgu @ Wg + u_gu @ Ag)
+    S = _tbf(w * dY)
+    wu_dn = _tbf(w * u_dn)                         # the row-weighted u_dn, stored like S
+    for n, got, ref in (("u_dn", b["u_dn"], u_dn), ("dgu", b["dgu"], dgu),
+                        ("u_gu", b["u_gu"], u_gu), ("dx_perm", b["dx_perm"], dx)):
+        _same_stored(n, got, ref)
+    _same_fp32("d_row_scale", b["d_row_scale"], (h * gd).sum(1))
+    _same_fp32("db_gu", b["db_gu"][0], dgu.T @ z_gu)
+    _same_fp32("da_gu", b["da_gu"][0], u_gu.T @ X)
+    _same_fp32("db_dn", b["db_dn"][0], S.T @ z_dn)
+    _same_fp32("da_dn", b["da_dn"][0], wu_dn.T @ h)
