@@ -128,6 +128,82 @@ def cpu_baseline(w, a, sample_tokens, min_seconds=10.0):
                       (sample_tokens, w.T, passes, dt)}
 
 
+def time_ep_share(steps, warmup, dev):
+    """One expert-parallel rank's share (4 local experts, 8192 pre-routed rows,
+    d = f = 2880): the grouped FFN forward + backward alone, as ExpertShare
+    runs it.  Rows per second, the grouped GEMMs' event times and their
+    fraction of the bf16 MFMA peak, and the dominant GEMM's roofline."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    from mixture_experts_layer_03_amd import inputs as I
+    from mixture_experts_layer_03_amd.layer import ExpertShare
+    w = I.EP8_SHARE
+    a = I.make_inputs(w)
+
+    def up(v, bf=True):
+        if bf:
+            return torch.from_numpy(I.bf16_bits(v).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+
+    xp, wgu, wd, dyp = (up(a[n]) for n in ("x_perm", "w_gu", "w_down", "dy_perm"))
+    wp = up(a["w_perm"], False)
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(a["counts"])]).astype(np.int32)).to(dev)
+    sh = ExpertShare(w.T, w.d, w.E, w.f, device=dev)
+
+    def step():
+        sh.forward(xp, off, wgu, wd, wp)
+        sh.backward(xp, off, wgu, wd, wp, dyp)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    abi.moe_timing_reset()
+    abi.moe_timing_enable(True)
+    nprof = 5
+    for _ in range(nprof):
+        step()
+    torch.cuda.synchronize()
+    abi.moe_timing_enable(False)
+    R = w.T
+    flops = gemm_flops(R, w.d, w.f)
+    nbytes = gemm_bytes(R, w.d, w.f, w.E)
+    us = {}
+    for n in flops:
+        ms, cnt = abi.moe_timing_query(n)
+        if cnt:
+            us[n] = 1e3 * ms / cnt
+    abi.moe_timing_reset()
+    out = {"workload": w.name, "counts": [int(c) for c in a["counts"]],
+           "ms_per_step": round(el * 1e3 / steps, 4), "rows_per_s": round(R * steps / el, 1),
+           "kernels_us": {n: round(v, 1) for n, v in us.items()}}
+    if us:
+        tot_f = sum(flops[n] for n in us)
+        tot_t = sum(us.values()) * 1e-6
+        out["grouped_gemm_tflops"] = round(tot_f / tot_t / 1e12, 1)
+        out["grouped_gemm_frac_of_bf16_peak"] = round(tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        dom = max(us, key=us.get)
+        t = us[dom] * 1e-6
+        t_m, t_h = flops[dom] / (PEAK_BF16_TFLOPS * 1e12), nbytes[dom] / (PEAK_HBM_GBS * 1e9)
+        if t_h > t_m:
+            ach = nbytes[dom] / t / 1e9
+            out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(ach / PEAK_HBM_GBS, 4)}
+        else:
+            ach = flops[dom] / t / 1e12
+            out["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    del sh
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +221,8 @@ def main():
                          "for dW_gate_up) or stored X_perm / dY_perm")
     ap.add_argument("--no-row-paths", action="store_true",
                     help="skip timing the other row arrangements")
+    ap.add_argument("--no-ep-share", action="store_true",
+                    help="skip timing the expert-parallel rank's share (grouped FFN alone)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (reference for HBM "
                          "byte counters)")
@@ -330,6 +408,11 @@ def main():
             row_paths[name] = {"ms_per_step": round(gel * 1e3 / args.steps, 4)}
             del gblk
 
+    ep_share = None
+    if not args.no_ep_share:
+        print("bench: expert-parallel rank share", file=sys.stderr, flush=True)
+        ep_share = time_ep_share(args.steps, max(2, args.warmup), dev)
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -454,6 +537,7 @@ def main():
         "lora": lora_out,
         "rows": args.rows,
         "row_paths": row_paths,
+        "ep_share": ep_share,
     }
     print(json.dumps(out), flush=True)
 

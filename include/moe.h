@@ -84,8 +84,11 @@ int moe_router_logits(const void *x, const void *w_r, const float *bias,
  * Per-token top-k and the combine weights (the "per-token top-k router" and
  * "weighted by the top-k probabilities" of the EP token-routing figure).
  * topk_idx[t,0..k-1]: the k largest logits of token t, by value descending;
- * equal values go to the lower expert id (-0 equals +0).  topk_w[t,j] =
- * softmax over the k selected logits.  Logits must be finite.
+ * equal values go to the lower expert id (-0 equals +0); a NaN ranks below
+ * every number (NaNs among themselves by lower id) and +-inf order as numbers,
+ * so the selection is always defined.  topk_w[t,j] = softmax over the k
+ * selected logits (NaN for every j when the selection holds a NaN or its
+ * largest logit is +inf; finite logits are the intended use).
  * logits: [T,E] fp32; topk_idx: [T,k] int32 (out); topk_w: [T,k] fp32 (out).
  */
 int moe_route(const float *logits, int64_t T, int E, int k,

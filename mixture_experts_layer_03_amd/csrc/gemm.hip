@@ -1047,10 +1047,19 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     MOE_ADVANCE();                                                                            \
   } while (0)
 
-  // prologue: the first NS stages
+  // prologue: the first NS stages.  GP: planning stage n reads the slot
+  // entry of stage n + 1; entries 1..NS-1 came with the initial loads (waited
+  // for above), entry NS with stage 0's loads, so the plan of stage NS - 1
+  // first waits for stage 0 (NS - 2 younger stages in flight).  From then on
+  // MOE_SYNC has stage s_done + 1 landed before stage s_done + NS is planned,
+  // and that stage carried the entry the plan reads.
 #pragma unroll
-  for (int n = 0; n < NS; ++n)
+  for (int n = 0; n < NS; ++n) {
+    if constexpr (GP) {
+      if (n == NS - 1 && ivalid) wait_stage<LOADS>(NS - 2);
+    }
     if (ivalid) MOE_ISSUE_ALL();
+  }
 
   // ---- compute cursor
   int cL = first, cseq = 0;

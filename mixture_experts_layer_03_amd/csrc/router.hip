@@ -172,7 +172,12 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
 // The winner of round j is kept by lane j of the group.
 constexpr int kMaxPerLane = kMaxExperts / 64;   // 16
 
+// A total order: greater value first, equal values (-0 == +0) by lower id,
+// and a NaN below every number (NaNs among themselves by lower id), so every
+// lane of a group agrees on each round's winner whatever the logits hold.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  const bool na = va != va, nb = vb != vb;
+  if (na || nb) return nb && (!na || ia < ib);
   return va > vb || (va == vb && ia < ib);
 }
 

@@ -15,7 +15,8 @@ on one stream, with no host synchronisation in between:
   balance : moe_expert_load -> moe_bias_update (selection-bias step)
 
 With ``gather`` the grouped GEMMs read the token rows of X and dY where they
-load them (moe_grouped_ffn_fwd_gather / moe_grouped_ffn_bwd_gather):
+load them (moe_grouped_ffn_fwd_gather / moe_grouped_ffn_bwd_gather; past
+their size limits, gather_fits(), the block falls back to stored rows):
 dY_perm is never stored and moe_combine_bwd drops out.  X_perm is still
 written by moe_permute for the dW_gu GEMM (its stored rows are the faster
 operand there) unless ``store_x_perm`` is False; then moe_permute writes only
@@ -41,6 +42,13 @@ import torch
 from . import abi
 
 
+def gather_fits(T: int, d: int, k: int) -> bool:
+    """Whether the gathered grouped-FFN calls take this size: their token-row
+    offsets are 32-bit (T*d < 2^30) and the slot -> token division is exact
+    while T*k*k < 2^32 (moe_grouped_ffn_fwd_gather's documented limits)."""
+    return T * d < (1 << 30) and T * k * k < (1 << 32)
+
+
 class MoEBlock:
     def __init__(self, T: int, d: int, E: int, k: int, f: int, dtype=torch.bfloat16,
                  device="cuda", backward: bool = True, fuse_router_dx: bool = True,
@@ -48,6 +56,11 @@ class MoEBlock:
                  store_x_perm: bool = True):
         if gather and (lora_rank or dtype != torch.bfloat16):
             raise ValueError("gather needs bf16 experts without LoRA")
+        # beyond the gathered calls' limits the block runs on stored rows
+        # (the same results bit for bit)
+        self.gather_fallback = bool(gather and not gather_fits(T, d, k))
+        if self.gather_fallback:
+            gather = False
         self.gather = gather
         self.store_x_perm = store_x_perm or not gather
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f

@@ -152,13 +152,17 @@ def router_logits(x, w_r, bias=None, noise=None) -> np.ndarray:
 def route(logits, k: int):
     """Per-token top-k (value descending, ties to the lower expert id) and the
     softmax over the k selected logits.  Returns (topk_idx int32 [T,k],
-    topk_w fp32 [T,k])."""
+    topk_w fp32 [T,k]).  A NaN logit ranks below every number (NaNs among
+    themselves by expert id); a selection holding a NaN, or whose largest
+    logit is +inf, gets NaN weights."""
     L = np.asarray(logits, dtype=np.float32)
-    # A stable sort of the negated values keeps equal values in expert order.
+    # A stable sort of the negated values keeps equal values in expert order;
+    # numpy sorts NaN after every number.
     idx = np.argsort(-L, axis=1, kind="stable")[:, :k].astype(np.int32)
     sel = _f64(np.take_along_axis(L, idx, axis=1))
-    ex = np.exp(sel - sel[:, :1])
-    w = ex / ex.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        ex = np.exp(sel - sel[:, :1])
+        w = ex / ex.sum(axis=1, keepdims=True)
     return idx, w.astype(np.float32)
 
 

@@ -326,3 +326,60 @@ def test_row_pieces_cover_each_chunk_once(nch):
                 c = piece * pw + 64 * h + np.arange(64)
                 seen[c[c < nvec]] += 1
         assert (seen == 1).all(), nvec
+
+
+# ---------------------------------------------------------------- gathered dW_gu: slot ring order
+#
+# Model of the per-wave ring of top-k slot entries in the dW_gate_up GEMM that
+# gathers X (GP): stage e's entry is written by a 4-byte direct-to-LDS load
+# issued with the loads of stage e - NS (entries 0..NS-1 by the initial loads,
+# which are waited for), and read when stage e - 1 is planned.  Loads complete
+# in issue order; a wait leaves at most N loads in flight.  Every read must
+# find its entry landed, and no entry may be overwritten (ring of 8) before
+# it is read.
+
+def _ring_schedule(NS, LOADS, total, prologue_wait=True):
+    """Returns, for each plan, (entry read, whether the ring slot held it)."""
+    inflight = []                                   # FIFO: entry number or None (data)
+    slot = {e % 8: e for e in range(NS)}            # initial loads, waited for
+    reads = []
+
+    def wait(n):
+        while len(inflight) > n:
+            e = inflight.pop(0)
+            if e is not None:
+                slot[e % 8] = e
+
+    s_issued = 0
+
+    def issue():
+        nonlocal s_issued
+        e = s_issued + 1
+        reads.append((e, slot.get(e % 8) == e))
+        inflight.extend([None] * (LOADS - 1) + [s_issued + NS])
+        s_issued += 1
+
+    for n in range(min(NS, total)):
+        if prologue_wait and n == NS - 1:
+            wait((NS - 2) * LOADS)
+        issue()
+    for s_done in range(total):
+        has_next = s_done + 1 < s_issued
+        younger = min(3, s_issued - s_done - 2) if has_next else 0
+        wait(younger * LOADS)
+        if s_issued < total:
+            issue()
+    return reads
+
+
+@pytest.mark.parametrize("NS,LOADS", [(2, 5), (3, 5), (4, 5), (4, 9)])
+def test_gathered_slot_ring_entries_land_before_they_are_read(NS, LOADS):
+    for total in (1, NS, NS + 1, 40):
+        for e, ok in _ring_schedule(NS, LOADS, total):
+            if e < total:                 # entries past the last stage read nothing
+                assert ok, (NS, LOADS, total, e)
+
+
+def test_slot_ring_without_the_prologue_wait_reads_early():
+    reads = _ring_schedule(4, 5, 40, prologue_wait=False)
+    assert any(not ok for e, ok in reads if e < 40)

@@ -659,3 +659,27 @@ def test_lora_storage_points_by_torch(seed):
     _same_fp32("da_gu", b["da_gu"][0], u_gu.T @ X)
     _same_fp32("db_dn", b["db_dn"][0], S.T @ z_dn)
     _same_fp32("da_dn", b["da_dn"][0], wu_dn.T @ h)
+
+
+def test_topk_order_with_nan_and_infinities():
+    """NaN ranks below every number (NaNs by id); +-inf order as numbers;
+    -0 ties +0.  Checked against a plain selection loop with that order."""
+    inf, nan = np.inf, np.nan
+    L = np.array([[1.0, nan, -inf, 2.0, nan, 0.5],
+                  [nan, nan, nan, nan, 1.0, nan],
+                  [-0.0, 0.0, -inf, -inf, nan, -1.0],
+                  [inf, 3.0, nan, inf, -inf, 0.0]], np.float32)
+
+    def key(v, e):                      # larger key = better
+        return (0, 0.0, -e) if np.isnan(v) else (1, float(v), -e)
+
+    for k in (1, 2, 3, 4, 6):
+        idx, w = O.route(L, k)
+        for t in range(L.shape[0]):
+            order = sorted(range(L.shape[1]), key=lambda e: key(L[t, e], e), reverse=True)
+            assert idx[t].tolist() == order[:k], (t, k)
+            sel = L[t, order[:k]]
+            if np.isnan(sel).any() or sel[0] == inf:
+                assert np.isnan(w[t]).all()
+            else:
+                assert abs(float(w[t].astype(np.float64).sum()) - 1.0) < 1e-6
