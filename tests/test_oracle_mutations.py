@@ -31,8 +31,8 @@ MUTATIONS = [
     ("ties resolved to the higher id", 'idx = np.argsort(-L, axis=1, kind="stable")[:, :k]',
      'idx = (L.shape[1] - 1 - np.argsort(-L[:, ::-1], axis=1, kind="stable"))[:, :k]'),
     ("softmax over all experts, not renormalised",
-     "sel[:, :1])\n    w = ex / ex.sum(axis=1, keepdims=True)",
-     "sel[:, :1])\n    w = ex / np.exp(L.astype(np.float64) - sel[:, :1]).sum(axis=1, keepdims=True)"),
+     "sel[:, :1])\n        w = ex / ex.sum(axis=1, keepdims=True)",
+     "sel[:, :1])\n        w = ex / np.exp(L.astype(np.float64) - sel[:, :1]).sum(axis=1, keepdims=True)"),
     ("H not rounded to bf16", "h = store(silu(gu[:, :f]) * _f64(gu[:, f:]), bf16)",
      "h = np.asarray(silu(gu[:, :f]) * _f64(gu[:, f:]), np.float32)"),
     ("gate and up halves swapped", "h = store(silu(gu[:, :f]) * _f64(gu[:, f:]), bf16)",
