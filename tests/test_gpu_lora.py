@@ -156,6 +156,7 @@ def test_lora_full_size():
     experts and rank-16 LoRA, as the benchmark times it, against the oracle:
     routing bit for bit, every row tensor and LoRA factor gradient in full."""
     import torch
+    from mixture_experts_layer_03_amd import abi
     from mixture_experts_layer_03_amd.layer import MoEBlock
     dev_ = need_gpu()
     w, r, scale = I.GPTOSS, 16, 1.0
