@@ -140,6 +140,25 @@ int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, int E, int64
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_grouped_ffn_fwd without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results (bit for bit), errors and
+ * conventions as moe_grouped_ffn_fwd minus ws / ws_bytes.  Its scratch -- the
+ * forward's two tile-start tables with their tile counters -- lives in a
+ * static device array of 8704 bytes (enough for E <= 1024; a larger need
+ * returns MOE_ERR_UNSUPPORTED), one copy per device, held until the process
+ * ends; its address is taken once per device on that device's first call.
+ * The call allocates nothing and clears what it needs itself, in stream
+ * order.  Every call on one device shares that array: calls that may run
+ * concurrently on one device (different streams, or threads) race and must
+ * be serialised by the caller.
+ */
+int moe_grouped_ffn_fwd_noalloc(const void *x_perm, const int32_t *offsets, int E, int64_t R,
+                                int d, int f, const void *w_gu, const void *w_down,
+                                const float *row_scale, int dtype, void *gu, void *h,
+                                void *y_perm, void *stream);
+
+/*
  * Backward of moe_grouped_ffn_fwd (expert weights receive gradients: the
  * "expert gradient all-to-all" that LoRA skips, section "One trainer
  * architecture, one parallelism stack", is the exchange of these).  Per row r

@@ -40,6 +40,9 @@ _SIGS = {
     "moe_grouped_ffn_fwd": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
                                    _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_fwd_noalloc": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32,
+                                           _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                           _c_void_p, _c_void_p, _c_void_p]),
     "moe_grouped_ffn_bwd": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32,
                                    _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -185,6 +188,15 @@ def moe_grouped_ffn_fwd(x_perm, offsets, E, w_gu, w_down, row_scale, gu, h, y_pe
         _p(x_perm), _p(offsets), E, R, d, f, _p(w_gu), _p(w_down), _p(row_scale),
         _dtype_code(x_perm), _p(gu), _p(h), _p(y_perm), _p(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn_fwd_noalloc(x_perm, offsets, E, w_gu, w_down, row_scale, gu, h, y_perm,
+                                stream=None):
+    R, d = x_perm.shape
+    f = w_down.shape[2]
+    _check("moe_grouped_ffn_fwd_noalloc", lib().moe_grouped_ffn_fwd_noalloc(
+        _p(x_perm), _p(offsets), E, R, d, f, _p(w_gu), _p(w_down), _p(row_scale),
+        _dtype_code(x_perm), _p(gu), _p(h), _p(y_perm), _stream(stream)))
 
 
 def moe_grouped_ffn_bwd(x_perm, gu, h, offsets, E, w_gu, w_down, row_scale, dy_perm, dgu,

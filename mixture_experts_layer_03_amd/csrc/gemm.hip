@@ -28,6 +28,8 @@
 // fragment with the 8 bf16 of 16-byte chunk (l/16) of the 32-wide k step (the
 // same chunk map for both operands, so the dot products pair correctly); the
 // result holds D[4*(l/16)+v][l%16], v = 0..3.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -1811,23 +1813,101 @@ static int ffn_fwd_bf16(GemmArgs a, int64_t R, void *ws, hipStream_t s, bool gat
       a, R, pt_dn, ts1, "gg_fwd_down_scale", s);
 }
 
+// Argument checks shared by the forward entry points (0 = go on).
+static int check_ffn_fwd_args(const char *fn, const void *x_perm, const int32_t *offsets, int E,
+                              int64_t R, int d, int f, const void *w_gu, const void *w_down,
+                              int dtype, const void *gu, const void *h, const void *y_perm) {
+  int rc = check_ffn(fn, E, R, d, f, dtype);
+  if (rc) return rc;
+  if (R == 0) return MOE_OK;
+  MOE_REQUIRE(x_perm && offsets && w_gu && w_down && h && y_perm, MOE_ERR_INVALID_ARG,
+              "%s: null pointer", fn);
+  MOE_REQUIRE(aligned16(x_perm) && aligned16(w_gu) && aligned16(w_down) && aligned16(h) &&
+                  aligned16(y_perm) && (!gu || aligned16(gu)),
+              MOE_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  return MOE_OK;
+}
+
+// The forward's launches on validated arguments; ws holds at least the two
+// tile-start tables (2 * tile_start_bytes(E)).
+static int ffn_fwd_run(const void *x_perm, const int32_t *offsets, int E, int64_t R, int d, int f,
+                       const void *w_gu, const void *w_down, const float *row_scale, int dtype,
+                       void *gu, void *h, void *y_perm, void *ws, hipStream_t s);
+
 extern "C" int moe_grouped_ffn_fwd(const void *x_perm, const int32_t *offsets, int E, int64_t R,
                                    int d, int f, const void *w_gu, const void *w_down,
                                    const float *row_scale, int dtype, void *gu, void *h,
                                    void *y_perm, void *ws, size_t ws_bytes, void *stream) {
   clear_error();
-  int rc = check_ffn("moe_grouped_ffn_fwd", E, R, d, f, dtype);
-  if (rc) return rc;
-  if (R == 0) return MOE_OK;
-  MOE_REQUIRE(x_perm && offsets && w_gu && w_down && h && y_perm, MOE_ERR_INVALID_ARG,
-              "moe_grouped_ffn_fwd: null pointer");
-  MOE_REQUIRE(aligned16(x_perm) && aligned16(w_gu) && aligned16(w_down) && aligned16(h) &&
-                  aligned16(y_perm) && (!gu || aligned16(gu)),
-              MOE_ERR_INVALID_ARG, "moe_grouped_ffn_fwd: pointers must be 16-byte aligned");
+  int rc = check_ffn_fwd_args("moe_grouped_ffn_fwd", x_perm, offsets, E, R, d, f, w_gu, w_down,
+                              dtype, gu, h, y_perm);
+  if (rc || R == 0) return rc;
   const size_t need = moe_grouped_ffn_workspace_size(R, E, d, f, dtype);
   MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_grouped_ffn_fwd: workspace %zu < %zu",
               ws_bytes, need);
-  hipStream_t s = (hipStream_t)stream;
+  return ffn_fwd_run(x_perm, offsets, E, R, d, f, w_gu, w_down, row_scale, dtype, gu, h, y_perm,
+                     ws, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ allocation-free forward
+//
+// moe_grouped_ffn_fwd_noalloc keeps the forward's scratch -- two tile-start
+// tables with their per-XCD tile counters, 2 * tile_start_bytes(E) bytes --
+// in this file-scope array instead of a caller workspace.  Each device holds
+// its own copy until the process ends; the host takes its device address once
+// per device (hipGetSymbolAddress, on that device's first call) and passes
+// that address to the kernels, never the array's name.  The tile-prefix
+// kernel rewrites the tables and clears the counters at the start of every
+// call, so nothing needs clearing in between; calls that overlap on one device
+// share the array and race.
+constexpr size_t kTileStartMax = (sizeof(int32_t) * (kMaxExperts + 1 + 8) + 255) / 256 * 256;
+constexpr size_t kNoAllocScratchBytes = 2 * kTileStartMax;   // 8704 bytes
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[kMaxDevices];
+
+static int scratch_address(const char *fn, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  MOE_REQUIRE(e == hipSuccess, MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "%s: device %d", fn, dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    MOE_REQUIRE(e == hipSuccess && p, MOE_ERR_HIP, "%s: hipGetSymbolAddress: %s", fn,
+                hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
+extern "C" int moe_grouped_ffn_fwd_noalloc(const void *x_perm, const int32_t *offsets, int E,
+                                           int64_t R, int d, int f, const void *w_gu,
+                                           const void *w_down, const float *row_scale, int dtype,
+                                           void *gu, void *h, void *y_perm, void *stream) {
+  clear_error();
+  const char *fn = "moe_grouped_ffn_fwd_noalloc";
+  int rc = check_ffn_fwd_args(fn, x_perm, offsets, E, R, d, f, w_gu, w_down, dtype, gu, h, y_perm);
+  if (rc || R == 0) return rc;
+  const size_t need = 2 * tile_start_bytes(E);
+  MOE_REQUIRE(need <= kNoAllocScratchBytes, MOE_ERR_UNSUPPORTED,
+              "%s: E=%d needs %zu bytes of scratch, more than the static %zu", fn, E, need,
+              kNoAllocScratchBytes);
+  void *ws = nullptr;
+  rc = scratch_address(fn, &ws);
+  if (rc) return rc;
+  return ffn_fwd_run(x_perm, offsets, E, R, d, f, w_gu, w_down, row_scale, dtype, gu, h, y_perm,
+                     ws, (hipStream_t)stream);
+}
+
+static int ffn_fwd_run(const void *x_perm, const int32_t *offsets, int E, int64_t R, int d, int f,
+                       const void *w_gu, const void *w_down, const float *row_scale, int dtype,
+                       void *gu, void *h, void *y_perm, void *ws, hipStream_t s) {
+  int rc = MOE_OK;
   if (dtype == MOE_F32) {
     const int64_t n1 = R * (f / 4), n2 = R * (d / 4);
     MOE_LAUNCH("ffn_gu_f32", s,
