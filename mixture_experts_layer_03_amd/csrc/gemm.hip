@@ -523,6 +523,14 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, c
 
 // ------------------------------------------------------------------ epilogues
 
+// h = silu(g) u from the stored (bf16) g and u, in fp32, before its own bf16
+// store.  The forward's SwiGLU epilogue and the backward's dSwiGLU epilogue
+// both form it with this one expression, so the backward recomputes the
+// stored H bit for bit instead of loading it.
+__device__ __forceinline__ float swiglu_h(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
 constexpr int kDhBatch = 4;   // dSwiGLU epilogue: fragments per batch of saved-activation loads
 //
 // Lane holds D[prow[i] + 4*(lane/16) + v][qrow[j] + lane%16].
@@ -550,7 +558,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
         for (int v = 0; v < 4; ++v) {
           g[v] = round_bf16(acc[i][j][v]);
           u[v] = round_bf16(acc[i + FP / 2][j][v]);
-          hv[v] = g[v] / (1.0f + __expf(-g[v])) * u[v];
+          hv[v] = swiglu_h(g[v], u[v]);
         }
         if (a.o_gu) {
           *reinterpret_cast<u32x2_t *>(a.o_gu + r * f2 + n) =
@@ -595,20 +603,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
       const bool rowok = q < Me;
       const int64_t r = (int64_t)seg0 + (rowok ? q : 0);
       const float w = a.row_scale ? a.row_scale[r] : 1.0f;
-      // the saved g, u, h of kDhBatch fragments' columns at a time (one
-      // wait each); columns past f read column 0 and store nothing
+      // the saved g, u of kDhBatch fragments' columns at a time (one wait
+      // each; H is recomputed from them, bit for bit as stored); columns
+      // past f read column 0 and store nothing
       float part = 0.0f;
 #pragma unroll
       for (int hh = 0; hh < FP / kDhBatch; ++hh) {
         constexpr int FH = kDhBatch;
-        u32x2_t g2[FH], u2[FH], h2[FH];
+        u32x2_t g2[FH], u2[FH];
 #pragma unroll
         for (int ii = 0; ii < FH; ++ii) {
           const int c = p0 + prow[hh * FH + ii] + er;
           const int cc = c < f ? c : 0;
           g2[ii] = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + cc);
           u2[ii] = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + f + cc);
-          h2[ii] = *reinterpret_cast<const u32x2_t *>(a.h + r * f + cc);
         }
 #pragma unroll
         for (int ii = 0; ii < FH; ++ii) {
@@ -618,10 +626,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
           float dg[4], du[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t gw = g2[ii][v >> 1], uw = u2[ii][v >> 1], hw = h2[ii][v >> 1];
+            const uint32_t gw = g2[ii][v >> 1], uw = u2[ii][v >> 1];
             const float g = bf16_bits_to_f32((v & 1) ? (gw >> 16) : (gw & 0xffffu));
             const float u = bf16_bits_to_f32((v & 1) ? (uw >> 16) : (uw & 0xffffu));
-            const float hv = bf16_bits_to_f32((v & 1) ? (hw >> 16) : (hw & 0xffffu));
+            const float hv = round_bf16(swiglu_h(g, u));
             const float sg = 1.0f / (1.0f + __expf(-g));
             const float silu = g * sg;
             const float gd = acc[i][j][v];

@@ -17,19 +17,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (lo in bits 0..15) with gfx950's packed conversion
+// (one v_cvt_pk_bf16_f32): round to nearest, ties to even -- on the box it
+// equals the bit arithmetic u + 0x7fff + ((u >> 16) & 1) >> 16 on every
+// non-NaN fp32 pattern, denormals included; a NaN stays a quiet NaN (sign and
+// leading payload bits kept).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2v_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) { return pack_bf16x2(v, 0.0f) & 0xffffu; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ float round_bf16(float v) { return bf16_bits_to_f32(f32_to_bf16_bits(v)); }
-// pack two fp32 into two bf16 (lo in bits 0..15)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
 
 // Storage traits: bf16 (uint16 storage) or fp32.
 template <typename T> struct Store;

@@ -87,6 +87,11 @@ def check_lora_ffn(got, a, lf, scale, offsets, x_perm, w_perm, dy_perm, wg=None)
     ref.update(O.expert_ffn_bwd_lora(x_perm, o_gu, offsets, a["w_gu"], a["w_down"], w_perm,
                                      dy_perm, lf["a_gu"], lf["b_gu"], lf["a_dn"], lf["b_dn"],
                                      scale, o_zg, o_zd, True))
+    # store(w u_dn) is one fp32 product rounded to bf16 on the device: bit for
+    # bit the oracle's rounding of the device's own operands (pins the
+    # device's round-to-nearest-even)
+    wg_ = np.asarray(w_perm if wg is None else wg, np.float32)
+    assert np.array_equal(got["uw_dn"], O.to_bf16(wg_[:, None] * got["u_dn"].astype(np.float32)))
     lora = (lf["a_gu"], lf["b_gu"], lf["a_dn"], lf["b_dn"], scale)
     return PC.check_ffn(got, ref, x_perm, offsets, a["w_gu"], a["w_down"],
                         w_perm if wg is None else wg, w_perm, dy_perm, lora=lora)
