@@ -15,6 +15,12 @@ every step through stored X_perm / dY_perm.  Both are bit-identical; the
 JSON line also times the other arrangements.  Inputs are resident in HBM
 before the timed region starts.
 
+The JSON line also carries, apart from the headline step: the other routed
+workloads' whole steps (--other-workloads, default the Zipf-skewed T=16384
+and the Qwen3-30B-A3B-like T=32768 layers), one expert-parallel rank's share
+(the grouped FFN alone over 8192 pre-routed rows), and the step with frozen
+experts and rank-16 LoRA.
+
 Prints one JSON line.  Besides throughput it reports the dominant kernel's
 roofline (its algorithmic FLOPs or HBM bytes per launch, whichever bounds it
 at peak, over its average launch time measured with HIP events on the stream
@@ -59,7 +65,8 @@ def gemm_bytes(R, d, f, E):
     return {
         "gg_fwd_gate_up_swiglu": b * (R * d + E * 2 * f * d + R * 2 * f + R * f),
         "gg_fwd_down_scale": b * (R * f + E * d * f + R * d) + 4.0 * R,
-        "gg_bwd_dh_dswiglu": b * (R * d + E * d * f + R * 2 * f + R * f + R * 2 * f) + 4.0 * R,
+        # dY rows, W_down, the saved GU (H is recomputed from it), dGU, w
+        "gg_bwd_dh_dswiglu": b * (R * d + E * d * f + R * 2 * f + R * 2 * f) + 4.0 * R,
         "gg_bwd_dx": b * (R * 2 * f + E * 2 * f * d + R * d),
         "gg_bwd_dw_down": b * (R * f + R * d) + 4.0 * E * d * f,
         "gg_bwd_dw_gate_up": b * (R * d + R * 2 * f) + 4.0 * E * 2 * f * d,
@@ -204,6 +211,68 @@ def time_ep_share(steps, warmup, dev):
     return out
 
 
+def time_routed_workload(key, steps, warmup, dev):
+    """The whole block fwd+bwd on another routed workload (gathered rows, as
+    the headline step): ms per step, tokens/s and the six grouped GEMMs'
+    fraction of the bf16 peak from their per-launch event times."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_03_amd import abi
+    from mixture_experts_layer_03_amd import inputs as I
+    from mixture_experts_layer_03_amd.layer import MoEBlock
+    w = I.BY_KEY[key]
+    a = I.make_inputs(w)
+
+    def up(v, bf=True):
+        if v is None:
+            return None
+        if bf:
+            return torch.from_numpy(I.bf16_bits(v).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+
+    x, wr, wgu, wd, dy = (up(a[n]) for n in ("x", "w_r", "w_gu", "w_down", "dy"))
+    bias, noise = up(a["bias"], False), up(a["noise"], False)
+    del a
+    blk = MoEBlock(w.T, w.d, w.E, w.k, w.f, dtype=torch.bfloat16, device=dev, gather=True)
+
+    def step():
+        blk.forward(x, wr, wgu, wd, bias, noise)
+        blk.backward(x, wr, wgu, wd, dy)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    abi.moe_timing_reset()
+    abi.moe_timing_enable(True)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    abi.moe_timing_enable(False)
+    flops = gemm_flops(w.R, w.d, w.f)
+    us = {}
+    for n in flops:
+        for kn in (n, n + "_gather"):
+            ms, cnt = abi.moe_timing_query(kn)
+            if cnt:
+                us[n] = 1e3 * ms / cnt
+    abi.moe_timing_reset()
+    out = {"workload": w.name, "ms_per_step": round(el * 1e3 / steps, 4),
+           "tokens_per_s": round(w.T * steps / el, 1),
+           "grouped_gemm_us": {n: round(v, 1) for n, v in us.items()}}
+    if us:
+        tot = sum(flops[n] for n in us) / (sum(us.values()) * 1e-6) / 1e12
+        out["grouped_gemm_tflops"] = round(tot, 1)
+        out["grouped_gemm_frac_of_bf16_peak"] = round(tot / PEAK_BF16_TFLOPS, 4)
+    del blk
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +290,8 @@ def main():
                          "for dW_gate_up) or stored X_perm / dY_perm")
     ap.add_argument("--no-row-paths", action="store_true",
                     help="skip timing the other row arrangements")
+    ap.add_argument("--other-workloads", default="c3,c5",
+                    help="routed workloads also timed (whole step, fewer steps), '' for none")
     ap.add_argument("--no-ep-share", action="store_true",
                     help="skip timing the expert-parallel rank's share (grouped FFN alone)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -408,6 +479,11 @@ def main():
             row_paths[name] = {"ms_per_step": round(gel * 1e3 / args.steps, 4)}
             del gblk
 
+    others = {}
+    for key in [k for k in args.other_workloads.split(",") if k and k != args.workload]:
+        print("bench: workload %s" % key, file=sys.stderr, flush=True)
+        others[key] = time_routed_workload(key, max(3, args.steps // 4), 2, dev)
+
     ep_share = None
     if not args.no_ep_share:
         print("bench: expert-parallel rank share", file=sys.stderr, flush=True)
@@ -538,6 +614,7 @@ def main():
         "rows": args.rows,
         "row_paths": row_paths,
         "ep_share": ep_share,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
 
