@@ -398,7 +398,8 @@ def main():
         abi.moe_timing_enable(False)
         launches = {"route_topk_biased": ["route_topk_biased"],
                     "expert_load": ["expert_load", "expert_load_reduce"],
-                    "bias_update": ["bias_update"], "aux_loss": ["aux_loss", "aux_loss_final"]}
+                    "bias_update": ["bias_update"],
+                    "aux_loss": ["aux_loss", "aux_loss_colsum", "aux_loss_final"]}
         for n in vb:
             us = 0.0
             for ln in launches[n]:

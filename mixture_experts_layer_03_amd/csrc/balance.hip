@@ -57,14 +57,47 @@ __global__ __launch_bounds__(256) void k_load_partial(const int32_t *__restrict_
   for (int e = threadIdx.x; e < E; e += 256) part[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-// load[e] = sum over blocks (ascending) of part[b][e]; optionally the bias step.
-__global__ __launch_bounds__(256) void k_load_reduce(const int32_t *__restrict__ part, int nblk,
-                                                     int E, int32_t *__restrict__ load) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+// Column sums of a [rows, E] table of per-block partials: a block of
+// kColWaves waves covers 64 experts (lane = expert, so each row's read is
+// one coalesced line per wave) and rows [y*kColRows, (y+1)*kColRows); wave w
+// takes the rows w, w + kColWaves, ... ascending, and the waves' sums are
+// added in wave order.  The order is fixed by the shape alone.
+constexpr int kColWaves = 16, kColRows = 256;
+
+template <typename T>
+__device__ __forceinline__ T col_sum(const T *__restrict__ tab, int rows, int E, int e, int y,
+                                     int w) {
+  const int r0 = y * kColRows, r1 = min(rows, r0 + kColRows);
+  T acc = T(0);
+  int r = r0 + w;
+  // four rows' loads in flight per lane, added in row order
+  for (; r + 3 * kColWaves < r1; r += 4 * kColWaves) {
+    T v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = e < E ? tab[(int64_t)(r + u * kColWaves) * E + e] : T(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += v[u];
+  }
+  for (; r < r1; r += kColWaves) acc += e < E ? tab[(int64_t)r * E + e] : T(0);
+  return acc;
+}
+
+// load[e] = sum over blocks of part[b][e] (integer counts: exact).
+__global__ __launch_bounds__(kColWaves * 64) void k_load_reduce(const int32_t *__restrict__ part,
+                                                                int nblk, int E,
+                                                                int32_t *__restrict__ load) {
+  __shared__ int red[kColWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
   int c = 0;
-  for (int b = 0; b < nblk; ++b) c += part[(int64_t)b * E + e];
-  load[e] = c;
+  for (int y = 0; y * kColRows < nblk; ++y) c += col_sum<int32_t>(part, nblk, E, e, y, w);
+  red[w][lane] = c;
+  __syncthreads();
+  if (w == 0 && e < E) {
+    int t = 0;
+    for (int i = 0; i < kColWaves; ++i) t += red[i][lane];
+    load[e] = t;
+  }
 }
 
 // b_e + rate * sign(n_valid*k - E*load_e): the sign is an exact integer
@@ -161,31 +194,36 @@ __global__ __launch_bounds__(256) void k_aux_partial(const float *__restrict__ l
   }
 }
 
-// One block of 1024 threads.  Psum_e = sum over blocks of psum[b][e]: Q =
-// 1024/E threads per expert (at least 1), thread q of expert e sums blocks
-// b = q, q+Q, ... ascending, and the Q partial sums are added in q order.
-// Then sum_e load_e * Psum_e by a fixed tree, aux = that * E / (n_valid^2 k);
-// out[0] = aux, out[1] = coeff * aux.
-__global__ __launch_bounds__(1024) void k_aux_final(const float *__restrict__ psum, int nblk,
+// Psum partials: pcol[y][e] = sum of psum[b][e] over the rows of row block
+// y (col_sum's order), grid (ceil(E/64), ceil(nblk/kColRows)).
+__global__ __launch_bounds__(kColWaves * 64) void k_aux_colsum(const float *__restrict__ psum,
+                                                               int nblk, int E,
+                                                               float *__restrict__ pcol) {
+  __shared__ float red[kColWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  red[w][lane] = col_sum<float>(psum, nblk, E, e, blockIdx.y, w);
+  __syncthreads();
+  if (w == 0 && e < E) {
+    float t = 0.0f;
+    for (int i = 0; i < kColWaves; ++i) t += red[i][lane];
+    pcol[(int64_t)blockIdx.y * E + e] = t;
+  }
+}
+
+// One block of 1024 threads.  Psum_e = sum over the row blocks y (ascending)
+// of pcol[y][e], then sum_e load_e * Psum_e by a fixed tree, aux = that * E /
+// (n_valid^2 k); out[0] = aux, out[1] = coeff * aux.
+__global__ __launch_bounds__(1024) void k_aux_final(const float *__restrict__ pcol, int ny,
                                                     const int32_t *__restrict__ load, int E,
                                                     float norm, float coeff,
                                                     float *__restrict__ out) {
-  __shared__ float part[1024];
   __shared__ float red[1024];
-  const int Q = E >= 1024 ? 1 : 1024 / E;
   const int tid = threadIdx.x;
-  const int e = tid / Q, q = tid % Q;
-  float acc = 0.0f;
-  if (e < E) {
-#pragma unroll 8
-    for (int b = q; b < nblk; b += Q) acc += psum[(int64_t)b * E + e];
-  }
-  part[tid] = acc;
-  __syncthreads();
   float term = 0.0f;
   if (tid < E) {
     float P = 0.0f;
-    for (int i = 0; i < Q; ++i) P += part[tid * Q + i];
+    for (int y = 0; y < ny; ++y) P += pcol[(int64_t)y * E + tid];
     term = (float)load[tid] * P;
   }
   red[tid] = term;
@@ -268,7 +306,8 @@ extern "C" int moe_expert_load(const int32_t *topk_idx, int64_t T, int64_t n_val
     MOE_LAUNCH("expert_load", s,
                k_load_partial<<<(unsigned)nblk, 256, 0, s>>>(topk_idx, nslots, E, part));
   MOE_LAUNCH("expert_load_reduce", s,
-             k_load_reduce<<<(unsigned)((E + 255) / 256), 256, 0, s>>>(part, (int)nblk, E, load));
+             k_load_reduce<<<(unsigned)((E + 63) / 64), kColWaves * 64, 0, s>>>(part, (int)nblk, E,
+                                                                              load));
   return check_launch("moe_expert_load");
 }
 
@@ -287,11 +326,20 @@ extern "C" int moe_bias_update(const int32_t *load, int64_t n_valid, int E, int 
   return check_launch("moe_bias_update");
 }
 
+// The per-block sums psum[nblk][E], then the row-block sums pcol[ny][E].
+static size_t aux_psum_bytes(int64_t nblk, int E) {
+  return align_up((size_t)nblk * (size_t)E * sizeof(float), 256);
+}
+static size_t aux_pcol_bytes(int64_t nblk, int E) {
+  return align_up((size_t)((nblk + kColRows - 1) / kColRows) * (size_t)E * sizeof(float), 256);
+}
+
 // Sized for one pass per block, which bounds the grid of every n_valid <= T.
 extern "C" size_t moe_aux_loss_workspace_size(int64_t T, int E) {
   if (T <= 0 || E <= 0 || E > kMaxExperts) return 256;
   const int64_t groups = 256 / route_group(E);
-  return align_up((size_t)((T + groups - 1) / groups) * (size_t)E * sizeof(float), 256);
+  const int64_t nmax = (T + groups - 1) / groups;
+  return aux_psum_bytes(nmax, E) + aux_pcol_bytes(nmax, E);
 }
 
 extern "C" int moe_aux_loss(const float *logits, const int32_t *load, int64_t T, int64_t n_valid,
@@ -311,12 +359,15 @@ extern "C" int moe_aux_loss(const float *logits, const int32_t *load, int64_t T,
   MOE_REQUIRE(logits && load && ws, MOE_ERR_INVALID_ARG, "moe_aux_loss: null pointer");
   const int64_t nblk = aux_blocks(n_valid, E);
   const int passes = aux_passes(n_valid, E);
-  MOE_REQUIRE(ws_bytes >= (size_t)nblk * (size_t)E * sizeof(float), MOE_ERR_WORKSPACE,
-              "moe_aux_loss: workspace %zu < %zu", ws_bytes, (size_t)nblk * (size_t)E * sizeof(float));
+  const size_t need = aux_psum_bytes(nblk, E) + aux_pcol_bytes(nblk, E);
+  MOE_REQUIRE(ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_aux_loss: workspace %zu < %zu", ws_bytes,
+              need);
   const double n = (double)n_valid;
   const float gscale = (float)((double)coeff * E / (n * n * k));
   const float norm = (float)((double)E / (n * n * k));
   float *psum = (float *)ws;
+  float *pcol = (float *)((char *)ws + aux_psum_bytes(nblk, E));
+  const int ny = (int)((nblk + kColRows - 1) / kColRows);
   const int G = route_group(E);
 #define AUX_CASE(GV)                                                                          \
   case GV:                                                                                    \
@@ -329,7 +380,10 @@ extern "C" int moe_aux_loss(const float *logits, const int32_t *load, int64_t T,
     AUX_CASE(1); AUX_CASE(2); AUX_CASE(4); AUX_CASE(8); AUX_CASE(16); AUX_CASE(32); AUX_CASE(64);
   }
 #undef AUX_CASE
+  MOE_LAUNCH("aux_loss_colsum", s,
+             k_aux_colsum<<<dim3((unsigned)((E + 63) / 64), (unsigned)ny), kColWaves * 64, 0, s>>>(
+                 psum, (int)nblk, E, pcol));
   MOE_LAUNCH("aux_loss_final", s,
-             k_aux_final<<<1, 1024, 0, s>>>(psum, (int)nblk, load, E, norm, coeff, aux_out));
+             k_aux_final<<<1, 1024, 0, s>>>(pcol, ny, load, E, norm, coeff, aux_out));
   return check_launch("moe_aux_loss");
 }
