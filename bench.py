@@ -57,19 +57,22 @@ def gemm_flops(R, d, f):
     }
 
 
-def gemm_bytes(R, d, f, E):
+def gemm_bytes(R, d, f, E, T=None):
     """Algorithmic HBM bytes of each grouped GEMM launch: every operand read
     once and every output written once (bf16 activations and weights, fp32
-    weight gradients and combine weights)."""
+    weight gradients and combine weights).  With T, the gathered forms: the
+    gate/up and dW_gate_up GEMMs read the token rows of X, the dH GEMM those
+    of dY, from the unpermuted [T, d] tensor, whose bytes count once."""
     b = 2.0
+    t = R if T is None else T
     return {
-        "gg_fwd_gate_up_swiglu": b * (R * d + E * 2 * f * d + R * 2 * f + R * f),
+        "gg_fwd_gate_up_swiglu": b * (t * d + E * 2 * f * d + R * 2 * f + R * f),
         "gg_fwd_down_scale": b * (R * f + E * d * f + R * d) + 4.0 * R,
         # dY rows, W_down, the saved GU (H is recomputed from it), dGU, w
-        "gg_bwd_dh_dswiglu": b * (R * d + E * d * f + R * 2 * f + R * 2 * f) + 4.0 * R,
+        "gg_bwd_dh_dswiglu": b * (t * d + E * d * f + R * 2 * f + R * 2 * f) + 4.0 * R,
         "gg_bwd_dx": b * (R * 2 * f + E * 2 * f * d + R * d),
         "gg_bwd_dw_down": b * (R * f + R * d) + 4.0 * E * d * f,
-        "gg_bwd_dw_gate_up": b * (R * d + R * 2 * f) + 4.0 * E * 2 * f * d,
+        "gg_bwd_dw_gate_up": b * (t * d + R * 2 * f) + 4.0 * E * 2 * f * d,
     }
 
 
@@ -501,14 +504,17 @@ def main():
 
     R = w.R
     flops = gemm_flops(R, w.d, w.f)
-    nbytes = gemm_bytes(R, w.d, w.f, w.E)
-    # a gathered GEMM does the algorithmic work of its stored-row counterpart
+    # a gathered GEMM does the algorithmic work of its stored-row counterpart;
+    # its gathered operand's bytes are the unpermuted token rows'
     gemm_us, launch_name = {}, {}
     for n in flops:
         for kn in (n, n + "_gather"):
             if kn in kernels:
                 gemm_us[n] = kernels[kn]["avg_us"]
                 launch_name[n] = kn
+    stored_b, gathered_b = gemm_bytes(R, w.d, w.f, w.E), gemm_bytes(R, w.d, w.f, w.E, T=w.T)
+    nbytes = {n: (gathered_b if launch_name[n].endswith("_gather") else stored_b)[n]
+              for n in gemm_us}
     roofline = None
     gemm_frac = None
     gemm_roof_frac = None
