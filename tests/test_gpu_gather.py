@@ -15,7 +15,7 @@ import pytest
 
 from mixture_experts_layer_03_amd import inputs as I
 from tests.gpu_util import close, down, need_gpu, up
-from tests.test_gpu_parity import SMALL, run_oracle
+from tests.test_gpu_parity import EDGE, SMALL, run_oracle
 from tests import parity as PC
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,7 @@ def check_against_oracle(g, o, b, a, k):
     PC.check_layer(g, o, b, a, k)
 
 
-CASES = [w for w in SMALL if w.dtype == "bf16"]
+CASES = [w for w in SMALL + EDGE if w.dtype == "bf16"]
 
 
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])

@@ -103,6 +103,24 @@ def test_layer_forward_backward_matches_oracle(w):
     check_block(g, o, b, a, w.k)
 
 
+# The largest expert count and top-k the library takes (E <= 1024, k <= 32):
+# the per-expert tables the GEMMs stage in LDS and the 1024-thread prefix
+# scans run full, most of the 1024 experts get no rows or a few, and each
+# token's 32 rows are gathered by the combine and its adjoint.
+EDGE = [
+    _wl(600, 64, 1024, 8, 64, seed=17),
+    _wl(96, 136, 64, 32, 72, seed=18),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
+def test_largest_expert_count_and_top_k(w):
+    a = I.make_inputs(w)
+    g = run_gpu(w, a)
+    o, b = run_oracle(w, a)
+    check_block(g, o, b, a, w.k)
+
+
 @pytest.mark.parametrize("w", SMALL[:2] + SMALL[4:5], ids=[w.name for w in SMALL[:2] + SMALL[4:5]])
 def test_router_dx_fused_matches_stored_path(w):
     """dX with the router term formed in the gather pass equals, bit for bit,
