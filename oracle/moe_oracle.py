@@ -28,7 +28,7 @@ bf16 workloads, fp32 otherwise).  The one exception is the router logits, for
 which the pages fix fp32; their accumulation order is fixed in
 ``router_fma.c`` (a chain of fp32 fused multiply-adds over the hidden index).
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
   * softmax over the k selected logits (equal to a full softmax renormalised
     over the selected experts);
   * top-k ordered by value, descending; equal values -> lower expert id first;
