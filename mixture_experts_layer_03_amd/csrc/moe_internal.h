@@ -21,7 +21,7 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> two bf16 (lo in bits 0..15) with gfx950's packed conversion
-// (one v_cvt_pk_bf16_f32): round to nearest, ties to even -- on the box it
+// (one v_cvt_pk_bf16_f32): round to nearest, ties to even -- measured on MI355X it
 // equals the bit arithmetic u + 0x7fff + ((u >> 16) & 1) >> 16 on every
 // non-NaN fp32 pattern, denormals included; a NaN stays a quiet NaN (sign and
 // leading payload bits kept).

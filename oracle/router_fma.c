@@ -10,7 +10,7 @@
  * benchmark proves it", section "Where the gap actually is"; and
  * `fp32_router: true` in the LFM2 recipe of section "The small-hardware end").
  * They do not fix an accumulation order.  Because top-k decisions on near-ties
- * depend on the last bit of a logit, this build fixes the order as part of the
+ * depend on the last bit of a logit, the order is fixed here as part of the
  * definition:
  *
  *   L[t,e] = ((fma-chain over c = 0..d-1 of x[t,c]*w_r[e,c], starting at +0)
