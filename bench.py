@@ -582,6 +582,25 @@ def main():
         copy_out = {"bytes": 2 * cb, "avg_us": round(us, 1), "GB_s": round(gbs, 1),
                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
         del csrc, cdst
+        # and a plain fill (torch's) of the bytes the scatters write (the R
+        # routed rows): they write four bytes per byte read, so the write
+        # rate bounds them, not the balanced copy's
+        fb = 2 * w.R * w.d // 16 * 16
+        fdst = torch.empty(fb // 4, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            fdst.fill_(1.0)
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            fdst.fill_(1.0)
+            e1.record()
+        torch.cuda.synchronize()
+        us = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / len(evs)
+        gbs = fb / (us * 1e-6) / 1e9
+        copy_out["fill_of_written_bytes"] = {"bytes": fb, "avg_us": round(us, 1),
+                                             "GB_s": round(gbs, 1),
+                                             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del fdst
     if gemm_us:
         roof = sum(max(t_mfma[n], t_hbm[n]) for n in gemm_us)
         roof += sum(rb[n] / (PEAK_HBM_GBS * 1e9) for n in rows_out)
