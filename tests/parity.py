@@ -261,20 +261,27 @@ def check_sampled_rows(g, rows, ref_rows, xp, dyp, offsets, w_gu, w_down, wg, wr
 
 
 def check_sampled_wgrad_cols(g_dw_gu_rows, g_dw_down_cols, e, cols, xp_e, dyp_e, w_gu, w_down,
-                             wg_e, wr_e, dg_g, du_g, h_g, tag=""):
+                             wg_e, wr_e, dg_g, du_g, h_g, tag="", tallies=None):
     """Weight gradients of expert e at hidden units `cols`: the oracle forms
     them (and their operands) from only those columns; the bound carries the
     observed deviations of the device's stored dGU columns (dg_g gate, du_g
-    up) and H columns (h_g), all over the expert's rows."""
+    up) and H columns (h_g), all over the expert's rows.  With `tallies`
+    (a Tallies) the comparisons are added to its per-tensor tallies (one
+    record over all the experts checked) instead of being finished here."""
     off = np.array([0, len(xp_e)])
     dg, du, dd, ops = O.weight_grads_sampled_cols(xp_e, off, w_gu[e:e + 1], w_down[e:e + 1],
                                                   wr_e, dyp_e, 0, cols, operands=True)
     X = f64(xp_e)
     dgg, dug, hg = f64(dg_g), f64(du_g), f64(h_g)
     S_g, S_r = f64(s_rows(wg_e, dyp_e)), ops["s"]
-    close(tag + "dw_gu[%d][gate cols]" % e, g_dw_gu_rows[0], dg,
-          bound=TB.b_wgrad(dgg - ops["dg"], dgg, ops["dg"], None, X, dg))
-    close(tag + "dw_gu[%d][up cols]" % e, g_dw_gu_rows[1], du,
-          bound=TB.b_wgrad(dug - ops["du"], dug, ops["du"], None, X, du))
-    close(tag + "dw_down[%d][:, cols]" % e, g_dw_down_cols, dd,
-          bound=TB.b_wgrad(S_g - S_r, S_g, S_r, hg - ops["h"], hg, dd))
+    checks = (("dw_gu[gate cols]", g_dw_gu_rows[0], dg,
+               TB.b_wgrad(dgg - ops["dg"], dgg, ops["dg"], None, X, dg)),
+              ("dw_gu[up cols]", g_dw_gu_rows[1], du,
+               TB.b_wgrad(dug - ops["du"], dug, ops["du"], None, X, du)),
+              ("dw_down[:, cols]", g_dw_down_cols, dd,
+               TB.b_wgrad(S_g - S_r, S_g, S_r, hg - ops["h"], hg, dd)))
+    for name, got, ref, bound in checks:
+        if tallies is None:
+            close(tag + name.replace("[", "[%d][" % e, 1), got, ref, bound=bound)
+        else:
+            tallies[name].add(got, ref, bound)

@@ -54,7 +54,7 @@ def test_ep_rank_share_full_oracle():
     check_share(sh, a, offsets)
 
 
-def _sampled_check(w, seed=0, n_rows=48, n_tok=24, n_cols=3):
+def _sampled_check(w, seed=0, n_rows=48, n_tok=24, n_cols=8, max_experts=32):
     """Bit-exact routing in full; sampled activations and gradients."""
     a = I.make_inputs(w)
     g = run_gpu(w, a)
@@ -119,19 +119,27 @@ def _sampled_check(w, seed=0, n_rows=48, n_tok=24, n_cols=3):
     extra = TB.absdot(ddl, wr_) + (E + k) * TB.U32 * (np.abs(g["d_logits"][toks]) @ np.abs(wr_))
     close("dx[tokens]", g["dx"][toks], dx_ref,
           bound=TB.b_sum_rows(g["dx"][toks], dx_ref, parts, dparts, extra))
-    # weight gradients: sampled hidden units of the largest, the smallest
-    # non-empty and one middle expert (sums over all of the expert's rows)
+    # weight gradients (sums over all of an expert's rows) at n_cols hidden
+    # units per expert, the first and the last (edge tiles) among them: every
+    # non-empty expert, or max_experts of them spread over the expert ids with
+    # the largest and the smallest non-empty ones, in one record per tensor
     ne = np.where(counts > 0)[0]
-    experts = sorted({int(ne[np.argmax(counts[ne])]), int(ne[np.argmin(counts[ne])]),
-                      int(ne[len(ne) // 2])})
-    for e in experts:
-        cols = np.unique(rng.integers(0, f, n_cols))
+    if len(ne) > max_experts:
+        pick = ne[np.linspace(0, len(ne) - 1, max_experts - 2).round().astype(int)]
+        ne = np.unique(np.concatenate([pick, [ne[np.argmax(counts[ne])]],
+                                       [ne[np.argmin(counts[ne])]]]))
+    wt = PC.Tallies()
+    for e in ne:
+        cols = np.unique(np.concatenate([[0, f - 1], rng.integers(0, f, n_cols - 2)]))
         s_, t_ = int(offsets[e]), int(offsets[e + 1])
         PC.check_sampled_wgrad_cols((g["dw_gu"][e][cols], g["dw_gu"][e][f + cols]),
-                                    g["dw_down"][e][:, cols], e, cols, xp[s_:t_], dyp[s_:t_],
-                                    a["w_gu"], a["w_down"], g["w_perm"][s_:t_], wp[s_:t_],
-                                    g["dgu"][s_:t_, cols], g["dgu"][s_:t_, f + cols],
-                                    g["h"][s_:t_, cols])
+                                    g["dw_down"][e][:, cols], int(e), cols, xp[s_:t_],
+                                    dyp[s_:t_], a["w_gu"], a["w_down"], g["w_perm"][s_:t_],
+                                    wp[s_:t_], g["dgu"][s_:t_, cols], g["dgu"][s_:t_, f + cols],
+                                    g["h"][s_:t_, cols], tallies=wt)
+    print("weight gradients checked: %d experts (%d rows), %d hidden units each"
+          % (len(ne), int(counts[ne].sum()), n_cols))
+    wt.finish()
     empty = np.where(counts == 0)[0]
     if len(empty):
         assert np.all(g["dw_gu"][empty] == 0) and np.all(g["dw_down"][empty] == 0)
