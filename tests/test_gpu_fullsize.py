@@ -54,7 +54,7 @@ def test_ep_rank_share_full_oracle():
     check_share(sh, a, offsets)
 
 
-def _sampled_check(w, seed=0, n_rows=48, n_tok=24, n_cols=8, max_experts=32):
+def _sampled_check(w, seed=0, n_rows=192, n_tok=96, n_cols=8, max_experts=32):
     """Bit-exact routing in full; sampled activations and gradients."""
     a = I.make_inputs(w)
     g = run_gpu(w, a)
@@ -156,7 +156,7 @@ def test_gpt_oss_layer_zipf_skew_sampled():
 
 
 def test_qwen3_layer_sampled():
-    _sampled_check(I.QWEN3, seed=5, n_rows=64, n_tok=32)
+    _sampled_check(I.QWEN3, seed=5, n_rows=256, n_tok=128)
 
 
 def test_expert_with_more_than_2_pow_31_gate_up_elements():
