@@ -1242,9 +1242,17 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
 #undef MOE_FETCH
 }
 
+// Threads of the one-block scans over the experts below: a power of two
+// >= E, at least a wave (the scan takes log2 of it barrier rounds).
+static unsigned scan_threads(int E) {
+  unsigned n = 64;
+  while (n < (unsigned)E) n <<= 1;
+  return n;
+}
+
 // For the two token GEMMs of a pass (token-tile heights BQa, BQb; P-tile
 // counts PTa, PTb): ts[e] = sum over e' < e of ceil(M_e' / BQ) * PT, and the
-// 8 tile counters that follow ts[E] cleared (one block).
+// 8 tile counters that follow ts[E] cleared (one block of scan_threads(E)).
 __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict__ offsets, int E,
                                                       int BQa, int PTa, int32_t *__restrict__ tsa,
                                                       int BQb, int PTb, int32_t *__restrict__ tsb) {
@@ -1259,7 +1267,7 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *__restrict_
   s[e] = v;
   sb[e] = vb;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
     const int t = e >= off ? s[e - off] : 0;
     const int tb = e >= off ? sb[e - off] : 0;
     __syncthreads();
@@ -1294,7 +1302,7 @@ __global__ __launch_bounds__(1024) void k_wg_bounds(const int32_t *__restrict__ 
   if (e < E) w = (offsets[e + 1] - offsets[e] + BK - 1) / BK + kWgTileCost;
   s[e] = w;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {   // inclusive prefix of the per-tile costs
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {   // inclusive prefix of the per-tile costs
     const long long t = e >= off ? s[e - off] : 0;
     __syncthreads();
     s[e] += t;
@@ -1736,7 +1744,8 @@ static int persistent_grid(int64_t tiles) {
 static int launch_tile_prefix(const GemmArgs &a, int BQa, int PTa, int32_t *tsa, int BQb, int PTb,
                               int32_t *tsb, hipStream_t s) {
   MOE_LAUNCH("tile_prefix", s,
-             k_tile_prefix<<<1, 1024, 0, s>>>(a.offsets, a.E, BQa, PTa, tsa, BQb, PTb, tsb));
+             k_tile_prefix<<<1, scan_threads(a.E), 0, s>>>(a.offsets, a.E, BQa, PTa, tsa, BQb,
+                                                           PTb, tsb));
   return check_launch("tile_prefix");
 }
 
@@ -2012,7 +2021,7 @@ static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, flo
   const int per_wd = persistent_grid((int64_t)E * pt_wd * qt_wd) / 8;
   const int per_wg = persistent_grid((int64_t)E * pt_wg * qt_wg) / 8;
   MOE_LAUNCH("wg_bounds", s,
-             k_wg_bounds<<<1, 1024, 0, s>>>(a.offsets, E, WG_BK, pt_wd * qt_wd, per_wd, wgb,
+             k_wg_bounds<<<1, scan_threads(E), 0, s>>>(a.offsets, E, WG_BK, pt_wd * qt_wd, per_wd, wgb,
                                             pt_wg * qt_wg, per_wg, wgb + 16));
   rc = check_launch("moe_grouped_ffn_bwd(wg bounds)");
   if (rc) return rc;
