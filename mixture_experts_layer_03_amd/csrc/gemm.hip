@@ -1357,76 +1357,165 @@ __global__ __launch_bounds__(256) void k_drs_reduce(const float *__restrict__ pa
 
 // ------------------------------------------------------------------ fp32 forward
 //
-// fp32 storage (no MFMA bf16 path): one thread per (row, 4 features), fp32
-// fma over k in order.  Used for fp32 workloads only.
-__global__ __launch_bounds__(256) void k_ffn_gu_f32(const float *__restrict__ x_perm,
-                                                    const int32_t *__restrict__ offsets, int E,
-                                                    int64_t R, int d, int f,
-                                                    const float *__restrict__ w_gu,
-                                                    float *__restrict__ gu, float *__restrict__ h) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int nq = f / 4;
-  if (i >= R * nq) return;
-  const int64_t r = i / nq;
-  const int n = (int)(i % nq) * 4;
-  int lo = 0, hi = E;
+// fp32 storage (no bf16 MFMA path): the same two contractions on the vector
+// ALUs.  A block computes 64 expert rows x 64 output columns, 4 x 4 per
+// thread, K staged through LDS 16 wide with coalesced 16-byte loads of the
+// K-contiguous rows of both operands; every output is one fmaf chain over
+// k = 0, 1, ... in order.  Tiles are (expert, column tile, row tile) with the
+// row tiles fastest, from the tile starts of k_tile_prefix (64-row tiles).
+// Used for fp32 workloads only.
+constexpr int F32_BR = 64, F32_BC = 64, F32_BK = 16;
+
+// expert e and its row-tile / column-tile of logical tile L (L < ts[E])
+__device__ __forceinline__ void f32_tile(const int32_t *__restrict__ offsets,
+                                         const int32_t *__restrict__ ts, int E, int L, int &e,
+                                         int &seg0, int &M, int &r0, int &c_tile) {
+  int lo = 0, hi = E;   // largest e with ts[e] <= L
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= r) lo = mid; else hi = mid;
+    if (ts[mid] <= L) lo = mid; else hi = mid;
   }
-  const int e = lo;
-  if (r < offsets[e] || r >= offsets[e + 1]) return;
-  const float *x = x_perm + r * d;
-  const float *wg = w_gu + ((int64_t)e * 2 * f + n) * d;
-  const float *wu = w_gu + ((int64_t)e * 2 * f + f + n) * d;
-  float g[4] = {0, 0, 0, 0}, u[4] = {0, 0, 0, 0};
-  for (int c = 0; c < d; ++c) {
-    const float xv = x[c];
+  e = lo;
+  seg0 = offsets[e];
+  M = offsets[e + 1] - seg0;
+  const int qt = (M + F32_BR - 1) / F32_BR;
+  const int rem = L - ts[e];
+  c_tile = rem / qt;
+  r0 = (rem - c_tile * qt) * F32_BR;
+}
+
+// The 64 x 16 slab of rows [row0, row0 + nrows) of a [*, ld] fp32 matrix at
+// column k0 into s[k][row] (rows past nrows and columns past ld read zeros).
+// Row i of the slab is matrix row rowmap(i).
+template <typename RowMap>
+__device__ __forceinline__ void f32_stage(const float *__restrict__ m, int ld, int k0,
+                                          RowMap rowmap, float (*s)[F32_BR + 4]) {
+  const int t = threadIdx.x, i = t >> 2, kk = (t & 3) * 4;
+  const int64_t row = rowmap(i);
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  if (row >= 0 && k0 + kk < ld) v = *reinterpret_cast<const float4 *>(m + row * ld + k0 + kk);
+  s[kk][i] = v.x;
+  s[kk + 1][i] = v.y;
+  s[kk + 2][i] = v.z;
+  s[kk + 3][i] = v.w;
+}
+
+// GU = [X W_g^T | X W_u^T], H = silu(g) u.  Column tile: 32 hidden units, whose
+// gate and up rows of W_gu are the block's 64 columns.
+__global__ __launch_bounds__(256) void k_ffn_gu_f32(const float *__restrict__ x_perm,
+                                                    const int32_t *__restrict__ offsets,
+                                                    const int32_t *__restrict__ ts, int E, int d,
+                                                    int f, const float *__restrict__ w_gu,
+                                                    float *__restrict__ gu, float *__restrict__ h) {
+  __shared__ float sx[F32_BK][F32_BR + 4], sw[F32_BK][F32_BC + 4];
+  const int L = blockIdx.x;
+  if (L >= ts[E]) return;
+  int e, seg0, M, r0, ct;
+  f32_tile(offsets, ts, E, L, e, seg0, M, r0, ct);
+  const int u0 = ct * (F32_BC / 2);
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const auto xrow = [&](int i) -> int64_t { return r0 + i < M ? (int64_t)seg0 + r0 + i : -1; };
+  const auto wrow = [&](int i) -> int64_t {   // columns 0..31 gate units, 32..63 up units
+    const int u = u0 + (i & 31);
+    return u < f ? (int64_t)e * 2 * f + (i < 32 ? 0 : f) + u : -1;
+  };
+  float acc[4][4];   // rows ty*4 + i; gate units tx*2, tx*2 + 1, then their up units
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      g[v] = fmaf(xv, wg[(int64_t)v * d + c], g[v]);
-      u[v] = fmaf(xv, wu[(int64_t)v * d + c], u[v]);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < d; k0 += F32_BK) {
+    f32_stage(x_perm, d, k0, xrow, sx);
+    f32_stage(w_gu, d, k0, wrow, sw);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < F32_BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sx[kk][ty * 4 + i];
+      b[0] = sw[kk][tx * 2];
+      b[1] = sw[kk][tx * 2 + 1];
+      b[2] = sw[kk][32 + tx * 2];
+      b[3] = sw[kk][32 + tx * 2 + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
+    __syncthreads();
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    if (gu) {
-      gu[r * 2 * f + n + v] = g[v];
-      gu[r * 2 * f + f + n + v] = u[v];
+  for (int i = 0; i < 4; ++i) {
+    const int rr = r0 + ty * 4 + i;
+    if (rr >= M) continue;
+    const int64_t r = (int64_t)seg0 + rr;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int u = u0 + tx * 2 + v;
+      if (u >= f) continue;
+      const float g = acc[i][v], up = acc[i][2 + v];
+      if (gu) {
+        gu[r * 2 * f + u] = g;
+        gu[r * 2 * f + f + u] = up;
+      }
+      h[r * f + u] = g / (1.0f + expf(-g)) * up;
     }
-    h[r * f + n + v] = g[v] / (1.0f + expf(-g[v])) * u[v];
   }
 }
 
+// Y_perm = w * (H W_down^T), 64 rows x 64 of the d output columns per block.
 __global__ __launch_bounds__(256) void k_ffn_down_f32(const float *__restrict__ h,
-                                                      const int32_t *__restrict__ offsets, int E,
-                                                      int64_t R, int d, int f,
-                                                      const float *__restrict__ w_down,
+                                                      const int32_t *__restrict__ offsets,
+                                                      const int32_t *__restrict__ ts, int E, int d,
+                                                      int f, const float *__restrict__ w_down,
                                                       const float *__restrict__ row_scale,
                                                       float *__restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int nq = d / 4;
-  if (i >= R * nq) return;
-  const int64_t r = i / nq;
-  const int n = (int)(i % nq) * 4;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= r) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  if (r < offsets[e] || r >= offsets[e + 1]) return;
-  const float *hr = h + r * f;
-  const float *wd = w_down + ((int64_t)e * d + n) * f;
-  float acc[4] = {0, 0, 0, 0};
-  for (int c = 0; c < f; ++c) {
-    const float hv = hr[c];
+  __shared__ float sx[F32_BK][F32_BR + 4], sw[F32_BK][F32_BC + 4];
+  const int L = blockIdx.x;
+  if (L >= ts[E]) return;
+  int e, seg0, M, r0, ct;
+  f32_tile(offsets, ts, E, L, e, seg0, M, r0, ct);
+  const int n0 = ct * F32_BC;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const auto hrow = [&](int i) -> int64_t { return r0 + i < M ? (int64_t)seg0 + r0 + i : -1; };
+  const auto wrow = [&](int i) -> int64_t {
+    return n0 + i < d ? (int64_t)e * d + n0 + i : -1;
+  };
+  float acc[4][4];   // rows ty*4 + i, columns tx*4 + j
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = fmaf(hv, wd[(int64_t)v * f + c], acc[v]);
-  }
-  const float w = row_scale ? row_scale[r] : 1.0f;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) y[r * d + n + v] = w * acc[v];
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < f; k0 += F32_BK) {
+    f32_stage(h, f, k0, hrow, sx);
+    f32_stage(w_down, f, k0, wrow, sw);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < F32_BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sx[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sw[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = r0 + ty * 4 + i;
+    if (rr >= M) continue;
+    const int64_t r = (int64_t)seg0 + rr;
+    const float w = row_scale ? row_scale[r] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < d) y[r * d + n] = w * acc[i][j];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ grouped LoRA
@@ -1926,16 +2015,26 @@ static int ffn_fwd_run(const void *x_perm, const int32_t *offsets, int E, int64_
                        void *gu, void *h, void *y_perm, void *ws, hipStream_t s) {
   int rc = MOE_OK;
   if (dtype == MOE_F32) {
-    const int64_t n1 = R * (f / 4), n2 = R * (d / 4);
+    int32_t *ts0 = (int32_t *)ws;
+    int32_t *ts1 = (int32_t *)((char *)ws + tile_start_bytes(E));
+    const int ct_gu = (f + F32_BC / 2 - 1) / (F32_BC / 2), ct_dn = (d + F32_BC - 1) / F32_BC;
+    const int64_t row_tiles = (R + F32_BR - 1) / F32_BR + E;   // a bound over the experts
+    MOE_REQUIRE(row_tiles * (ct_gu > ct_dn ? ct_gu : ct_dn) < ((int64_t)1 << 31),
+                MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_fwd: fp32 problem too large");
+    GemmArgs ta{};
+    ta.offsets = offsets;
+    ta.E = E;
+    rc = launch_tile_prefix(ta, F32_BR, ct_gu, ts0, F32_BR, ct_dn, ts1, s);
+    if (rc) return rc;
     MOE_LAUNCH("ffn_gu_f32", s,
-               k_ffn_gu_f32<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
-                   (const float *)x_perm, offsets, E, R, d, f, (const float *)w_gu, (float *)gu,
+               k_ffn_gu_f32<<<(unsigned)(row_tiles * ct_gu), 256, 0, s>>>(
+                   (const float *)x_perm, offsets, ts0, E, d, f, (const float *)w_gu, (float *)gu,
                    (float *)h));
     rc = check_launch("moe_grouped_ffn_fwd(gu f32)");
     if (rc) return rc;
     MOE_LAUNCH("ffn_down_f32", s,
-               k_ffn_down_f32<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
-                   (const float *)h, offsets, E, R, d, f, (const float *)w_down, row_scale,
+               k_ffn_down_f32<<<(unsigned)(row_tiles * ct_dn), 256, 0, s>>>(
+                   (const float *)h, offsets, ts1, E, d, f, (const float *)w_down, row_scale,
                    (float *)y_perm));
     return check_launch("moe_grouped_ffn_fwd(down f32)");
   }

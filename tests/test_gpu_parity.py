@@ -146,6 +146,25 @@ def test_tiny_fp32_forward_matches_oracle():
     check_block(g, o, None, a, w.k, backward=False, bf16=False)
 
 
+# fp32 forward tiles (64 rows x 64 columns, K in 16-wide steps): a K tail of
+# 8 (d = 136), partial column tiles in both GEMMs (f = 72: 32-unit gate/up
+# tiles 32 + 32 + 8; d = 136: 64 + 64 + 8), empty experts (Zipf-skewed), and
+# one expert over many row tiles
+F32_CASES = [
+    _wl(300, 136, 6, 2, 72, dtype="fp32", backward=False, seed=31),
+    _wl(512, 64, 16, 4, 96, dtype="fp32", routing="zipf", backward=False, seed=32),
+    _wl(700, 40, 1, 1, 24, dtype="fp32", backward=False, seed=33),
+]
+
+
+@pytest.mark.parametrize("w", F32_CASES, ids=[w.name for w in F32_CASES])
+def test_fp32_forward_tiles_match_oracle(w):
+    a = I.make_inputs(w)
+    g = run_gpu(w, a, backward=False)
+    o, _ = run_oracle(w, a, backward=False)
+    check_block(g, o, None, a, w.k, backward=False, bf16=False)
+
+
 def test_bitwise_repeatable():
     w = SMALL[1]
     a = I.make_inputs(w)
