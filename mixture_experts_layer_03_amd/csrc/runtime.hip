@@ -59,7 +59,11 @@ TimedLaunch::TimedLaunch(const char *name, hipStream_t s) : name_(name), stream_
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_timing) return;
   hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) return;
+  if (!a || !b) {   // no timing for this launch; keep what was taken
+    if (a) g_pool.push_back(a);
+    if (b) g_pool.push_back(b);
+    return;
+  }
   (void)hipEventRecord(a, s);
   g_records.push_back(Record{std::string(name), a, b});
   slot_ = (int)g_records.size() - 1;
