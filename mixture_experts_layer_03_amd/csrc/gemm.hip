@@ -744,7 +744,7 @@ __device__ __forceinline__ void mfma_block(f32x4_t (&acc)[FP][FQ], const bf16x8_
 // MFMAs of stage n.  After a tile's epilogue, the next tile's first MFMAs are
 // issued before the wait, so the epilogue's stores drain under them.
 template <int KIND, int BP, int BQ, int WP, int WQ, int NS, int BK, bool LORA = false,
-          bool GATHER = false>
+          bool GATHER = false, bool EARLY = false>
 __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   using KT = KindTraits<KIND>;
   constexpr int NW = WP * WQ;
@@ -753,6 +753,15 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   constexpr bool GQ = GATHER && (KIND == FWD_GU || KIND == BWD_DH);
   constexpr bool GP = GATHER && KIND == BWD_DWGU;
   static_assert(!GATHER || ((GQ || GP) && !LORA), "gathered kinds");
+  // EARLY: the next stage's loads are planned (resources and LDS
+  // destinations, all scalar work) before the stage barrier, so that the
+  // planning overlaps the other waves' last MFMAs instead of following the
+  // barrier on every wave.  Only where no plan issues loads at once: the
+  // host takes it for K-tail-free token GEMMs (a K tail's plan loads its
+  // stage directly, as does the LoRA stage); measured on MI355X: down and
+  // dX 4-6% faster, the gathered gate/up and dH GEMMs and the weight-gradient
+  // GEMMs not.
+  constexpr bool EARLY_PLAN = EARLY && !GQ && !GP && !LORA && !KT::WG;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int FP = BP / WP / 16;
   constexpr int FQ = BQ / WQ / 16;
@@ -1050,6 +1059,17 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       }                                                                                       \
     }                                                                                         \
   } while (0)
+// Stage barrier and the plan of the next loads (EARLY_PLAN: the plan first)
+#define MOE_SYNC_PLAN()                                                                       \
+  do {                                                                                        \
+    if constexpr (EARLY_PLAN) {                                                               \
+      MOE_PLAN();                                                                             \
+      MOE_SYNC();                                                                             \
+    } else {                                                                                  \
+      MOE_SYNC();                                                                             \
+      MOE_PLAN();                                                                             \
+    }                                                                                         \
+  } while (0)
 #define MOE_ISSUE_ALL()                                                                       \
   do {                                                                                        \
     MOE_PLAN();                                                                               \
@@ -1161,8 +1181,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
         if (nk > 1) MOE_READ_STEP(s_done + 1, 0);
         ++s_done;
         for (int kt = 1; kt < nk - 1; ++kt) {
-          MOE_SYNC();
-          MOE_PLAN();
+          MOE_SYNC_PLAN();
           MOE_WARM(s_done + 1, 0, true);
           MOE_ADVANCE();
           ++s_done;
@@ -1176,8 +1195,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       } else {
         MOE_READ_STEP(s_done, 1);
         for (int kt = 0; kt < nk - 1; ++kt) {
-          MOE_SYNC();
-          MOE_PLAN();
+          MOE_SYNC_PLAN();
           MOE_WARM(s_done + 1, 0, true);
           MOE_ADVANCE();
           ++s_done;
@@ -1231,6 +1249,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
     }
   }
 #undef MOE_SYNC
+#undef MOE_SYNC_PLAN
 #undef MOE_READ_STEP
 #undef MOE_WARM
 #undef MOE_PLAN
@@ -1848,6 +1867,16 @@ static int launch_token_gemm(GemmArgs a, int64_t R, int PT, int32_t *tile_start,
   a.counters = tile_start + a.E + 1;
   const int64_t bound = ((R + BQ - 1) / BQ + a.E) * (int64_t)PT;
   const int grid = persistent_grid(bound);
+  // the plan-before-barrier instance where no stage has a K tail
+  if constexpr (!LORA && !GATHER) {
+    const int K = (KIND == FWD_DOWN) ? a.f : (KIND == BWD_DX) ? 2 * a.f : a.d;
+    if (K % BK == 0) {
+      MOE_LAUNCH(name, s,
+                 (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK, false, false, true>
+                  <<<grid, WP * WQ * 64, 0, s>>>(a)));
+      return check_launch(name);
+    }
+  }
   MOE_LAUNCH(name, s,
              (k_grouped_gemm<KIND, BP, BQ, WP, WQ, NS, BK, LORA, GATHER>
               <<<grid, WP * WQ * 64, 0, s>>>(a)));
