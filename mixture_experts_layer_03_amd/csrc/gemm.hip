@@ -1180,7 +1180,22 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
         if (ivalid) MOE_ISSUE_ALL();
         if (nk > 1) MOE_READ_STEP(s_done + 1, 0);
         ++s_done;
-        for (int kt = 1; kt < nk - 1; ++kt) {
+        // two stages per pass, so that the Q fragments read during a stage's
+        // MFMAs alternate between two register sets; with one stage per pass
+        // the compiler copies them back, waiting for the reads, before each
+        // stage's first MFMA
+        int kt = 1;
+        for (; kt + 1 < nk - 1; kt += 2) {
+          MOE_SYNC_PLAN();
+          MOE_WARM(s_done + 1, 0, true);
+          MOE_ADVANCE();
+          ++s_done;
+          MOE_SYNC_PLAN();
+          MOE_WARM(s_done + 1, 0, true);
+          MOE_ADVANCE();
+          ++s_done;
+        }
+        if (kt < nk - 1) {
           MOE_SYNC_PLAN();
           MOE_WARM(s_done + 1, 0, true);
           MOE_ADVANCE();
