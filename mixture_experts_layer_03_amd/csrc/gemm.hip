@@ -531,7 +531,6 @@ __device__ __forceinline__ float swiglu_h(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-constexpr int kDhBatch = 4;   // dSwiGLU epilogue: fragments per batch of saved-activation loads
 //
 // Lane holds D[prow[i] + 4*(lane/16) + v][qrow[j] + lane%16].
 template <int KIND, int FP, int FQ, int WP>
@@ -594,7 +593,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
       }
     }
   } else if (KIND == BWD_DH) {
+    // Fragments 2m and 2m+1 (16 columns apart) trade 16-lane rows
+    // (v_permlane16_swap): lane group g then holds 8 consecutive columns,
+    // from c0 + 8*sig(g) with sig = (0, 2, 1, 3), so the saved g, u are read
+    // and dGU written 16 bytes per lane -- 16 rows x 64 B per access, half
+    // the accesses of 4-column pieces (measured on MI355X: the epilogue's
+    // loads and stores at 8 bytes per lane each cost dH 13-17%).
+    static_assert(FP % 2 == 0, "fragment pairs");
+    constexpr int NPR = FP / 2;
     const int nparts = a.PT * WP;
+    const int grp = lane >> 4;
+    const int sig = ((grp & 1) << 1) | (grp >> 1);
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       // token row (rows past the expert's end read row seg0 and store
@@ -603,47 +612,52 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
       const bool rowok = q < Me;
       const int64_t r = (int64_t)seg0 + (rowok ? q : 0);
       const float w = a.row_scale ? a.row_scale[r] : 1.0f;
-      // the saved g, u of kDhBatch fragments' columns at a time (one wait
-      // each; H is recomputed from them, bit for bit as stored); columns
-      // past f read column 0 and store nothing
+      // the saved g, u of the wave's columns of this row, all loads out
+      // before the arithmetic (H is recomputed from them, bit for bit as
+      // stored); columns past f read column 0 and store nothing
+      u32x4_t g8[NPR], u8[NPR];
+#pragma unroll
+      for (int m = 0; m < NPR; ++m) {
+        const int c = p0 + prow[2 * m] + 8 * sig;
+        const int cc = c < f ? c : 0;
+        g8[m] = *reinterpret_cast<const u32x4_t *>(a.gu + r * f2 + cc);
+        u8[m] = *reinterpret_cast<const u32x4_t *>(a.gu + r * f2 + f + cc);
+      }
       float part = 0.0f;
 #pragma unroll
-      for (int hh = 0; hh < FP / kDhBatch; ++hh) {
-        constexpr int FH = kDhBatch;
-        u32x2_t g2[FH], u2[FH];
+      for (int m = 0; m < NPR; ++m) {
+        const int c = p0 + prow[2 * m] + 8 * sig;
+        const bool ok = rowok && c < f;
+        float gd[8];
 #pragma unroll
-        for (int ii = 0; ii < FH; ++ii) {
-          const int c = p0 + prow[hh * FH + ii] + er;
-          const int cc = c < f ? c : 0;
-          g2[ii] = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + cc);
-          u2[ii] = *reinterpret_cast<const u32x2_t *>(a.gu + r * f2 + f + cc);
+        for (int v = 0; v < 4; ++v) {
+          const float lo = acc[2 * m][j][v], hi = acc[2 * m + 1][j][v];
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi),
+                                                           false, false);
+          gd[v] = __uint_as_float(sw[0]);
+          gd[4 + v] = __uint_as_float(sw[1]);
         }
+        float dg[8], du[8];
 #pragma unroll
-        for (int ii = 0; ii < FH; ++ii) {
-          const int i = hh * FH + ii;
-          const int c = p0 + prow[i] + er;
-          const bool ok = rowok && c < f;
-          float dg[4], du[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t gw = g2[ii][v >> 1], uw = u2[ii][v >> 1];
-            const float g = bf16_bits_to_f32((v & 1) ? (gw >> 16) : (gw & 0xffffu));
-            const float u = bf16_bits_to_f32((v & 1) ? (uw >> 16) : (uw & 0xffffu));
-            const float hv = round_bf16(swiglu_h(g, u));
-            const float sg = 1.0f / (1.0f + __expf(-g));
-            const float silu = g * sg;
-            const float gd = acc[i][j][v];
-            part += ok ? hv * gd : 0.0f;
-            const float dh = w * gd;
-            dg[v] = dh * u * sg * (1.0f + g * (1.0f - sg));
-            du[v] = dh * silu;
-          }
-          if (ok) {
-            *reinterpret_cast<u32x2_t *>(a.o_dgu + r * f2 + c) =
-                u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-            *reinterpret_cast<u32x2_t *>(a.o_dgu + r * f2 + f + c) =
-                u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-          }
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t gw = g8[m][t >> 1], uw = u8[m][t >> 1];
+          const float g = bf16_bits_to_f32((t & 1) ? (gw >> 16) : (gw & 0xffffu));
+          const float u = bf16_bits_to_f32((t & 1) ? (uw >> 16) : (uw & 0xffffu));
+          const float hv = round_bf16(swiglu_h(g, u));
+          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float silu = g * sg;
+          part += ok ? hv * gd[t] : 0.0f;
+          const float dh = w * gd[t];
+          dg[t] = dh * u * sg * (1.0f + g * (1.0f - sg));
+          du[t] = dh * silu;
+        }
+        if (ok) {
+          *reinterpret_cast<u32x4_t *>(a.o_dgu + r * f2 + c) =
+              u32x4_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
+                      pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
+          *reinterpret_cast<u32x4_t *>(a.o_dgu + r * f2 + f + c) =
+              u32x4_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                      pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
         }
       }
       // sum over the 4 lane groups that share this token (fixed order)
