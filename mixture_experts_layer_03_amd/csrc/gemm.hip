@@ -523,6 +523,20 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs &a, const int *s_off, c
 
 // ------------------------------------------------------------------ epilogues
 
+// Exchange between the 16-lane rows 2k and 2k+1 of a wave (lanes l and
+// l ^ 16), x0 and x1 being a lane's words of two fragments: a lane of an
+// even row keeps its x0 and takes its partner's x0, a lane of an odd row
+// takes its partner's x1 and keeps its x1.  Per 16-lane row r (x[r] the
+// words of row r): out0 = (x0[0], x1[0], x0[2], x1[2]), out1 = (x0[1], x1[1],
+// x0[3], x1[3]): gfx950's v_permlane16_swap, one instruction per word pair.
+__device__ __forceinline__ void pair_rows(uint32_t x0, uint32_t x1, uint32_t &out0,
+                                          uint32_t &out1) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+  out0 = sw[0];
+  out1 = sw[1];
+}
+
+
 // h = silu(g) u from the stored (bf16) g and u, in fp32, before its own bf16
 // store.  The forward's SwiGLU epilogue and the backward's dSwiGLU epilogue
 // both form it with this one expression, so the backward recomputes the
@@ -534,7 +548,7 @@ __device__ __forceinline__ float swiglu_h(float g, float u) {
 //
 // Lane holds D[prow[i] + 4*(lane/16) + v][qrow[j] + lane%16].
 template <int KIND, int FP, int FQ, int WP>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const f32x4_t (&acc)[FP][FQ],
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, f32x4_t (&acc)[FP][FQ],
                                          const int (&prow)[FP], const int (&qrow)[FQ], int lane,
                                          int wp) {
   const int d = a.d, f = a.f;
@@ -542,7 +556,61 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
   const int er = 4 * (lane >> 4);
   const int ec = lane & 15;
   const int seg0 = t.seg0, Me = t.Me, p0 = t.p0, q0 = t.q0;
-  if (KIND == FWD_GU) {
+  // Lane (g, c) of a fragment holds 4 consecutive P columns (4g..4g+3) of
+  // token row c.  In the tiles of 64 x 64 waves (the gathered gate/up and the
+  // dH GEMMs), fragments 16 columns apart trade 16-lane rows (pair_rows):
+  // lane group g then holds 8 consecutive columns of its row, from 8*sig(g)
+  // in the pair's 32 with sig = (0, 2, 1, 3), and a 16-byte access covers 16
+  // rows x 64 B instead of 16 rows x 32 B.  (Measured on MI355X: the 4-column
+  // stores cost the gate/up GEMM 11-21% of its time, the down and dX GEMMs
+  // 6-33%.  In the 128 x 64 waves of those 256 x 256 tiles the exchange
+  // pushes the kernels past 256 registers -- 270-340 bytes of spills -- so
+  // they keep the 4-column stores.)
+  const int grp = lane >> 4;
+  const int sig = ((grp & 1) << 1) | (grp >> 1);
+  if (KIND == FWD_GU && FP == 4) {
+    // gate units are fragments 0, 1, their up features 2, 3
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int q = q0 + qrow[j] + ec;
+      const int64_t r = (int64_t)seg0 + q;
+#pragma unroll
+      for (int i = 0; i < FP / 2; i += 2) {   // one pair
+        float g[8], u[8], hv[8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float g0 = acc[i][j][v], g1 = acc[i + 1][j][v];
+          const float u0 = acc[i + FP / 2][j][v], u1 = acc[i + 1 + FP / 2][j][v];
+          uint32_t ga, gb, ua, ub;
+          pair_rows(__float_as_uint(g0), __float_as_uint(g1), ga, gb);
+          pair_rows(__float_as_uint(u0), __float_as_uint(u1), ua, ub);
+          g[v] = __uint_as_float(ga);
+          g[4 + v] = __uint_as_float(gb);
+          u[v] = __uint_as_float(ua);
+          u[4 + v] = __uint_as_float(ub);
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          g[v] = round_bf16(g[v]);
+          u[v] = round_bf16(u[v]);
+          hv[v] = swiglu_h(g[v], u[v]);
+        }
+        const int n = p0 + prow[i] + 8 * sig;   // gate feature; up feature = f + n
+        if (q >= Me || n >= f) continue;
+        if (a.o_gu) {
+          *reinterpret_cast<u32x4_t *>(a.o_gu + r * f2 + n) =
+              u32x4_t{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                      pack_bf16x2(g[6], g[7])};
+          *reinterpret_cast<u32x4_t *>(a.o_gu + r * f2 + f + n) =
+              u32x4_t{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]),
+                      pack_bf16x2(u[6], u[7])};
+        }
+        *reinterpret_cast<u32x4_t *>(a.o_h + r * f + n) =
+            u32x4_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]),
+                    pack_bf16x2(hv[4], hv[5]), pack_bf16x2(hv[6], hv[7])};
+      }
+    }
+  } else if (KIND == FWD_GU) {
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       const int q = q0 + qrow[j] + ec;
@@ -594,7 +662,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
     }
   } else if (KIND == BWD_DH) {
     // Fragments 2m and 2m+1 (16 columns apart) trade 16-lane rows
-    // (v_permlane16_swap): lane group g then holds 8 consecutive columns,
+    // (pair_rows): lane group g then holds 8 consecutive columns,
     // from c0 + 8*sig(g) with sig = (0, 2, 1, 3), so the saved g, u are read
     // and dGU written 16 bytes per lane -- 16 rows x 64 B per access, half
     // the accesses of 4-column pieces (measured on MI355X: the epilogue's
@@ -602,8 +670,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
     static_assert(FP % 2 == 0, "fragment pairs");
     constexpr int NPR = FP / 2;
     const int nparts = a.PT * WP;
-    const int grp = lane >> 4;
-    const int sig = ((grp & 1) << 1) | (grp >> 1);
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       // token row (rows past the expert's end read row seg0 and store
@@ -631,11 +697,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, const
         float gd[8];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float lo = acc[2 * m][j][v], hi = acc[2 * m + 1][j][v];
-          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi),
-                                                           false, false);
-          gd[v] = __uint_as_float(sw[0]);
-          gd[4 + v] = __uint_as_float(sw[1]);
+          uint32_t xa, xb;
+          pair_rows(__float_as_uint(acc[2 * m][j][v]), __float_as_uint(acc[2 * m + 1][j][v]), xa,
+                    xb);
+          gd[v] = __uint_as_float(xa);
+          gd[4 + v] = __uint_as_float(xb);
         }
         float dg[8], du[8];
 #pragma unroll
