@@ -547,10 +547,16 @@ __device__ __forceinline__ float swiglu_h(float g, float u) {
 
 //
 // Lane holds D[prow[i] + 4*(lane/16) + v][qrow[j] + lane%16].
+// Per-wave LDS slot of the down and dX epilogues (128 x 64 waves): 16 token
+// rows x 64 bf16 columns, rows padded to 144 bytes.
+constexpr int kEpiPitch = 144, kEpiSlot = 16 * kEpiPitch;
+template <int KIND, int FP>
+constexpr bool epi_via_lds() { return (KIND == FWD_DOWN || KIND == BWD_DX) && FP == 8; }
+
 template <int KIND, int FP, int FQ, int WP>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, f32x4_t (&acc)[FP][FQ],
                                          const int (&prow)[FP], const int (&qrow)[FQ], int lane,
-                                         int wp) {
+                                         int wp, LDS_AS char *epi) {
   const int d = a.d, f = a.f;
   const int64_t f2 = 2 * (int64_t)f;
   const int er = 4 * (lane >> 4);
@@ -645,19 +651,56 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, f32x4
       const int q = q0 + qrow[j] + ec;
       wj[j] = (KIND == FWD_DOWN && a.row_scale) ? a.row_scale[(int64_t)seg0 + (q < Me ? q : 0)] : 1.0f;
     }
+    if constexpr (epi_via_lds<KIND, FP>()) {
+      // 16 rows x 64 columns at a time through the wave's own LDS slot:
+      // 4-column pieces in (lane (g, c): row c), 16-byte row chunks out (lane
+      // l: chunk l%8 of rows l/8 and 8 + l/8), so that each store covers 8
+      // token rows x 128 contiguous bytes.  (Measured on MI355X: stores of
+      // 16 rows x 32 B cost these GEMMs 6-33% of their time; a register
+      // exchange between lanes instead overflows their 256 registers.)
+      const int rr = lane >> 3, ch = lane & 7;
 #pragma unroll
-    for (int j = 0; j < FQ; ++j) {
-      const int q = q0 + qrow[j] + ec;
-      if (q >= Me) continue;
-      const int64_t r = (int64_t)seg0 + q;
-      const float w = wj[j];
+      for (int j = 0; j < FQ; ++j) {
+        const float w = wj[j];
+        const int qa = q0 + qrow[j] + rr;
 #pragma unroll
-      for (int i = 0; i < FP; ++i) {
-        const int n = p0 + prow[i] + er;
-        if (n >= d) continue;
-        *reinterpret_cast<u32x2_t *>(out + r * d + n) =
-            u32x2_t{pack_bf16x2(w * acc[i][j][0], w * acc[i][j][1]),
-                    pack_bf16x2(w * acc[i][j][2], w * acc[i][j][3])};
+        for (int h = 0; h < FP / 4; ++h) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * h + ii;
+            *reinterpret_cast<LDS_AS u32x2_t *>(epi + ec * kEpiPitch + (16 * ii + er) * 2) =
+                u32x2_t{pack_bf16x2(w * acc[i][j][0], w * acc[i][j][1]),
+                        pack_bf16x2(w * acc[i][j][2], w * acc[i][j][3])};
+          }
+          wait_vm_lgkm0<63>();               // the wave's writes have landed
+          __builtin_amdgcn_wave_barrier();   // (and the reads stay behind them)
+          const u32x4_t A = *reinterpret_cast<const LDS_AS u32x4_t *>(epi + rr * kEpiPitch + ch * 16);
+          const u32x4_t B =
+              *reinterpret_cast<const LDS_AS u32x4_t *>(epi + (rr + 8) * kEpiPitch + ch * 16);
+          __builtin_amdgcn_wave_barrier();   // the next writes stay behind these reads
+          const int n = p0 + prow[4 * h] + ch * 8;
+          if (n < d) {
+            if (qa < Me) *reinterpret_cast<u32x4_t *>(out + ((int64_t)seg0 + qa) * d + n) = A;
+            if (qa + 8 < Me)
+              *reinterpret_cast<u32x4_t *>(out + ((int64_t)seg0 + qa + 8) * d + n) = B;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) {
+        const int q = q0 + qrow[j] + ec;
+        if (q >= Me) continue;
+        const int64_t r = (int64_t)seg0 + q;
+        const float w = wj[j];
+#pragma unroll
+        for (int i = 0; i < FP; ++i) {
+          const int n = p0 + prow[i] + er;
+          if (n >= d) continue;
+          *reinterpret_cast<u32x2_t *>(out + r * d + n) =
+              u32x2_t{pack_bf16x2(w * acc[i][j][0], w * acc[i][j][1]),
+                      pack_bf16x2(w * acc[i][j][2], w * acc[i][j][3])};
+        }
       }
     }
   } else if (KIND == BWD_DH) {
@@ -870,12 +913,15 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   // GP: per wave, a ring of 8 entries of 64 top-k slot indices (the wave's
   // k-rows of one stage in the first KRW)
   __shared__ int s_gidx[GP ? NW * 8 * 64 : 1];
+  // the epilogue's per-wave slots (down and dX GEMMs of 128 x 64 waves)
+  __shared__ u32x4_t sepi[epi_via_lds<KIND, FP>() ? NW * kEpiSlot / 16 : 1];
   const LDS_AS char *lds = (const LDS_AS char *)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave % WP, wq = wave / WP;
+  LDS_AS char *const epi = (LDS_AS char *)sepi + (epi_via_lds<KIND, FP>() ? wave * kEpiSlot : 0);
 
   const int per = gridDim.x >> 3;                  // blocks per XCD
   // Token GEMMs: tiles differ in cost (an expert's last token tile is
@@ -1177,7 +1223,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
   Tile ct{};
   if (cvalid) ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
   while (cvalid && ct.nk == 0) {   // experts with no rows: zero weight gradients
-    epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
+    epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp, epi);
     cL += per;
     cvalid = cL < cend;
     if (cvalid) ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
@@ -1318,7 +1364,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
       }
     }
     // The last barrier published stage s_done: the next tile's first stage.
-    epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
+    epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp, epi);
 #pragma unroll
     for (int i = 0; i < FP; ++i)
 #pragma unroll
@@ -1329,7 +1375,7 @@ __global__ __launch_bounds__(WP *WQ * 64) void k_grouped_gemm(GemmArgs a) {
         cvalid = cL < cend;
         if (cvalid) {
           ct = make_tile<KIND, BP, BQ, BK, LORA>(a, s_off, s_ts, cL);
-          if (ct.nk == 0) epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp);
+          if (ct.nk == 0) epilogue<KIND, FP, FQ, WP>(a, ct, acc, prow, qrow, lane, wp, epi);
         }
       } while (cvalid && ct.nk == 0);
     } else {
