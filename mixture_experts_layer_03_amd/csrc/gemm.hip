@@ -704,63 +704,76 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, f32x4
       }
     }
   } else if (KIND == BWD_DH) {
-    // Fragments 2m and 2m+1 (16 columns apart) trade 16-lane rows
-    // (pair_rows): lane group g then holds 8 consecutive columns,
-    // from c0 + 8*sig(g) with sig = (0, 2, 1, 3), so the saved g, u are read
-    // and dGU written 16 bytes per lane -- 16 rows x 64 B per access, half
-    // the accesses of 4-column pieces (measured on MI355X: the epilogue's
-    // loads and stores at 8 bytes per lane each cost dH 13-17%).
-    static_assert(FP % 2 == 0, "fragment pairs");
-    constexpr int NPR = FP / 2;
+    // The wave's 64 columns at once: fragments 0,1 and 2,3 trade 16-lane
+    // rows (pair_rows: lane group g then holds 8 consecutive columns of its
+    // row, from 8*sig(g) in each pair's 32), then the pairs trade places
+    // between lanes c and c+8 of each 16-lane row (DPP row_ror:8): lane (g, c)
+    // works on token rows c%8 ("A") and 8 + c%8 ("B") at columns
+    // 32*(c >= 8) + 8*sig(g) .. +7, so the saved g, u are read and dGU
+    // written 16 bytes per lane, each access 8 rows x 128 B (measured on
+    // MI355X: the epilogue's loads and stores at 8 bytes per lane cost dH
+    // 13-17% each).
+    static_assert(KIND != BWD_DH || FP == 4, "the 64 columns of four fragments");
     const int nparts = a.PT * WP;
+    const bool lo = ec < 8;
+    const int c = p0 + prow[0] + (lo ? 0 : 32) + 8 * sig;
+    const bool colok = c < f;
+    const int cc = colok ? c : 0;   // columns past f read column 0, store nothing
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
-      // token row (rows past the expert's end read row seg0 and store
-      // nothing) and its combine weight
-      const int q = q0 + qrow[j] + ec;
-      const bool rowok = q < Me;
-      const int64_t r = (int64_t)seg0 + (rowok ? q : 0);
-      const float w = a.row_scale ? a.row_scale[r] : 1.0f;
-      // the saved g, u of the wave's columns of this row, all loads out
-      // before the arithmetic (H is recomputed from them, bit for bit as
-      // stored); columns past f read column 0 and store nothing
-      u32x4_t g8[NPR], u8[NPR];
+      // rows A and B of this lane (rows past the expert's end read row seg0
+      // and store nothing) and their combine weights
+      const int qa = q0 + qrow[j] + (ec & 7), qb = qa + 8;
+      const bool oka = qa < Me, okb = qb < Me;
+      const int64_t ra = (int64_t)seg0 + (oka ? qa : 0), rb = (int64_t)seg0 + (okb ? qb : 0);
+      const float wa = a.row_scale ? a.row_scale[ra] : 1.0f;
+      const float wb = a.row_scale ? a.row_scale[rb] : 1.0f;
+      // the saved g, u (H is recomputed from them, bit for bit as stored)
+      const u32x4_t ga = *reinterpret_cast<const u32x4_t *>(a.gu + ra * f2 + cc);
+      const u32x4_t ua = *reinterpret_cast<const u32x4_t *>(a.gu + ra * f2 + f + cc);
+      const u32x4_t gb = *reinterpret_cast<const u32x4_t *>(a.gu + rb * f2 + cc);
+      const u32x4_t ub = *reinterpret_cast<const u32x4_t *>(a.gu + rb * f2 + f + cc);
+      // Gd in the same layout
+      float gda[8], gdb[8];
 #pragma unroll
-      for (int m = 0; m < NPR; ++m) {
-        const int c = p0 + prow[2 * m] + 8 * sig;
-        const int cc = c < f ? c : 0;
-        g8[m] = *reinterpret_cast<const u32x4_t *>(a.gu + r * f2 + cc);
-        u8[m] = *reinterpret_cast<const u32x4_t *>(a.gu + r * f2 + f + cc);
+      for (int v = 0; v < 4; ++v) {
+        uint32_t p00, p01, p10, p11;   // pair 0 (columns 0..31), pair 1 (32..63); row c
+        pair_rows(__float_as_uint(acc[0][j][v]), __float_as_uint(acc[1][j][v]), p00, p01);
+        pair_rows(__float_as_uint(acc[2][j][v]), __float_as_uint(acc[3][j][v]), p10, p11);
+        // row_ror:8 (DPP control 0x128): lane c of each 16-lane row takes
+        // lane (c + 8) % 16
+        const uint32_t s00 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p00, 0x128, 0xf, 0xf, false);
+        const uint32_t s01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0x128, 0xf, 0xf, false);
+        const uint32_t s10 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p10, 0x128, 0xf, 0xf, false);
+        const uint32_t s11 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p11, 0x128, 0xf, 0xf, false);
+        gda[v] = __uint_as_float(lo ? p00 : s10);
+        gda[4 + v] = __uint_as_float(lo ? p01 : s11);
+        gdb[v] = __uint_as_float(lo ? s00 : p10);
+        gdb[4 + v] = __uint_as_float(lo ? s01 : p11);
       }
-      float part = 0.0f;
+      float parta = 0.0f, partb = 0.0f;
 #pragma unroll
-      for (int m = 0; m < NPR; ++m) {
-        const int c = p0 + prow[2 * m] + 8 * sig;
-        const bool ok = rowok && c < f;
-        float gd[8];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          uint32_t xa, xb;
-          pair_rows(__float_as_uint(acc[2 * m][j][v]), __float_as_uint(acc[2 * m + 1][j][v]), xa,
-                    xb);
-          gd[v] = __uint_as_float(xa);
-          gd[4 + v] = __uint_as_float(xb);
-        }
-        float dg[8], du[8];
+      for (int half = 0; half < 2; ++half) {   // rows A, then B
+        const u32x4_t gw8 = half ? gb : ga, uw8 = half ? ub : ua;
+        const float w = half ? wb : wa;
+        const bool ok = (half ? okb : oka) && colok;
+        float dg[8], du[8], part = 0.0f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const uint32_t gw = g8[m][t >> 1], uw = u8[m][t >> 1];
+          const uint32_t gw = gw8[t >> 1], uw = uw8[t >> 1];
           const float g = bf16_bits_to_f32((t & 1) ? (gw >> 16) : (gw & 0xffffu));
           const float u = bf16_bits_to_f32((t & 1) ? (uw >> 16) : (uw & 0xffffu));
+          const float gd = half ? gdb[t] : gda[t];
           const float hv = round_bf16(swiglu_h(g, u));
           const float sg = 1.0f / (1.0f + __expf(-g));
           const float silu = g * sg;
-          part += ok ? hv * gd[t] : 0.0f;
-          const float dh = w * gd[t];
+          part += ok ? hv * gd : 0.0f;
+          const float dh = w * gd;
           dg[t] = dh * u * sg * (1.0f + g * (1.0f - sg));
           du[t] = dh * silu;
         }
         if (ok) {
+          const int64_t r = half ? rb : ra;
           *reinterpret_cast<u32x4_t *>(a.o_dgu + r * f2 + c) =
               u32x4_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
                       pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
@@ -768,12 +781,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t, f32x4
               u32x4_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
                       pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
         }
+        if (half) partb = part; else parta = part;
       }
-      // sum over the 4 lane groups that share this token (fixed order)
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      if (a.o_drs && rowok && lane < 16)
-        a.o_drs[r * nparts + t.p_tile * WP + wp] = part;
+      // sum over the 8 lanes that share a row (fixed order: the two column
+      // halves, then the 4 lane groups)
+      parta += __shfl_xor(parta, 8, 64);
+      partb += __shfl_xor(partb, 8, 64);
+      parta += __shfl_xor(parta, 16, 64);
+      partb += __shfl_xor(partb, 16, 64);
+      parta += __shfl_xor(parta, 32, 64);
+      partb += __shfl_xor(partb, 32, 64);
+      if (a.o_drs && lane < 8) {
+        if (oka) a.o_drs[ra * nparts + t.p_tile * WP + wp] = parta;
+        if (okb) a.o_drs[rb * nparts + t.p_tile * WP + wp] = partb;
+      }
     }
   } else {   // weight gradients: dw[e][q][p]
     const int Pdim = (KIND == BWD_DWDOWN) ? f : d;
