@@ -1943,53 +1943,6 @@ __global__ __launch_bounds__(256) void k_row_scale(const bf16_t *__restrict__ dy
   }
 }
 
-// The same from the unpermuted dY in token order: each token row is read
-// once and its k scaled copies written, S[slot_to_row[t*k+j]] =
-// store(w[that row] * dY[t]).  One wave per (token, piece of 192 16-byte
-// chunks), three chunks per lane (two pieces per 2880-wide bf16 row).
-constexpr int kRsNch = 3, kRsPiece = 64 * kRsNch;
-__global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restrict__ dy,
-                                                           const int32_t *__restrict__ slot_to_row,
-                                                           const float *__restrict__ w,
-                                                           int64_t ntok, int d, int k,
-                                                           bf16_t *__restrict__ s) {
-  const int nvec = d / 8;
-  const int pieces = (nvec + kRsPiece - 1) / kRsPiece;
-  const int64_t wid =
-      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t t = wid / pieces;
-  if (t >= ntok) return;
-  const int lane = threadIdx.x & 63;
-  // equal pieces of whole 64-chunk columns (256 chunks: 128 + 128)
-  const int pw = ((nvec + pieces - 1) / pieces + 63) / 64 * 64;
-  const int c0 = (int)(wid - t * pieces) * pw + lane;   // chunk h: c0 + 64 h
-  const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
-  const float myw = (myr >= 0 && w) ? w[myr] : 1.0f;
-  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(dy + t * d);
-  u32x4_t x[kRsNch];
-  bool ok[kRsNch];
-#pragma unroll
-  for (int h = 0; h < kRsNch; ++h) {
-    ok[h] = 64 * h < pw && c0 + 64 * h < nvec;
-    x[h] = u32x4_t{0u, 0u, 0u, 0u};
-    if (ok[h]) x[h] = src[c0 + 64 * h];
-  }
-  for (int j = 0; j < k; ++j) {
-    const int r = __builtin_amdgcn_readlane(myr, j);
-    if (r < 0) continue;
-    const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), j));
-    u32x4_t *o = reinterpret_cast<u32x4_t *>(s + (int64_t)r * d);
-#pragma unroll
-    for (int h = 0; h < kRsNch; ++h) {
-      u32x4_t y;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        y[q] = pack_bf16x2(bf16_bits_to_f32(x[h][q] & 0xffffu) * wr, bf16_bits_to_f32(x[h][q] >> 16) * wr);
-      if (ok[h]) o[c0 + 64 * h] = y;
-    }
-  }
-}
-
 static inline int pad8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
 // Persistent grid: one block per CU of the current device (a multiple of 8),
@@ -2293,11 +2246,8 @@ static int ffn_bwd_bf16(GemmArgs a, int64_t R, float *dw_gu, float *dw_down, flo
   if (R > 0) {
     const unsigned blocks = (unsigned)((R + 3) / 4);
     if (gather) {
-      const int64_t T = R / k;
-      const int64_t waves = T * ((d / 8 + kRsPiece - 1) / kRsPiece);
-      MOE_LAUNCH("row_scale", s,
-                 k_row_scale_scatter<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(
-                     gdy, slot_to_row, a.row_scale, T, d, k, s_perm));
+      rc = launch_row_scale_scatter(gdy, slot_to_row, a.row_scale, R / k, d, k, s_perm, s);
+      if (rc) return rc;
     } else
       MOE_LAUNCH("row_scale", s,
                  k_row_scale<<<blocks, 256, 0, s>>>(a.dy_perm, a.row_scale, R, d, s_perm));

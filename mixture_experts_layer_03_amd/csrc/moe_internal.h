@@ -63,6 +63,12 @@ struct TimedLaunch {
 // Check the last launch; returns MOE_OK or MOE_ERR_HIP with a message.
 int check_launch(const char *what);
 
+// S[slot_to_row[t*k+j]] = store(w[that row] * dY[t]) for T tokens (w NULL:
+// a copy), the weight-gradient operand of the gathered backward; launched on
+// stream s, named "row_scale" for timing (csrc/permute.hip).
+int launch_row_scale_scatter(const bf16_t *dy, const int32_t *slot_to_row, const float *w,
+                             int64_t T, int d, int k, bf16_t *s_rows, hipStream_t s);
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 #define MOE_REQUIRE(cond, code, ...)   \

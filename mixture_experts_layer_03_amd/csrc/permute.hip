@@ -278,6 +278,53 @@ static unsigned row_blocks(int64_t ntok, int d, bool rows = true, int piece = kR
   return (unsigned)((ntok * pieces + 3) / 4);
 }
 
+// The same from the unpermuted dY in token order: each token row is read
+// once and its k scaled copies written, S[slot_to_row[t*k+j]] =
+// store(w[that row] * dY[t]).  One wave per (token, piece of 192 16-byte
+// chunks), three chunks per lane (two pieces per 2880-wide bf16 row).
+constexpr int kRsNch = 3, kRsPiece = 64 * kRsNch;
+__global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restrict__ dy,
+                                                           const int32_t *__restrict__ slot_to_row,
+                                                           const float *__restrict__ w,
+                                                           int64_t ntok, int d, int k,
+                                                           bf16_t *__restrict__ s) {
+  const int nvec = d / 8;
+  const int pieces = (nvec + kRsPiece - 1) / kRsPiece;
+  const int64_t wid =
+      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t t = wid / pieces;
+  if (t >= ntok) return;
+  const int lane = threadIdx.x & 63;
+  // equal pieces of whole 64-chunk columns (256 chunks: 128 + 128)
+  const int pw = ((nvec + pieces - 1) / pieces + 63) / 64 * 64;
+  const int c0 = (int)(wid - t * pieces) * pw + lane;   // chunk h: c0 + 64 h
+  const int myr = lane < k ? slot_to_row[t * k + lane] : -1;   // k <= 32
+  const float myw = (myr >= 0 && w) ? w[myr] : 1.0f;
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(dy + t * d);
+  u32x4_t x[kRsNch];
+  bool ok[kRsNch];
+#pragma unroll
+  for (int h = 0; h < kRsNch; ++h) {
+    ok[h] = 64 * h < pw && c0 + 64 * h < nvec;
+    x[h] = u32x4_t{0u, 0u, 0u, 0u};
+    if (ok[h]) x[h] = src[c0 + 64 * h];
+  }
+  for (int j = 0; j < k; ++j) {
+    const int r = __builtin_amdgcn_readlane(myr, j);
+    if (r < 0) continue;
+    const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), j));
+    u32x4_t *o = reinterpret_cast<u32x4_t *>(s + (int64_t)r * d);
+#pragma unroll
+    for (int h = 0; h < kRsNch; ++h) {
+      u32x4_t y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        y[q] = pack_bf16x2(bf16_bits_to_f32(x[h][q] & 0xffffu) * wr, bf16_bits_to_f32(x[h][q] >> 16) * wr);
+      if (ok[h]) o[c0 + 64 * h] = y;
+    }
+  }
+}
+
 // ---- persistent, software-pipelined row kernels (top-k <= 8)
 //
 // The one-wave-per-piece kernels above issue a piece's loads, wait for them
@@ -331,13 +378,20 @@ struct RowWalk {
   }
 };
 
-// dst[slot_to_row[t*k+j]] = src[t] for j < k <= KMAX (w_dst: WS), as
-// k_scatter_rows; a piece is three 16-byte chunks per lane.
-template <typename T, bool WS, int KMAX>
+// dst[slot_to_row[t*k+j]] = src[t] for j < k <= KMAX, as k_scatter_rows;
+// a piece is three 16-byte chunks per lane.  MODE kRowCopy: rows only;
+// kRowCopyW: also w_dst[that row] = w[t*k+j] (w by slot); kRowScale (bf16):
+// the copies scaled, store(w[that row] * src[t]) as k_row_scale_scatter (w
+// by row: a load behind the slot index, issued when the unit's stores are
+// next, which then wait for the previous unit's stores).
+constexpr int kRowCopy = 0, kRowCopyW = 1, kRowScale = 2;
+template <typename T, int MODE, int KMAX>
 __global__ __launch_bounds__(256) void k_scatter_rows_persist(
     const T *__restrict__ src, const int32_t *__restrict__ slot_to_row,
-    const float *__restrict__ w_src, int ntok, int d, int k, T *__restrict__ dst,
+    const float *__restrict__ w, int ntok, int d, int k, T *__restrict__ dst,
     uint64_t dst_bytes, float *__restrict__ w_dst) {
+  constexpr bool WS = MODE == kRowCopyW, SC = MODE == kRowScale;
+  static_assert(!SC || sizeof(T) == 2, "scaled rows are bf16");
   constexpr int NCH = kScatterNch;
   const int nvec = d * (int)sizeof(T) / 16;
   const int pieces = (nvec + 64 * NCH - 1) / (64 * NCH);
@@ -354,8 +408,9 @@ __global__ __launch_bounds__(256) void k_scatter_rows_persist(
     return slot_to_row[(int64_t)(c.t < ntok ? c.t : ntok - 1) * k + lk];
   };
   auto get_w = [&](RowCur c) {
-    return WS ? w_src[(int64_t)(c.t < ntok ? c.t : ntok - 1) * k + lk] : 0.0f;
+    return WS ? w[(int64_t)(c.t < ntok ? c.t : ntok - 1) * k + lk] : 0.0f;
   };
+  auto get_wrow = [&](int myr) { return w[myr >= 0 ? myr : 0]; };
   auto load = [&](RowCur c, u32x4_t (&v)[NCH]) {
     const int cc = c.p * pw + lane;
 #pragma unroll
@@ -383,7 +438,15 @@ __global__ __launch_bounds__(256) void k_scatter_rows_persist(
         // dropped stores get distinct offsets, so none is merged away
         const uint32_t off = ok ? ((uint32_t)r * (uint32_t)nvec + (uint32_t)col) * 16u
                                 : kDrop + (uint32_t)(j * NCH + h) * 16u;
-        __builtin_amdgcn_raw_buffer_store_b128(v[h], rd, (int)off, 0, 0);
+        u32x4_t y = v[h];
+        if (SC) {
+          const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), j));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            y[q] = pack_bf16x2(bf16_bits_to_f32(v[h][q] & 0xffffu) * wr,
+                               bf16_bits_to_f32(v[h][q] >> 16) * wr);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(y, rd, (int)off, 0, 0);
       }
     }
   };
@@ -400,12 +463,14 @@ __global__ __launch_bounds__(256) void k_scatter_rows_persist(
   }
   do {   // a wave without a unit runs once, every access dropped
     const RowCur cb = walk.next(ca);
+    if (SC) wa = get_wrow(ia);
     const int ib = get_idx(cb);
-    const float wb = get_w(cb);
+    float wb = get_w(cb);
     load(cb, vb);
     __builtin_amdgcn_sched_barrier(0);
     store(ca, ia, wa, va);
     ca = walk.next(cb);
+    if (SC) wb = get_wrow(ib);
     ia = get_idx(ca);
     wa = get_w(ca);
     load(ca, va);
@@ -689,17 +754,17 @@ static int launch_scatter(const char *name, const T *src, const int32_t *slot_to
     const int n = (int)ntok;
     if (k <= 4) {
       if (w_dst)
-        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, true, 4><<<g, 256, 0, s>>>(
+        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, kRowCopyW, 4><<<g, 256, 0, s>>>(
                                 src, slot_to_row, w_src, n, d, k, dst, db, w_dst));
       else
-        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, false, 4><<<g, 256, 0, s>>>(
+        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, kRowCopy, 4><<<g, 256, 0, s>>>(
                                 src, slot_to_row, w_src, n, d, k, dst, db, w_dst));
     } else {
       if (w_dst)
-        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, true, 8><<<g, 256, 0, s>>>(
+        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, kRowCopyW, 8><<<g, 256, 0, s>>>(
                                 src, slot_to_row, w_src, n, d, k, dst, db, w_dst));
       else
-        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, false, 8><<<g, 256, 0, s>>>(
+        MOE_LAUNCH(name, s, k_scatter_rows_persist<T, kRowCopy, 8><<<g, 256, 0, s>>>(
                                 src, slot_to_row, w_src, n, d, k, dst, db, w_dst));
     }
   } else {
@@ -730,6 +795,29 @@ static int launch_gather(const char *name, const T *src, const int32_t *slot_to_
                             src, slot_to_row, add, nullptr, nullptr, 0, ntok, d, k, dst));
   }
   return check_launch(name);
+}
+
+int launch_row_scale_scatter(const bf16_t *dy, const int32_t *slot_to_row, const float *w,
+                             int64_t T, int d, int k, bf16_t *s_rows, hipStream_t s) {
+  if (T <= 0) return MOE_OK;
+  if (!w)   // scaling by one is the copy
+    return launch_scatter<bf16_t>("row_scale", dy, slot_to_row, nullptr, T, d, k, s_rows,
+                                  nullptr, s);
+  if (row_persist_ok(T, d, k, sizeof(bf16_t))) {
+    const unsigned g = row_grid(row_blocks<bf16_t>(T, d, true, kScatterPiece));
+    const uint64_t db = (uint64_t)T * k * d * sizeof(bf16_t);
+    if (k <= 4)
+      MOE_LAUNCH("row_scale", s, k_scatter_rows_persist<bf16_t, kRowScale, 4><<<g, 256, 0, s>>>(
+                                     dy, slot_to_row, w, (int)T, d, k, s_rows, db, nullptr));
+    else
+      MOE_LAUNCH("row_scale", s, k_scatter_rows_persist<bf16_t, kRowScale, 8><<<g, 256, 0, s>>>(
+                                     dy, slot_to_row, w, (int)T, d, k, s_rows, db, nullptr));
+  } else {
+    const int64_t waves = T * ((d / 8 + kRsPiece - 1) / kRsPiece);
+    MOE_LAUNCH("row_scale", s, k_row_scale_scatter<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(
+                                   dy, slot_to_row, w, T, d, k, s_rows));
+  }
+  return check_launch("row_scale");
 }
 
 }  // namespace moe
