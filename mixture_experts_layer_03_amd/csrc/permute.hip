@@ -719,9 +719,8 @@ __global__ __launch_bounds__(256) void k_gather_sum(const T *__restrict__ src,
 }
 
 
-// Blocks of the persistent row kernels: kRowGridPerCu per CU of the current
-// device, never more than the one-wave-per-piece grid would have.
-static unsigned row_grid(unsigned blocks) {
+// CUs of the current device (cached per device)
+static unsigned device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -731,15 +730,27 @@ static unsigned row_grid(unsigned blocks) {
       n = 256;
     cus[dev] = n;
   }
-  const unsigned g = (unsigned)cus[dev] * kRowGridPerCu;
+  return (unsigned)cus[dev];
+}
+
+// Blocks of the persistent row kernels: kRowGridPerCu per CU, never more
+// than the one-wave-per-piece grid would have.
+static unsigned row_grid(unsigned blocks) {
+  const unsigned g = device_cus() * kRowGridPerCu;
   return blocks < g ? blocks : g;
 }
 
-// The persistent kernels take top-k <= 8 and keep every in-range byte offset
-// (T*k rows of d elements) below kDrop; the one-wave-per-piece kernels take
-// the rest.
-static bool row_persist_ok(int64_t T, int d, int k, size_t elem) {
-  return T > 0 && k <= 8 && (uint64_t)T * (uint64_t)k * (uint64_t)d * elem < (uint64_t)kDrop;
+// The persistent kernels take top-k <= 8, keep every in-range byte offset
+// (T*k rows of d elements) below kDrop, and pay off only while the
+// one-wave-per-piece grid (`units` waves) is at most two rounds of resident
+// waves (32 per CU): with more rounds those kernels already overlap one
+// wave's reads with another's writes.  Measured, persistent against one wave
+// per piece: 4096 tokens (about one round) 21.5 -> 21.0 us (forward permute),
+// 23.5 -> 21.4 us (combine); the Qwen3-30B-A3B-like layer (32768 tokens,
+// top-8) 211 -> 226 us, 247 -> 253 us; 16384 tokens mixed within +-4%.
+static bool row_persist_ok(int64_t T, int d, int k, size_t elem, int64_t units) {
+  return T > 0 && k <= 8 && (uint64_t)T * (uint64_t)k * (uint64_t)d * elem < (uint64_t)kDrop &&
+         units <= (int64_t)device_cus() * 64;
 }
 
 // src[t] -> dst[slot_to_row[t*k+j]] (and w_dst) for T tokens
@@ -748,7 +759,7 @@ static int launch_scatter(const char *name, const T *src, const int32_t *slot_to
                           const float *w_src, int64_t ntok, int d, int k, T *dst, float *w_dst,
                           hipStream_t s) {
   const unsigned blocks = row_blocks<T>(ntok, d, src != nullptr, kScatterPiece);
-  if (src && row_persist_ok(ntok, d, k, sizeof(T))) {
+  if (src && row_persist_ok(ntok, d, k, sizeof(T), 4 * (int64_t)blocks)) {
     const unsigned g = row_grid(blocks);
     const uint64_t db = (uint64_t)ntok * k * d * sizeof(T);
     const int n = (int)ntok;
@@ -778,17 +789,18 @@ static int launch_scatter(const char *name, const T *src, const int32_t *slot_to
 template <typename T>
 static int launch_gather(const char *name, const T *src, const int32_t *slot_to_row,
                          const float *add, int64_t ntok, int d, int k, T *dst, hipStream_t s) {
-  if (!add && row_persist_ok(ntok, d, k, sizeof(T))) {
+  const unsigned blocks = row_blocks<T>(ntok, d, true, k <= 4 ? 192 : 64);
+  if (!add && row_persist_ok(ntok, d, k, sizeof(T), 4 * (int64_t)blocks)) {
     const uint64_t sb = (uint64_t)ntok * k * d * sizeof(T);
     const int n = (int)ntok;
     if (k <= 4) {
       // three chunks per lane: 21.3-21.4 us at the gpt-oss-20b-like shape,
       // against 21.6-21.9 with two and 22.3 with one
-      const unsigned g = row_grid(row_blocks<T>(ntok, d, true, 192));
+      const unsigned g = row_grid(blocks);
       MOE_LAUNCH(name, s, k_gather_sum_persist<T, 4, 3><<<g, 256, 0, s>>>(src, sb, slot_to_row, n,
                                                                          d, k, dst));
     } else {
-      const unsigned g = row_grid(row_blocks<T>(ntok, d, true, 64));
+      const unsigned g = row_grid(blocks);
       MOE_LAUNCH(name, s, k_gather_sum_persist<T, 8, 1><<<g, 256, 0, s>>>(src, sb, slot_to_row, n,
                                                                          d, k, dst));
     }
@@ -805,8 +817,9 @@ int launch_row_scale_scatter(const bf16_t *dy, const int32_t *slot_to_row, const
   if (!w)   // scaling by one is the copy
     return launch_scatter<bf16_t>("row_scale", dy, slot_to_row, nullptr, T, d, k, s_rows,
                                   nullptr, s);
-  if (row_persist_ok(T, d, k, sizeof(bf16_t))) {
-    const unsigned g = row_grid(row_blocks<bf16_t>(T, d, true, kScatterPiece));
+  const unsigned blocks = row_blocks<bf16_t>(T, d, true, kScatterPiece);
+  if (row_persist_ok(T, d, k, sizeof(bf16_t), 4 * (int64_t)blocks)) {
+    const unsigned g = row_grid(blocks);
     const uint64_t db = (uint64_t)T * k * d * sizeof(bf16_t);
     if (k <= 4)
       MOE_LAUNCH("row_scale", s, k_scatter_rows_persist<bf16_t, kRowScale, 4><<<g, 256, 0, s>>>(

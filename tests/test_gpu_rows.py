@@ -3,8 +3,9 @@ permute backward -- against their definitions, bit for bit.
 
 Copies are exact; the sums are fp32 additions in ascending j (a dropped slot
 skipped) followed by one rounding to the stored dtype, recomputed here in
-numpy.  The cases cover top-k 1..9 (k <= 8 takes the persistent pipelined
-kernels, k = 9 and the permute backward's added term the one-wave-per-piece
+numpy.  The cases cover top-k 1..9 (k <= 8 with at most two rounds of
+one-wave-per-piece units takes the persistent pipelined kernels; k = 9, the
+permute backward's added term and larger inputs the one-wave-per-piece
 ones), row widths that leave partial pieces and chunks, dropped slots
 (expert id outside [0, E)), fp32 rows, and enough units that each wave of the
 persistent grid walks several loop trips, ending on either half of one.
@@ -29,6 +30,7 @@ CASES = [   # T, d, k, dtype, fraction of dropped slots
     (33, 48, 7, "fp32", 0.0),
     (2000, 24, 2, "bf16", 0.05),
     (16384, 256, 4, "bf16", 0.0),
+    (5000, 520, 6, "bf16", 0.02),
     (9001, 1000, 6, "bf16", 0.02),
 ]
 
