@@ -333,8 +333,10 @@ __global__ __launch_bounds__(256) void k_row_scale_scatter(const bf16_t *__restr
 // blocks per CU whose waves walk the (token, piece) units u = w, w + W,
 // w + 2W, ... and keep two units in flight: the loads of unit n + 1 are
 // issued before unit n's sums and stores.  Measured at the gpt-oss-20b-like
-// shape (T = 4096, d = 2880, k = 4): the forward permute 21.5 -> 21.0 us,
-// the combine 23.5 -> 22.0 us.
+// shape (T = 4096, d = 2880, k = 4; kernel durations in a trace): the
+// combine 21.1 -> 19.5 us, S = w dY 23.2 -> 21.0 us, the forward permute
+// unchanged (19.5 -> 19.4 us).  Larger inputs keep the one-wave kernels
+// (row_persist_ok).
 //
 // Every access is issued unconditionally through a buffer resource; a
 // masked one (past the row, a dropped slot, j >= k, a unit past the end)
@@ -747,7 +749,8 @@ static unsigned row_grid(unsigned blocks) {
 // wave's reads with another's writes.  Measured, persistent against one wave
 // per piece: 4096 tokens (about one round) 21.5 -> 21.0 us (forward permute),
 // 23.5 -> 21.4 us (combine); the Qwen3-30B-A3B-like layer (32768 tokens,
-// top-8) 211 -> 226 us, 247 -> 253 us; 16384 tokens mixed within +-4%.
+// top-8) 211 -> 226 us, 247 -> 253 us; 16384 tokens mixed within +-4%
+// (event timing).
 static bool row_persist_ok(int64_t T, int d, int k, size_t elem, int64_t units) {
   return T > 0 && k <= 8 && (uint64_t)T * (uint64_t)k * (uint64_t)d * elem < (uint64_t)kDrop &&
          units <= (int64_t)device_cus() * 64;
