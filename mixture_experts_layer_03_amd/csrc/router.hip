@@ -20,15 +20,20 @@ namespace moe {
 // or 2 x 2 and the block covers 4 (2) times the tokens (and 2 times the
 // experts): each LDS read then feeds several chains (the kernel reads both
 // operands from LDS for every fma: LDS reads and instruction issue bound it).  Operands
-// come from LDS tiles of kLogitCk columns (fp32, rows
-// padded so that the 8 distinct rows one read touches fall on distinct
-// banks; the 8 lanes that share a row read it as a broadcast); the next
-// tile's global loads are in flight while the current one is used (widened
-// to fp32 only when staged).
+// come from LDS tiles of logit_cols<TB>() columns (fp32, rows padded so that
+// the 8 distinct rows one read touches fall on distinct banks; the 8 lanes
+// that share a row read it as a broadcast); the next tile's global loads are
+// in flight while the current one is used (widened to fp32 only when
+// staged).  One chain per lane (few chains, two waves per SIMD) takes tiles
+// of 256 columns, as wide as one 16-byte x load per thread allows, so that a
+// tile's fmas cover more of the next tile's load latency: 38.6-39.3 -> 34.5-35.5
+// us at T = 4096, E = 32.  The blocked forms keep 64 (at 128 the 2 x 2 form
+// at T = 32768, E = 128 ran 366-369 -> 383-386 us: its larger LDS tiles
+// leave fewer blocks per CU).
 constexpr int kLogitTok = 8;     // tokens per block
 constexpr int kLogitExp = 32;    // experts per block
-constexpr int kLogitCk = 64;     // columns per LDS tile
-constexpr int kLogitPad = kLogitCk + 4;
+template <int TB>
+constexpr int logit_cols() { return TB == 1 ? 256 : 64; }   // columns per LDS tile
 
 // 8 consecutive elements, raw
 struct Raw8 {
@@ -70,12 +75,13 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
                                                        int64_t ntok, int d, int E,
                                                        float *__restrict__ logits) {
   constexpr int NT = kLogitTok * TB, NE = kLogitExp * EB;   // block tokens, experts
-  constexpr int UPR = kLogitCk / 8;                           // 8-element units per tile row
+  constexpr int CK = logit_cols<TB>(), PAD = CK + 4;         // tile columns, row pitch
+  constexpr int UPR = CK / 8;                                 // 8-element units per tile row
   constexpr int XU = NT * UPR, WU = NE * UPR;                 // units of the x and w tiles
   static_assert(XU <= 256 && WU % 256 == 0, "at most one x unit, whole w units per thread");
   constexpr int WPT = WU / 256;
-  __shared__ __attribute__((aligned(16))) float xs[NT][kLogitPad];
-  __shared__ __attribute__((aligned(16))) float ws[NE][kLogitPad];
+  __shared__ __attribute__((aligned(16))) float xs[NT][PAD];
+  __shared__ __attribute__((aligned(16))) float ws[NE][PAD];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int tok = lane >> 3, el = wave * 8 + (lane & 7);
@@ -119,11 +125,11 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
   };
 
   fetch(0);
-  for (int c0 = 0; c0 < d; c0 += kLogitCk) {
+  for (int c0 = 0; c0 < d; c0 += CK) {
     stage();
     __syncthreads();
-    if (c0 + kLogitCk < d) fetch(c0 + kLogitCk);
-    const int cn = min(kLogitCk, d - c0);   // a multiple of 8
+    if (c0 + CK < d) fetch(c0 + CK);
+    const int cn = min(CK, d - c0);   // a multiple of 8
     auto step = [&](int cc) {
       float4 xv[TB], wv[EB];
 #pragma unroll
@@ -140,10 +146,10 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
           acc[i][j] = fmaf(xv[i].w, wv[j].w, acc[i][j]);
         }
     };
-    if (cn == kLogitCk) {
+    if (cn == CK) {
       // whole tile: unrolled, so the LDS reads run ahead of the fma chains
 #pragma unroll
-      for (int cc = 0; cc < kLogitCk; cc += 4) step(cc);
+      for (int cc = 0; cc < CK; cc += 4) step(cc);
     } else {
       for (int cc = 0; cc < cn; cc += 4) step(cc);
     }
