@@ -171,8 +171,9 @@ __global__ __launch_bounds__(256) void k_router_logits(const T *__restrict__ x,
 
 // ------------------------------------------------------------------ top-k
 //
-// A group of G = min(64, pow2ceil(E)) lanes serves one token; a wave serves
-// 64/G tokens.  Lane s of a group holds experts s, s+G, s+2G, ...  Each of the
+// A group of G = min(32, pow2ceil(E)) lanes (64 past 512 experts) serves one
+// token; a wave serves 64/G tokens.  Lane s of a group holds experts s, s+G,
+// s+2G, ...  Each of the
 // k rounds takes the best unselected value of every lane and reduces it over
 // the group with xor-shuffles (greater value wins; equal values -> lower id).
 // The winner of round j is kept by lane j of the group.
@@ -503,12 +504,16 @@ static int route_impl(const float *logits, const float *sel_bias, int64_t T, int
   if (T == 0) return MOE_OK;
   MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
   hipStream_t s = (hipStream_t)stream;
+  // Groups of up to 32 lanes (64 past 512 experts, at most 16 experts per
+  // lane): each round's reduction then takes one xor step fewer and a wave
+  // serves two tokens.
+  const int gmax = E > 32 * kMaxPerLane ? 64 : 32;
   int G = 1;
-  while (G < E && G < 64) G <<= 1;
+  while (G < E && G < gmax) G <<= 1;
   const int64_t threads = T * G;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   const char *name = sel_bias ? "route_topk_biased" : "route_topk";
-  int vpl = 1;   // experts per lane of a 64-lane group, a power of two
+  int vpl = 1;   // experts per lane of a group, a power of two
   while (vpl * G < E) vpl <<= 1;
 #define ROUTE_CASE(GV, VV)                                                                    \
   MOE_LAUNCH(name, s,                                                                         \
@@ -520,7 +525,15 @@ static int route_impl(const float *logits, const float *sel_bias, int64_t T, int
     case 4: ROUTE_CASE(4, 1); break;
     case 8: ROUTE_CASE(8, 1); break;
     case 16: ROUTE_CASE(16, 1); break;
-    case 32: ROUTE_CASE(32, 1); break;
+    case 32:
+      switch (vpl) {
+        case 1: ROUTE_CASE(32, 1); break;
+        case 2: ROUTE_CASE(32, 2); break;
+        case 4: ROUTE_CASE(32, 4); break;
+        case 8: ROUTE_CASE(32, 8); break;
+        default: ROUTE_CASE(32, 16); break;
+      }
+      break;
     default:
       switch (vpl) {
         case 1: ROUTE_CASE(64, 1); break;
