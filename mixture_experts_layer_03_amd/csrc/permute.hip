@@ -138,14 +138,62 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool valid, int nbits) {
   return valid ? m : 0ull;
 }
 
+// SCAN: `base` is the histogram itself (E x nchunk, at most kPlaceScanMax
+// entries): every block sums it for its chunk's first rows and the experts'
+// totals (integer sums, exact in any order), and block 0 writes counts and
+// offsets -- the k_scan launch is then not needed.
+constexpr int kPlaceScanMax = 16384;
+template <bool SCAN>
 __global__ __launch_bounds__(256) void k_place(const int32_t *__restrict__ idx, int64_t R, int E,
                                                int chunk, int nchunk, int nbits,
                                                const int32_t *__restrict__ base,
                                                int32_t *__restrict__ slot_to_row,
-                                               int32_t *__restrict__ row_to_slot) {
+                                               int32_t *__restrict__ row_to_slot,
+                                               int32_t *__restrict__ counts,
+                                               int32_t *__restrict__ offsets) {
   __shared__ int cnt[4][kMaxExperts];
+  __shared__ int s_base[SCAN ? kMaxExperts : 1], s_tot[SCAN ? kMaxExperts : 1];
+  __shared__ int s_part[SCAN ? 256 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < 4 * E; e += 256) cnt[e / E][e % E] = 0;
+  if constexpr (SCAN) {
+    // thread i: experts [i*epb, (i+1)*epb); their totals and, for this
+    // block, the rows of the earlier chunks
+    const int epb = (E + 255) / 256;
+    const int e_lo = min(E, (int)threadIdx.x * epb), e_hi = min(E, e_lo + epb);
+    int mine = 0;
+    for (int e = e_lo; e < e_hi; ++e) {
+      const int32_t *h = base + (int64_t)e * nchunk;
+      int tot = 0, pre = 0;
+#pragma unroll 8
+      for (int c = 0; c < nchunk; ++c) {
+        const int v = h[c];
+        tot += v;
+        pre += c < (int)blockIdx.x ? v : 0;
+      }
+      s_base[e] = pre;
+      s_tot[e] = tot;
+      mine += tot;
+    }
+    s_part[threadIdx.x] = mine;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {   // inclusive scan of the 256 parts
+      const int v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int run = s_part[threadIdx.x] - mine;   // rows of the experts before e_lo
+    for (int e = e_lo; e < e_hi; ++e) {
+      s_base[e] += run;
+      if (blockIdx.x == 0) {
+        offsets[e] = run;
+        counts[e] = s_tot[e];
+      }
+      run += s_tot[e];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = s_part[255];
+  }
   __syncthreads();
   const int64_t cbeg = (int64_t)blockIdx.x * chunk;
   const int quarter = chunk / 4;   // multiple of 64
@@ -181,7 +229,7 @@ __global__ __launch_bounds__(256) void k_place(const int32_t *__restrict__ idx, 
       if (valid) {
         const int before = cnt[wave][e];
         const int rank = __popcll(m & lt);
-        const int row = base[(int64_t)e * nchunk + blockIdx.x] + before + rank;
+        const int row = (SCAN ? s_base[e] : base[(int64_t)e * nchunk + blockIdx.x]) + before + rank;
         slot_to_row[s] = row;
         row_to_slot[row] = (int32_t)s;
         if (rank == 0) cnt[wave][e] = before + __popcll(m);
@@ -907,10 +955,19 @@ extern "C" int moe_permute(const void *x, const int32_t *topk_idx, const float *
   while ((1 << nbits) < E) ++nbits;
   MOE_LAUNCH("permute_hist", s,
              k_hist<<<p.nchunk, 256, 0, s>>>(topk_idx, p.R, E, p.chunk, p.nchunk, hist));
-  MOE_LAUNCH("permute_scan", s, k_scan<<<1, 1024, 0, s>>>(hist, E, p.nchunk, base, counts, offsets));
-  MOE_LAUNCH("permute_place", s,
-             k_place<<<p.nchunk, 256, 0, s>>>(topk_idx, p.R, E, p.chunk, p.nchunk, nbits, base,
-                                              slot_to_row, row_to_slot));
+  if ((int64_t)E * p.nchunk <= kPlaceScanMax) {   // the blocks scan the histogram themselves
+    MOE_LAUNCH("permute_place", s,
+               k_place<true><<<p.nchunk, 256, 0, s>>>(topk_idx, p.R, E, p.chunk, p.nchunk, nbits,
+                                                      hist, slot_to_row, row_to_slot, counts,
+                                                      offsets));
+  } else {
+    MOE_LAUNCH("permute_scan", s,
+               k_scan<<<1, 1024, 0, s>>>(hist, E, p.nchunk, base, counts, offsets));
+    MOE_LAUNCH("permute_place", s,
+               k_place<false><<<p.nchunk, 256, 0, s>>>(topk_idx, p.R, E, p.chunk, p.nchunk, nbits,
+                                                       base, slot_to_row, row_to_slot, nullptr,
+                                                       nullptr));
+  }
   rc = check_launch("moe_permute(maps)");
   if (rc) return rc;
   if (x || w_perm) {
